@@ -1,0 +1,163 @@
+"""Throughput of the fused lattice Boltzmann step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A "step" is one pass of the whole fused step (the in-place AA kernel for
+D3Q19 (+D3Q7), plus the link gather/scatter kernels when the box has walls or
+solids) over the resident population buffer.  W untimed steps, then exactly
+K timed steps in one submission, bracketed by stream synchronisation; HIP
+events on the library's stream (torch's current stream) time the region.
+
+Prints one JSON line: MLUPS (cells * steps / s / 1e6, every cell counted),
+the roofline of the dominant kernel (algorithmic HBM bytes per launch / its
+average duration, against the 8 TB/s HBM peak) and the oracle's throughput on
+the host cores on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLUPS and achieved HBM TB/s, D3Q19(+D3Q7) fp32 AA step, 128³–512³, 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+
+# algorithmic bytes per cell update: every population read once and written once
+def bytes_per_cell(thermal: bool, dtype: int, streaming: int) -> int:
+    q = 19 + (7 if thermal else 0)
+    passes = 2 if streaming == 2 else 1  # two-buffer: collide in place, then pull
+    return 2 * q * dtype * passes
+
+
+WORKLOAD_INFO = {
+    "sol256": "D3Q19 MRT isothermal, 256^3 periodic, tau=0.55, seeded random solenoidal velocity "
+              "(|u|<=0.05) on rho=1 (the 128^3 in-place/two-buffer recipe at 256^3)",
+    "sol128": "D3Q19 MRT isothermal, 128^3 periodic, tau=0.55, seeded random solenoidal velocity (|u|<=0.05)",
+    "sphere128": "D3Q19 MRT, 128^3 periodic, centred solid sphere R=16, bounce-back links, gx=1e-6",
+    "cavity256": "thermal D3Q19+D3Q7 MRT, 256^3 cavity, x- hot/x+ cold, adiabatic others, Ra=1e7, Pr=0.71",
+    "rb512": "thermal D3Q19+D3Q7 MRT, 512^3, periodic x/y, z- hot/z+ cold, random spheres R 4..12 (10%), "
+             "Ra=1e8, Pr=0.71",
+    "tg32": "D3Q19 MRT, 32^3 periodic Taylor-Green, tau=0.6",
+}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "lattice_boltzmann_cfd_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(name.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, dtype: int, streaming: int):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources (else null)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{'f32' if dtype == 4 else 'f64'}"
+                        f"_{'ab' if streaming == 2 else 'aa'}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, steps: int):
+    import oracle
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    oracle.build(force=False)
+    t0 = time.perf_counter()
+    oracle.run(w.params, steps, w.rho, w.u, w.T if w.params.get("thermal") else None, labels=w.labels,
+               nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": w.cells * steps / dt / 1e6, "unit": "MLUPS", "cores": threads, "kind": "oracle",
+            "sample": f"{steps} steps of the full {w.shape[0]}x{w.shape[1]}x{w.shape[2]} box "
+                      f"(fp64 two-buffer collide-then-pull, OpenMP over cells), {dt:.1f} s"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default="sol256", choices=sorted(WORKLOAD_INFO))
+    ap.add_argument("--dtype", type=int, default=4, choices=(4, 8))
+    ap.add_argument("--streaming", type=int, default=1, choices=(1, 2), help="1 in place (AA), 2 two buffers")
+    ap.add_argument("--cpu-steps", type=int, default=6, help="oracle steps for the CPU baseline (0: skip)")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the multi-GPU slab decomposition is a design, not code", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from lattice_boltzmann_cfd_amd import binding, inputs
+
+    w = inputs.make(args.workload)
+    thermal = bool(w.params.get("thermal"))
+    solver = binding.Solver(w.params, w.labels, dtype=args.dtype, streaming=args.streaming)
+    solver.init(w.rho, w.u, w.T if thermal else None)
+    stream = torch.cuda.current_stream()
+    solver.step(args.warmup)
+    torch.cuda.synchronize()
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    solver.step(args.steps)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    # unstable runs raise here (LBM_E_UNSTABLE) rather than report a number
+    rho, _, _ = solver.macros()
+    solver.wall_force(0)
+    ms_per_step = ms / args.steps
+    mlups = w.cells * args.steps / (ms / 1e3) / 1e6
+
+    bpc = bytes_per_cell(thermal, args.dtype, args.streaming)
+    has_links = (solver.num_links(19) + solver.num_links(7)) > 0
+    launches = 1 if args.streaming == 1 else 2
+    per_launch_bytes = bpc * w.cells / launches
+    # periodic boxes run exactly `launches` bulk kernels per step and nothing else
+    kernel_ms = ms_per_step / launches
+    achieved = per_launch_bytes / (kernel_ms / 1e3) / 1e9
+    traffic = load_traffic(args.workload, args.dtype, args.streaming)
+    kernel = "k_aa_step" if args.streaming == 1 else "k_ab_collide+k_ab_pull"
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": kernel,
+                "bytes_per_cell": bpc, "launch_includes_links": has_links}
+
+    line = {
+        "metric": METRIC, "value": round(mlups, 1), "unit": "MLUPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32" if args.dtype == 4 else "f64", "data": "synthetic",
+        "config": {"workload": args.workload, "description": WORKLOAD_INFO[args.workload],
+                   "shape": list(w.shape), "cells": w.cells,
+                   "streaming": "AA in place" if args.streaming == 1 else "A-B two buffers",
+                   "hbm_TBps_algorithmic": round(bpc * w.cells * args.steps / (ms / 1e3) / 1e12, 3)},
+        "roofline": roofline,
+    }
+    solver.close()
+    del rho
+    if args.cpu_steps > 0:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_steps)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

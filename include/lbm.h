@@ -1,0 +1,177 @@
+/*
+ * lbm.h -- C ABI of the MI355X fused lattice Boltzmann time step.
+ *
+ * One library, liblbm_hip.so, built from hand-written HIP kernels for gfx950.
+ * Every call takes plain pointers and sizes; no C++ or framework types cross
+ * this boundary.  All compute runs in the library's kernels on the caller's
+ * HIP stream; calls are stream-ordered and asynchronous except
+ * lbm_wall_force(), which synchronises the stream.
+ *
+ * What the library computes (the pages it follows):
+ *  - "Multi-GPU thermal lattice Boltzmann simulations using OpenACC and MPI",
+ *    Sec. 2: double-distribution thermal LB model, D3Q19 for the flow and D3Q7
+ *    for the temperature, both with MRT collision; the force term
+ *    F' = M^-1 (I - S/2) M F~ with F = rho g beta_T (T - T0) z;
+ *    rho = sum f, u = (sum e f + F/2)/rho, T = sum g; half-way bounce-back
+ *    f_ibar(x, t+dt) = f_i^+(x, t) for no-slip walls; half-way anti-bounce-back
+ *    g_ibar(x, t+dt) = -g_i^+(x, t) + w T_w with w = (6 + a_T)/21 for a
+ *    Dirichlet temperature wall and g_ibar = g_i^+ for an adiabatic one;
+ *    Sec. 3: structure-of-arrays storage, population i of cell (x, y, z) at
+ *    x + Nx*y + Nx*Ny*z + Nx*Ny*Nz*i.
+ *  - "GPU lattice Boltzmann: streaming layout and performance" (OneCAD docs):
+ *    one population buffer streamed in place with the AA pattern (even steps
+ *    read (q, x) and write (opposite(q), x); odd steps read
+ *    (opposite(q), x - c_q) and write (q, x + c_q)); coordinates computed once
+ *    per cell and neighbours wrapped with a compare and an add; wall links
+ *    handled by a gather pass into scratch followed by a scatter pass, with the
+ *    momentum exchange taken in the gather of a submission's last step; the
+ *    two-buffer layout (collide in place, then pull into the other buffer) as
+ *    an option.
+ *  - "GPU Optimization for High-Quality Kinetic Fluid Simulation", Sec. 3.1,
+ *    Eq. 1-5: the lattice Boltzmann update as streaming plus collision with a
+ *    force term, MRT relaxation Omega = -M^-1 D (m - m_eq).
+ *
+ * Readings of what the pages leave open (the library and its test oracle
+ * follow the same readings, each in its own code):
+ *  - D3Q19 = rest, 6 axis and 12 face-diagonal velocities; weights 1/3, 1/18,
+ *    1/36; moment basis = the orthogonal basis of d'Humieres et al. with rows
+ *    (in this order, which is the order of lbm_params.s19):
+ *      0 rho: 1              1 e: 19c^2-30          2 eps: (21c^4-53c^2+24)/2
+ *      3 jx: cx              4 qx: (5c^2-9)cx       5 jy, 6 qy, 7 jz, 8 qz
+ *      9 3pxx: 3cx^2-c^2     10 3pixx: (3c^2-5)(3cx^2-c^2)
+ *      11 pww: cy^2-cz^2     12 piww: (3c^2-5)(cy^2-cz^2)
+ *      13 pxy: cx cy         14 pyz: cy cz          15 pxz: cx cz
+ *      16 mx: (cy^2-cz^2)cx  17 my: (cz^2-cx^2)cy   18 mz: (cx^2-cy^2)cz
+ *    m_eq = M f_eq with f_eq = w rho [1 + 3 c.u + 9/2 (c.u)^2 - 3/2 u.u];
+ *    F~ = w [3 (c - u) + 9 (c.u) c] . F (Guo).
+ *  - D3Q7 directions (0, +x, -x, +y, -y, +z, -z); rows of N (order of
+ *    lbm_params.s7): 1, e_x, e_y, e_z, (-6,1,1,1,1,1,1), (0,2,2,-1,-1,-1,-1),
+ *    (0,0,0,1,1,-1,-1); n_eq = (T, ux T, uy T, uz T, a_T T, 0, 0).
+ *  - F = rho*accel + rho*gbeta*(T - T0) (gbeta a vector; buoyancy against
+ *    gravity).  Initial state: f = f_eq(rho, u), g = N^-1 n_eq(T, u).
+ *  - Momentum exchange on a wall link: the wall receives 2 c_p f_p^+; heat into
+ *    the fluid through a Dirichlet link: w T_w - 2 g_p^+.
+ *  - Walls sit half-way between the last fluid cell and the box face; a box
+ *    face is either periodic or a no-slip wall, the same on both ends of an
+ *    axis.  A link crossing two faces belongs to the first crossed axis in
+ *    x, y, z order.
+ */
+#ifndef LBM_H
+#define LBM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lbm_status {
+    LBM_OK = 0,
+    LBM_E_INVALID = 1,  /* bad argument; no device work was done */
+    LBM_E_NOMEM = 2,    /* device_bytes smaller than lbm_required_bytes() */
+    LBM_E_DEVICE = 3,   /* a HIP call failed; text in lbm_last_error() */
+    LBM_E_UNSTABLE = 4, /* a fluid cell's rho or T was non-finite at a read-back */
+} lbm_status;
+
+enum { LBM_FACE_PERIODIC = 0, LBM_FACE_WALL = 1 };
+enum { LBM_ADIABATIC = 0, LBM_DIRICHLET = 1 };
+enum { LBM_STREAM_AUTO = 0, LBM_STREAM_AA = 1, LBM_STREAM_AB = 2 };
+enum { LBM_MAX_GROUPS = 261 }; /* 6 faces + 255 solid labels */
+
+/* Faces are numbered 0..5 = x-, x+, y-, y+, z-, z+.  Force/heat group g is
+ * face g for g < 6 and solid label g - 5 for g >= 6. */
+typedef struct lbm_params {
+    int32_t nx, ny, nz;      /* cells per axis, each >= 1; nx*ny*nz*dtype < 2^32 - 2^20 */
+    int32_t dtype;           /* 4: fp32 populations and arithmetic, 8: fp64 */
+    int32_t streaming;       /* LBM_STREAM_*; AUTO = in place (AA) */
+    int32_t thermal;         /* 0: D3Q19 only, 1: D3Q19 + D3Q7 */
+    int32_t face_kind[6];    /* LBM_FACE_PERIODIC or LBM_FACE_WALL */
+    int32_t face_thermal[6]; /* LBM_ADIABATIC or LBM_DIRICHLET (wall faces) */
+    double face_T[6];        /* Dirichlet wall temperature per face */
+    int32_t solid_thermal;   /* thermal rule of every solid cell */
+    int32_t reserved0;       /* must be 0 */
+    double solid_T;          /* Dirichlet temperature of the solids */
+    double s19[19];          /* D3Q19 relaxation rates, row order above, each in [0, 2) */
+    double s7[7];            /* D3Q7 relaxation rates, row order above, each in [0, 2) */
+    double a_T;              /* D3Q7 constant a_T (rest weight (1 - a_T)/7), in (-6, 1] */
+    double accel[3];         /* body acceleration: F = rho*accel + ... */
+    double gbeta[3];         /* buoyancy vector g*beta_T: F = ... + rho*gbeta*(T - T0) */
+    double T0;               /* reference temperature of the buoyancy term */
+} lbm_params;
+
+typedef struct lbm_ctx lbm_ctx;
+
+/* Device bytes that lbm_create() needs for these parameters and labels:
+ * population buffer(s), link arrays, link scratch, force accumulators and a
+ * copy of the labels.  solid_labels: host, nx*ny*nz bytes in the order
+ * x + nx*(y + ny*z), 0 = fluid, l >= 1 = solid of group 5 + l; NULL = no
+ * solids.  Returns 0 if the parameters are invalid. */
+size_t lbm_required_bytes(const lbm_params* p, const uint8_t* solid_labels);
+
+/* Validate the parameters, build the wall/solid link lists on the host
+ * (every fluid cell x and direction p whose neighbour x + c_p is a wall face
+ * or a solid cell), carve device_buf and upload the links.
+ * device_buf: device memory of device_bytes bytes, BORROWED: the caller owns
+ * it and keeps it alive until lbm_destroy(); the populations live in it, so
+ * saving its bytes and lbm_time() checkpoints the state.
+ * hip_stream: a hipStream_t (NULL = the null stream), BORROWED.
+ * Host arrays are copied before the call returns.  On failure nothing is kept
+ * and *out is NULL.  Errors: LBM_E_INVALID (bad sizes, a rate outside [0, 2),
+ * a_T outside (-6, 1], one face of an axis periodic and the other a wall,
+ * dtype not 4 or 8), LBM_E_NOMEM (device_bytes too small), LBM_E_DEVICE. */
+lbm_status lbm_create(const lbm_params* p, const uint8_t* solid_labels, void* device_buf,
+                      size_t device_bytes, void* hip_stream, lbm_ctx** out);
+
+/* Set the state to equilibrium of the given fields and the time to 0.
+ * rho: nx*ny*nz values, u: three planes (ux, uy, uz) of nx*ny*nz values,
+ * T: nx*ny*nz values or NULL (thermal runs then start at T = 0); all device
+ * pointers in the context's dtype, read by kernels enqueued on the stream.
+ * Values on solid cells are ignored.  Asynchronous. */
+lbm_status lbm_init_fields(lbm_ctx* ctx, const void* rho, const void* u, const void* T);
+
+/* Enqueue n fused time steps (a "submission"): per step one in-place kernel
+ * (collision + streaming of D3Q19 and, if thermal, D3Q7), then, when the box
+ * has wall or solid links, the link gather and scatter kernels.  The forces
+ * and heat of the submission's last step are latched for lbm_wall_force().
+ * n = 0 is a no-op; n < 0 is LBM_E_INVALID.  Asynchronous. */
+lbm_status lbm_step(lbm_ctx* ctx, int64_t n);
+
+/* Macroscopic fields at the current time: rho, u = (sum c f + F/2)/rho as
+ * three planes, T (may be NULL; ignored unless thermal).  Device pointers in
+ * the context's dtype, written by a kernel on the stream.  Solid cells get
+ * NaN.  If a fluid cell's rho or T is not finite, a sticky LBM_E_UNSTABLE is
+ * recorded and returned by the next lbm_wall_force().  Asynchronous. */
+lbm_status lbm_read_macros(lbm_ctx* ctx, void* rho, void* u, void* T);
+
+/* Copy the latched per-group sums of the last step of the last submission to
+ * out (host, 4*n_groups doubles): (Fx, Fy, Fz) = force on the wall face or
+ * solid, Q = heat into the fluid through its Dirichlet links.  Groups beyond
+ * LBM_MAX_GROUPS are zero-filled.  Synchronises the stream; returns
+ * LBM_E_UNSTABLE if a read-back saw a non-finite fluid value. */
+lbm_status lbm_wall_force(lbm_ctx* ctx, double* out, int32_t n_groups);
+
+/* Current time step count (number of steps since lbm_init_fields). */
+int64_t lbm_time(const lbm_ctx* ctx);
+
+/* Number of links of the D3Q19 (lattice = 19) or D3Q7 (lattice = 7) list. */
+int64_t lbm_num_links(const lbm_ctx* ctx, int32_t lattice);
+
+/* Host only (no device work): the number of links lbm_create() would build
+ * for these parameters and labels on the D3Q19 (19) or D3Q7 (7) lattice; a
+ * link is a fluid cell x and direction p with x + c_p a wall face or a solid
+ * cell.  Returns -1 for invalid parameters or lattice. */
+int64_t lbm_count_links(const lbm_params* p, const uint8_t* solid_labels, int32_t lattice);
+
+/* Last error text of this context (or of the last failed lbm_create when ctx
+ * is NULL).  Valid until the next call on the same context. */
+const char* lbm_last_error(const lbm_ctx* ctx);
+
+/* Release the context (host memory only; device_buf stays the caller's). */
+void lbm_destroy(lbm_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LBM_H */

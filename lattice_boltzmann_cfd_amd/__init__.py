@@ -6,14 +6,6 @@ ctypes (argument marshalling only).  ``inputs`` makes the seeded synthetic
 workloads.  The binding loads the library on first use and raises if it is
 missing: there is no CPU fallback.
 """
-from . import inputs  # noqa: F401
+from . import binding, inputs  # noqa: F401
 
 __all__ = ["inputs", "binding"]
-
-
-def __getattr__(name):
-    if name == "binding":
-        from . import binding
-
-        return binding
-    raise AttributeError(name)

@@ -1,0 +1,655 @@
+// lbm_api.cpp -- the C ABI of include/lbm.h: parameter checks, the host link
+// builder, carving of the caller's device buffer and the per-step launch
+// sequence.  All arithmetic of the method runs in lbm_kernels.hip.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <exception>
+#include <new>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "lbm.h"
+#include "lbm_internal.hpp"
+
+using namespace lbm;
+
+struct lbm_ctx {
+    lbm_params p;
+    int es = 4;
+    bool thermal = false;
+    bool ab = false;
+    hipStream_t stream = nullptr;
+    Geometry geo{};
+    char* f = nullptr;
+    char* g = nullptr;
+    char* f2 = nullptr;
+    char* g2 = nullptr;
+    uint8_t* labels = nullptr;
+    int32_t* lcell = nullptr;
+    int32_t* lcellw = nullptr;
+    uint32_t* lmeta = nullptr;
+    char* scratch = nullptr;
+    double* wall_T = nullptr;
+    double* accum = nullptr;
+    int32_t* unstable = nullptr;
+    int64_t n_f = 0, n_g = 0;
+    int64_t t = 0;
+    bool initialised = false;
+    std::string err;
+    Collision<float> colf{};
+    Collision<double> cold{};
+};
+
+namespace {
+
+thread_local std::string g_create_error;
+
+constexpr size_t ALIGN = 256;
+constexpr int64_t MAX_CELLS = (int64_t(1) << 31) - (int64_t(1) << 20);
+
+size_t align_up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+
+DivMagic make_magic(uint32_t d)
+{
+    uint32_t l = 0;
+    while ((uint64_t(1) << l) < d) ++l;
+    const uint64_t num = uint64_t(1) << (31 + l);
+    DivMagic m;
+    m.mul = (num + d - 1) / d;
+    m.shift = 31 + l;
+    m.d = d;
+    return m;
+}
+
+bool magic_ok(const DivMagic& m, uint32_t limit)
+{
+    const uint32_t d = m.d;
+    const uint32_t probes[] = {0u, 1u, d - 1, d, d + 1, 2 * d - 1, 2 * d, limit - 1, limit - d, limit / 2,
+                               (limit / d) * d, (limit / d) * d - 1, 0x7fffffffu, 0x7ffffffeu};
+    for (uint32_t n : probes) {
+        if (n > 0x7fffffffu) continue;
+        if (divide(n, m) != n / d) return false;
+    }
+    for (uint32_t n = 0; n < 100000; ++n)
+        if (divide(n * 2654435761u % 0x7fffffffu, m) != (n * 2654435761u % 0x7fffffffu) / d) return false;
+    return true;
+}
+
+bool finite(double v) { return std::isfinite(v); }
+
+// Returns an empty string when the parameters are acceptable.
+std::string validate(const lbm_params* p)
+{
+    if (!p) return "params is NULL";
+    if (p->nx < 1 || p->ny < 1 || p->nz < 1) return "nx, ny, nz must be >= 1";
+    const int64_t n = (int64_t)p->nx * p->ny * p->nz;
+    if (n >= MAX_CELLS) return "nx*ny*nz too large for 32-bit cell indices";
+    if (p->dtype != 4 && p->dtype != 8) return "dtype must be 4 or 8";
+    // kernels address a population plane with 32-bit byte offsets
+    if ((n + 63) / 64 * 64 * (int64_t)p->dtype >= (int64_t(1) << 32) - (int64_t(1) << 20))
+        return "nx*ny*nz*dtype too large for 32-bit plane offsets";
+    if (p->streaming < 0 || p->streaming > 2) return "streaming must be 0, 1 or 2";
+    if (p->thermal != 0 && p->thermal != 1) return "thermal must be 0 or 1";
+    if (p->reserved0 != 0) return "reserved0 must be 0";
+    for (int f = 0; f < 6; ++f) {
+        if (p->face_kind[f] != LBM_FACE_PERIODIC && p->face_kind[f] != LBM_FACE_WALL) return "bad face_kind";
+        if (p->face_thermal[f] != LBM_ADIABATIC && p->face_thermal[f] != LBM_DIRICHLET) return "bad face_thermal";
+        if (!finite(p->face_T[f])) return "face_T must be finite";
+    }
+    for (int a = 0; a < 3; ++a)
+        if (p->face_kind[2 * a] != p->face_kind[2 * a + 1])
+            return "the two faces of an axis must both be periodic or both be walls";
+    if (p->solid_thermal != LBM_ADIABATIC && p->solid_thermal != LBM_DIRICHLET) return "bad solid_thermal";
+    if (!finite(p->solid_T)) return "solid_T must be finite";
+    for (int k = 0; k < 19; ++k)
+        if (!(p->s19[k] >= 0.0 && p->s19[k] < 2.0)) return "s19 rates must lie in [0, 2)";
+    for (int k = 0; k < 7; ++k)
+        if (!(p->s7[k] >= 0.0 && p->s7[k] < 2.0)) return "s7 rates must lie in [0, 2)";
+    if (!(p->a_T > -6.0 && p->a_T <= 1.0)) return "a_T must lie in (-6, 1]";
+    for (int a = 0; a < 3; ++a)
+        if (!finite(p->accel[a]) || !finite(p->gbeta[a])) return "accel and gbeta must be finite";
+    if (!finite(p->T0)) return "T0 must be finite";
+    return "";
+}
+
+template <typename R>
+Collision<R> make_collision(const lbm_params* p)
+{
+    Collision<R> c{};
+    const double* s = p->s19;
+    c.s_e = (R)s[1];
+    c.s_eps = (R)s[2];
+    c.s_qx = (R)s[4];
+    c.s_qy = (R)s[6];
+    c.s_qz = (R)s[8];
+    c.s_3pxx = (R)s[9];
+    c.s_3pixx = (R)s[10];
+    c.s_pww = (R)s[11];
+    c.s_piww = (R)s[12];
+    c.s_pxy = (R)s[13];
+    c.s_pyz = (R)s[14];
+    c.s_pxz = (R)s[15];
+    c.s_mx = (R)s[16];
+    c.s_my = (R)s[17];
+    c.s_mz = (R)s[18];
+    c.q_jx = (R)p->s7[1];
+    c.q_jy = (R)p->s7[2];
+    c.q_jz = (R)p->s7[3];
+    c.q_e = (R)p->s7[4];
+    c.q_5 = (R)p->s7[5];
+    c.q_6 = (R)p->s7[6];
+    for (int a = 0; a < 3; ++a) {
+        c.accel[a] = (R)p->accel[a];
+        c.gbeta[a] = p->thermal ? (R)p->gbeta[a] : R(0);
+    }
+    c.T0 = (R)p->T0;
+    c.a_T = (R)p->a_T;
+    return c;
+}
+
+// ------------------------------------------------------------- links
+
+struct LinkList {
+    std::vector<int32_t> cell, cellw;
+    std::vector<uint32_t> meta;
+};
+
+struct Dir {
+    int c[3];
+};
+
+// For fluid cell (x, y, z) and direction c: the group of the blocked link, or
+// -1.  A link is blocked when x + c leaves the box through a wall face (the
+// first crossed axis in x, y, z order) or its periodic image is solid.
+inline int blocked_group(const lbm_params* p, const uint8_t* labels, int x, int y, int z, const int* c,
+                         int32_t* image)
+{
+    const int n[3] = {p->nx, p->ny, p->nz};
+    int t[3] = {x + c[0], y + c[1], z + c[2]};
+    int grp = -1;
+    for (int a = 0; a < 3 && grp < 0; ++a) {
+        if (t[a] < 0 && p->face_kind[2 * a] == LBM_FACE_WALL) grp = 2 * a;
+        else if (t[a] >= n[a] && p->face_kind[2 * a + 1] == LBM_FACE_WALL) grp = 2 * a + 1;
+    }
+    for (int a = 0; a < 3; ++a) t[a] = t[a] < 0 ? t[a] + n[a] : (t[a] >= n[a] ? t[a] - n[a] : t[a]);
+    *image = t[0] + p->nx * (t[1] + p->ny * t[2]);
+    if (grp >= 0) return grp;
+    if (labels && labels[*image]) return 5 + labels[*image];
+    return -1;
+}
+
+// Build (or only count) the links of one lattice.  Cells are visited in
+// index order by several host threads; the result is then ordered by group
+// with a stable counting sort so that wavefronts of the gather pass mostly
+// see a single group.
+int64_t build_links(const lbm_params* p, const uint8_t* labels, bool d3q7, LinkList* out)
+{
+    std::vector<Dir> dirs;
+    if (!d3q7) {
+        for (int q = 1; q < Q19; ++q) dirs.push_back({{cx19(q), cy19(q), cz19(q)}});
+    } else {
+        for (int k = 1; k < Q7; ++k) dirs.push_back({{cx7(k), cy7(k), cz7(k)}});
+    }
+    const int nz = p->nz;
+    unsigned nthreads = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+    nthreads = std::min<unsigned>(nthreads, (unsigned)nz);
+    std::vector<LinkList> parts(nthreads);
+    std::vector<int64_t> counts(nthreads, 0);
+    const bool walls_x = p->face_kind[0] == LBM_FACE_WALL;
+    const bool walls_y = p->face_kind[2] == LBM_FACE_WALL;
+    const bool walls_z = p->face_kind[4] == LBM_FACE_WALL;
+
+    auto work = [&](unsigned tid) {
+        const int z0 = (int)((int64_t)nz * tid / nthreads), z1 = (int)((int64_t)nz * (tid + 1) / nthreads);
+        LinkList& L = parts[tid];
+        int64_t cnt = 0;
+        for (int z = z0; z < z1; ++z)
+            for (int y = 0; y < p->ny; ++y)
+                for (int x = 0; x < p->nx; ++x) {
+                    const int32_t cell = x + p->nx * (y + p->ny * z);
+                    if (labels && labels[cell]) continue;
+                    const bool edge = (walls_x && (x == 0 || x == p->nx - 1)) ||
+                                      (walls_y && (y == 0 || y == p->ny - 1)) ||
+                                      (walls_z && (z == 0 || z == nz - 1));
+                    if (!edge && !labels) continue;
+                    for (size_t i = 0; i < dirs.size(); ++i) {
+                        int32_t image;
+                        const int grp = blocked_group(p, labels, x, y, z, dirs[i].c, &image);
+                        if (grp < 0) continue;
+                        ++cnt;
+                        if (!out) continue;
+                        uint32_t meta = (uint32_t)(i + 1) | ((uint32_t)grp << LINK_GROUP_SHIFT);
+                        if (d3q7) {
+                            const int dir = grp < 6 ? p->face_thermal[grp] : p->solid_thermal;
+                            if (dir == LBM_DIRICHLET) meta |= LINK_DIRICHLET;
+                        }
+                        L.cell.push_back(cell);
+                        L.cellw.push_back(image);
+                        L.meta.push_back(meta);
+                    }
+                }
+        counts[tid] = cnt;
+    };
+    std::vector<std::thread> pool;
+    for (unsigned t = 1; t < nthreads; ++t) pool.emplace_back(work, t);
+    work(0);
+    for (auto& th : pool) th.join();
+    int64_t total = 0;
+    for (auto c : counts) total += c;
+    if (!out) return total;
+
+    // stable counting sort by group
+    std::vector<int64_t> bucket(LBM_MAX_GROUPS + 1, 0);
+    for (auto& L : parts)
+        for (uint32_t m : L.meta) ++bucket[((m >> LINK_GROUP_SHIFT) & LINK_GROUP_MASK) + 1];
+    for (int g = 0; g < LBM_MAX_GROUPS; ++g) bucket[g + 1] += bucket[g];
+    out->cell.resize(total);
+    out->cellw.resize(total);
+    out->meta.resize(total);
+    for (auto& L : parts)
+        for (size_t i = 0; i < L.meta.size(); ++i) {
+            const int64_t pos = bucket[(L.meta[i] >> LINK_GROUP_SHIFT) & LINK_GROUP_MASK]++;
+            out->cell[pos] = L.cell[i];
+            out->cellw[pos] = L.cellw[i];
+            out->meta[pos] = L.meta[i];
+        }
+    return total;
+}
+
+bool any_solid(const lbm_params* p, const uint8_t* labels)
+{
+    if (!labels) return false;
+    const int64_t n = (int64_t)p->nx * p->ny * p->nz;
+    for (int64_t i = 0; i < n; ++i)
+        if (labels[i]) return true;
+    return false;
+}
+
+struct Layout {
+    size_t f, g, f2, g2, labels, lcell, lcellw, lmeta, scratch, wall_T, accum, unstable, total;
+    int64_t stride;
+};
+
+Layout make_layout(const lbm_params* p, bool solids, int64_t n_links)
+{
+    Layout L{};
+    const int64_t n = (int64_t)p->nx * p->ny * p->nz;
+    L.stride = (n + 63) / 64 * 64;
+    const size_t es = (size_t)p->dtype;
+    const size_t fb = align_up(19 * (size_t)L.stride * es);
+    const size_t gb = p->thermal ? align_up(7 * (size_t)L.stride * es) : 0;
+    const bool ab = p->streaming == LBM_STREAM_AB;
+    size_t off = 0;
+    L.f = off; off += fb;
+    L.g = off; off += gb;
+    L.f2 = off; off += ab ? fb : 0;
+    L.g2 = off; off += ab ? gb : 0;
+    L.labels = off; off += solids ? align_up((size_t)n) : 0;
+    L.lcell = off; off += align_up(4 * (size_t)n_links);
+    L.lcellw = off; off += align_up(4 * (size_t)n_links);
+    L.lmeta = off; off += align_up(4 * (size_t)n_links);
+    L.scratch = off; off += align_up(es * (size_t)n_links);
+    L.wall_T = off; off += align_up(8 * LBM_MAX_GROUPS);
+    L.accum = off; off += align_up(8 * 4 * LBM_MAX_GROUPS);
+    L.unstable = off; off += ALIGN;
+    L.total = off;
+    return L;
+}
+
+lbm_status device_error(lbm_ctx* ctx, hipError_t e, const char* what)
+{
+    ctx->err = std::string(what) + ": " + hipGetErrorString(e);
+    return LBM_E_DEVICE;
+}
+
+#define LBM_HIP(ctx, call, what)                              \
+    do {                                                      \
+        hipError_t e_ = (call);                               \
+        if (e_ != hipSuccess) return device_error(ctx, e_, what); \
+    } while (0)
+
+template <typename R>
+LinkArgs<R> link_args(lbm_ctx* c, int mode, bool accumulate, char* fsrc, char* fdst, char* gsrc, char* gdst)
+{
+    LinkArgs<R> a{};
+    a.geo = c->geo;
+    a.cell = c->lcell;
+    a.cellw = c->lcellw;
+    a.meta = c->lmeta;
+    a.scratch = (R*)c->scratch;
+    a.wall_T = c->wall_T;
+    a.accum = c->accum;
+    a.f_src = (R*)fsrc;
+    a.f_dst = (R*)fdst;
+    a.g_src = (R*)gsrc;
+    a.g_dst = (R*)gdst;
+    a.n_f = c->n_f;
+    a.n_total = c->n_f + c->n_g;
+    a.omega = (6.0 + c->p.a_T) / 21.0;
+    a.mode = mode;
+    a.accumulate = accumulate ? 1 : 0;
+    return a;
+}
+
+template <typename R>
+const Collision<R>& collision(const lbm_ctx* c);
+template <>
+const Collision<float>& collision<float>(const lbm_ctx* c) { return c->colf; }
+template <>
+const Collision<double>& collision<double>(const lbm_ctx* c) { return c->cold; }
+
+template <typename R>
+lbm_status step_impl(lbm_ctx* c, int64_t n)
+{
+    const bool links = (c->n_f + c->n_g) > 0;
+    for (int64_t k = 0; k < n; ++k) {
+        const bool last = (k == n - 1);
+        if (last) LBM_HIP(c, launch_zero_f64(c->accum, 4 * LBM_MAX_GROUPS, c->stream), "zero accumulators");
+        const int parity = (int)(c->t & 1);
+        StepArgs<R> s{};
+        s.geo = c->geo;
+        s.col = collision<R>(c);
+        if (!c->ab) {
+            s.f = (R*)c->f;
+            s.g = (R*)c->g;
+            s.parity = parity;
+            LBM_HIP(c, launch_aa_step<R>(s, c->thermal, c->stream), "AA step kernel");
+            if (links) {
+                const int mode = parity == 0 ? LINK_AA_AFTER_EVEN : LINK_AA_AFTER_ODD;
+                LinkArgs<R> la = link_args<R>(c, mode, last, c->f, c->f, c->g, c->g);
+                LBM_HIP(c, launch_link_gather<R>(la, c->stream), "link gather kernel");
+                LBM_HIP(c, launch_link_scatter<R>(la, c->stream), "link scatter kernel");
+            }
+        } else {
+            char* fa = parity ? c->f2 : c->f;
+            char* fb = parity ? c->f : c->f2;
+            char* ga = parity ? c->g2 : c->g;
+            char* gb = parity ? c->g : c->g2;
+            s.f = (R*)fa;
+            s.g = (R*)ga;
+            s.f2 = (R*)fb;
+            s.g2 = (R*)gb;
+            LBM_HIP(c, launch_ab_collide<R>(s, c->thermal, c->stream), "A-B collide kernel");
+            LBM_HIP(c, launch_ab_pull<R>(s, c->thermal, c->stream), "A-B pull kernel");
+            if (links) {
+                LinkArgs<R> la = link_args<R>(c, LINK_AB, last, fa, fb, ga, gb);
+                LBM_HIP(c, launch_link_gather<R>(la, c->stream), "link gather kernel");
+                LBM_HIP(c, launch_link_scatter<R>(la, c->stream), "link scatter kernel");
+            }
+        }
+        c->t += 1;
+    }
+    return LBM_OK;
+}
+
+template <typename R>
+FieldArgs<R> field_args(lbm_ctx* c)
+{
+    FieldArgs<R> a{};
+    a.geo = c->geo;
+    const bool second = c->ab && (c->t & 1);
+    a.f = (R*)(second ? c->f2 : c->f);
+    a.g = (R*)(second ? c->g2 : c->g);
+    a.labels = c->labels;
+    a.unstable = c->unstable;
+    a.parity = (int32_t)(c->t & 1);
+    a.ab = c->ab ? 1 : 0;
+    a.col = collision<R>(c);
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lbm_required_bytes(const lbm_params* p, const uint8_t* solid_labels)
+{
+    try {
+        if (!validate(p).empty()) return 0;
+        const bool solids = any_solid(p, solid_labels);
+        const uint8_t* lab = solids ? solid_labels : nullptr;
+        int64_t nl = build_links(p, lab, false, nullptr);
+        if (p->thermal) nl += build_links(p, lab, true, nullptr);
+        return make_layout(p, solids, nl).total;
+    } catch (...) {
+        return 0;
+    }
+}
+
+lbm_status lbm_create(const lbm_params* p, const uint8_t* solid_labels, void* device_buf, size_t device_bytes,
+                      void* hip_stream, lbm_ctx** out)
+{
+    if (out) *out = nullptr;
+    g_create_error.clear();
+    if (!out) {
+        g_create_error = "out is NULL";
+        return LBM_E_INVALID;
+    }
+    const std::string why = validate(p);
+    if (!why.empty()) {
+        g_create_error = why;
+        return LBM_E_INVALID;
+    }
+    if (!device_buf) {
+        g_create_error = "device_buf is NULL";
+        return LBM_E_INVALID;
+    }
+    lbm_ctx* c = nullptr;
+    try {
+        c = new lbm_ctx();
+        c->p = *p;
+        c->es = p->dtype;
+        c->thermal = p->thermal != 0;
+        c->ab = p->streaming == LBM_STREAM_AB;
+        c->stream = (hipStream_t)hip_stream;
+        const bool solids = any_solid(p, solid_labels);
+        const uint8_t* lab = solids ? solid_labels : nullptr;
+        LinkList lf, lg;
+        c->n_f = build_links(p, lab, false, &lf);
+        c->n_g = c->thermal ? build_links(p, lab, true, &lg) : 0;
+        const int64_t nl = c->n_f + c->n_g;
+        const Layout L = make_layout(p, solids, nl);
+        if (device_bytes < L.total) {
+            g_create_error = "device_bytes " + std::to_string(device_bytes) + " < required " + std::to_string(L.total);
+            delete c;
+            return LBM_E_NOMEM;
+        }
+        if (((uintptr_t)device_buf) % ALIGN) {
+            g_create_error = "device_buf must be 256-byte aligned";
+            delete c;
+            return LBM_E_INVALID;
+        }
+        Geometry& G = c->geo;
+        G.nx = p->nx;
+        G.ny = p->ny;
+        G.nz = p->nz;
+        G.nxy = p->nx * p->ny;
+        G.ncell = G.nxy * p->nz;
+        G.stride = L.stride;
+        G.div_nx = make_magic((uint32_t)p->nx);
+        G.div_ny = make_magic((uint32_t)p->ny);
+        if (!magic_ok(G.div_nx, (uint32_t)G.ncell) || !magic_ok(G.div_ny, (uint32_t)G.ncell)) {
+            g_create_error = "internal: division constants failed their self-check";
+            delete c;
+            return LBM_E_INVALID;
+        }
+        char* base = (char*)device_buf;
+        c->f = base + L.f;
+        c->g = c->thermal ? base + L.g : nullptr;
+        c->f2 = c->ab ? base + L.f2 : nullptr;
+        c->g2 = (c->ab && c->thermal) ? base + L.g2 : nullptr;
+        c->labels = solids ? (uint8_t*)(base + L.labels) : nullptr;
+        c->lcell = (int32_t*)(base + L.lcell);
+        c->lcellw = (int32_t*)(base + L.lcellw);
+        c->lmeta = (uint32_t*)(base + L.lmeta);
+        c->scratch = base + L.scratch;
+        c->wall_T = (double*)(base + L.wall_T);
+        c->accum = (double*)(base + L.accum);
+        c->unstable = (int32_t*)(base + L.unstable);
+        c->colf = make_collision<float>(p);
+        c->cold = make_collision<double>(p);
+
+        // concatenate D3Q19 then D3Q7 links and upload
+        std::vector<int32_t> cell(nl), cellw(nl);
+        std::vector<uint32_t> meta(nl);
+        std::copy(lf.cell.begin(), lf.cell.end(), cell.begin());
+        std::copy(lf.cellw.begin(), lf.cellw.end(), cellw.begin());
+        std::copy(lf.meta.begin(), lf.meta.end(), meta.begin());
+        std::copy(lg.cell.begin(), lg.cell.end(), cell.begin() + c->n_f);
+        std::copy(lg.cellw.begin(), lg.cellw.end(), cellw.begin() + c->n_f);
+        std::copy(lg.meta.begin(), lg.meta.end(), meta.begin() + c->n_f);
+        std::vector<double> wallT(LBM_MAX_GROUPS, 0.0);
+        for (int f = 0; f < 6; ++f) wallT[f] = p->face_T[f];
+        for (int gidx = 6; gidx < LBM_MAX_GROUPS; ++gidx) wallT[gidx] = p->solid_T;
+        hipError_t e = hipSuccess;
+        if (nl > 0) {
+            if (e == hipSuccess) e = hipMemcpyAsync(c->lcell, cell.data(), 4 * nl, hipMemcpyHostToDevice, c->stream);
+            if (e == hipSuccess) e = hipMemcpyAsync(c->lcellw, cellw.data(), 4 * nl, hipMemcpyHostToDevice, c->stream);
+            if (e == hipSuccess) e = hipMemcpyAsync(c->lmeta, meta.data(), 4 * nl, hipMemcpyHostToDevice, c->stream);
+        }
+        if (e == hipSuccess && solids)
+            e = hipMemcpyAsync(c->labels, solid_labels, (size_t)G.ncell, hipMemcpyHostToDevice, c->stream);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(c->wall_T, wallT.data(), 8 * LBM_MAX_GROUPS, hipMemcpyHostToDevice, c->stream);
+        if (e == hipSuccess) e = launch_zero_f64(c->accum, 4 * LBM_MAX_GROUPS, c->stream);
+        if (e == hipSuccess) e = launch_zero_f64((double*)c->unstable, 1, c->stream);  // flag sits in a 256-B slot
+        // the host vectors die at return: wait for the copies
+        if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+        if (e != hipSuccess) {
+            g_create_error = std::string("upload: ") + hipGetErrorString(e);
+            delete c;
+            return LBM_E_DEVICE;
+        }
+        *out = c;
+        return LBM_OK;
+    } catch (const std::bad_alloc&) {
+        g_create_error = "host allocation failed";
+    } catch (const std::exception& ex) {
+        g_create_error = ex.what();
+    } catch (...) {
+        g_create_error = "unknown error";
+    }
+    delete c;
+    return LBM_E_INVALID;
+}
+
+lbm_status lbm_init_fields(lbm_ctx* c, const void* rho, const void* u, const void* T)
+{
+    if (!c) return LBM_E_INVALID;
+    if (!rho || !u) {
+        c->err = "rho and u are required";
+        return LBM_E_INVALID;
+    }
+    c->t = 0;
+    hipError_t e;
+    if (c->es == 4) {
+        FieldArgs<float> a = field_args<float>(c);
+        a.rho = (const float*)rho;
+        a.u = (const float*)u;
+        a.T = (const float*)T;
+        e = launch_init<float>(a, c->thermal, c->stream);
+    } else {
+        FieldArgs<double> a = field_args<double>(c);
+        a.rho = (const double*)rho;
+        a.u = (const double*)u;
+        a.T = (const double*)T;
+        e = launch_init<double>(a, c->thermal, c->stream);
+    }
+    if (e != hipSuccess) return device_error(c, e, "init kernel");
+    c->initialised = true;
+    return LBM_OK;
+}
+
+lbm_status lbm_step(lbm_ctx* c, int64_t n)
+{
+    if (!c) return LBM_E_INVALID;
+    if (n < 0) {
+        c->err = "n must be >= 0";
+        return LBM_E_INVALID;
+    }
+    if (!c->initialised) {
+        c->err = "lbm_init_fields has not been called";
+        return LBM_E_INVALID;
+    }
+    if (n == 0) return LBM_OK;
+    return c->es == 4 ? step_impl<float>(c, n) : step_impl<double>(c, n);
+}
+
+lbm_status lbm_read_macros(lbm_ctx* c, void* rho, void* u, void* T)
+{
+    if (!c) return LBM_E_INVALID;
+    if (!c->initialised) {
+        c->err = "lbm_init_fields has not been called";
+        return LBM_E_INVALID;
+    }
+    hipError_t e;
+    if (c->es == 4) {
+        FieldArgs<float> a = field_args<float>(c);
+        a.rho_out = (float*)rho;
+        a.u_out = (float*)u;
+        a.T_out = (float*)T;
+        e = launch_read<float>(a, c->thermal, c->stream);
+    } else {
+        FieldArgs<double> a = field_args<double>(c);
+        a.rho_out = (double*)rho;
+        a.u_out = (double*)u;
+        a.T_out = (double*)T;
+        e = launch_read<double>(a, c->thermal, c->stream);
+    }
+    if (e != hipSuccess) return device_error(c, e, "read kernel");
+    return LBM_OK;
+}
+
+lbm_status lbm_wall_force(lbm_ctx* c, double* out, int32_t n_groups)
+{
+    if (!c) return LBM_E_INVALID;
+    if (n_groups < 0 || (n_groups > 0 && !out)) {
+        c->err = "bad output buffer";
+        return LBM_E_INVALID;
+    }
+    std::vector<double> acc(4 * LBM_MAX_GROUPS, 0.0);
+    int32_t unstable = 0;
+    LBM_HIP(c, hipMemcpyAsync(acc.data(), c->accum, 8 * 4 * LBM_MAX_GROUPS, hipMemcpyDeviceToHost, c->stream),
+            "copy accumulators");
+    LBM_HIP(c, hipMemcpyAsync(&unstable, c->unstable, sizeof(int32_t), hipMemcpyDeviceToHost, c->stream),
+            "copy flag");
+    LBM_HIP(c, hipStreamSynchronize(c->stream), "synchronise");
+    for (int32_t i = 0; i < n_groups; ++i)
+        for (int k = 0; k < 4; ++k) out[4 * i + k] = i < LBM_MAX_GROUPS ? acc[4 * i + k] : 0.0;
+    if (unstable) {
+        c->err = "a fluid cell's rho, u or T was not finite at a read-back";
+        return LBM_E_UNSTABLE;
+    }
+    return LBM_OK;
+}
+
+int64_t lbm_time(const lbm_ctx* c) { return c ? c->t : -1; }
+
+int64_t lbm_count_links(const lbm_params* p, const uint8_t* solid_labels, int32_t lattice)
+{
+    try {
+        if (!validate(p).empty() || (lattice != 19 && lattice != 7)) return -1;
+        const uint8_t* lab = any_solid(p, solid_labels) ? solid_labels : nullptr;
+        return build_links(p, lab, lattice == 7, nullptr);
+    } catch (...) {
+        return -1;
+    }
+}
+
+int64_t lbm_num_links(const lbm_ctx* c, int32_t lattice)
+{
+    if (!c) return -1;
+    if (lattice == 19) return c->n_f;
+    if (lattice == 7) return c->n_g;
+    return -1;
+}
+
+const char* lbm_last_error(const lbm_ctx* c) { return c ? c->err.c_str() : g_create_error.c_str(); }
+
+void lbm_destroy(lbm_ctx* c) { delete c; }
+
+}  // extern "C"

@@ -1,0 +1,115 @@
+// lbm_internal.hpp -- launch descriptors shared by the C-ABI host code and
+// the kernels of liblbm_hip.so (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lbm_lattice.hpp"
+
+namespace lbm {
+
+// Unsigned division by a run-time constant d >= 1 for numerators < 2^31:
+// n / d == (n * mul) >> shift with mul = ceil(2^(31+l) / d), shift = 31 + l,
+// l = ceil(log2 d) (Granlund-Montgomery round-up method).
+struct DivMagic {
+    uint64_t mul;
+    uint32_t shift;
+    uint32_t d;
+};
+
+__host__ __device__ inline uint32_t divide(uint32_t n, const DivMagic& m)
+{
+    return (uint32_t)(((uint64_t)n * m.mul) >> m.shift);
+}
+
+// Box geometry as the kernels see it.
+struct Geometry {
+    int32_t nx, ny, nz;
+    int32_t nxy;
+    int32_t ncell;
+    int32_t pad0;
+    int64_t stride;  // elements between consecutive population planes
+    DivMagic div_nx, div_ny;
+};
+
+// Link record (structure of arrays):
+//   cell  : the fluid cell x of the link
+//   cellw : the periodic image of x + c_p (where the population lands)
+//   meta  : bits 0..4 direction p (kernel order of the lattice),
+//           bits 5..13 force/heat group, bit 14 Dirichlet (D3Q7 only)
+// Links [0, n_f) belong to D3Q19, [n_f, n_f + n_g) to D3Q7.
+constexpr uint32_t LINK_DIR_MASK = 31u;
+constexpr uint32_t LINK_GROUP_SHIFT = 5;
+constexpr uint32_t LINK_GROUP_MASK = 511u;
+constexpr uint32_t LINK_DIRICHLET = 1u << 14;
+
+// Which slots a link pass reads and writes.
+enum LinkMode : int32_t {
+    LINK_AA_AFTER_EVEN = 0,  // src (opp p, x), dst (p, x + c_p)
+    LINK_AA_AFTER_ODD = 1,   // src (p, x + c_p), dst (opp p, x)
+    LINK_AB = 2,             // src A(p, x) post-collision, dst B(opp p, x)
+};
+
+template <typename R>
+struct StepArgs {
+    Geometry geo;
+    R* f;  // D3Q19 populations (AA: the only buffer; AB: source/in-place buffer)
+    R* g;  // D3Q7 populations or null
+    R* f2; // AB: destination buffer of the pull
+    R* g2;
+    int32_t parity;
+    int32_t pad0;
+    Collision<R> col;
+};
+
+template <typename R>
+struct LinkArgs {
+    Geometry geo;
+    const int32_t* cell;
+    const int32_t* cellw;
+    const uint32_t* meta;
+    R* scratch;
+    const double* wall_T;  // per group: Dirichlet temperature
+    double* accum;         // per group: Fx, Fy, Fz, Q
+    R* f_src;
+    R* f_dst;
+    R* g_src;
+    R* g_dst;
+    int64_t n_f;
+    int64_t n_total;
+    double omega;          // (6 + a_T)/21
+    int32_t mode;
+    int32_t accumulate;
+};
+
+template <typename R>
+struct FieldArgs {
+    Geometry geo;
+    R* f;
+    R* g;
+    const uint8_t* labels;  // null when there are no solids
+    const R* rho;
+    const R* u;
+    const R* T;
+    R* rho_out;
+    R* u_out;
+    R* T_out;
+    int32_t* unstable;
+    int32_t parity;
+    int32_t ab;  // populations in natural layout (two-buffer mode)
+    Collision<R> col;
+};
+
+// Launch wrappers (defined in lbm_kernels.hip).  Each returns the HIP error
+// of the launch.
+template <typename R> hipError_t launch_aa_step(const StepArgs<R>& a, bool thermal, hipStream_t s);
+template <typename R> hipError_t launch_ab_collide(const StepArgs<R>& a, bool thermal, hipStream_t s);
+template <typename R> hipError_t launch_ab_pull(const StepArgs<R>& a, bool thermal, hipStream_t s);
+template <typename R> hipError_t launch_link_gather(const LinkArgs<R>& a, hipStream_t s);
+template <typename R> hipError_t launch_link_scatter(const LinkArgs<R>& a, hipStream_t s);
+template <typename R> hipError_t launch_init(const FieldArgs<R>& a, bool thermal, hipStream_t s);
+template <typename R> hipError_t launch_read(const FieldArgs<R>& a, bool thermal, hipStream_t s);
+hipError_t launch_zero_f64(double* p, int64_t n, hipStream_t s);
+
+}  // namespace lbm

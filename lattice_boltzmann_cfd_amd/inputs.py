@@ -278,11 +278,14 @@ def cavity256(shape=(256, 256, 256), Ra=1e7, Pr=0.71, H=256) -> Workload:
     return Workload("cavity256", p, rho, u, T, None, 5000, dict(scales=sc, Ra=Ra, Pr=Pr, H=H))
 
 
-def rb512(shape=(512, 512, 512), Ra=1e8, Pr=0.71, H=512, seed=5) -> Workload:
+def rb512(shape=(512, 512, 512), Ra=1e8, Pr=0.71, H=512, seed=5, rmin=4, rmax=12) -> Workload:
+    """Reduced boxes keep the recipe; the largest radius is clamped to
+    (nz - 1)//2 - 1 so that a sphere fits between the plates."""
     nx, ny, nz = shape
     sc = thermal_scales(H, Ra, Pr)
     rho, u, T = rest(nx, ny, nz)
-    lab, spheres = random_spheres(nx, ny, nz, seed=seed)
+    rmax = max(rmin, min(rmax, (nz - 1) // 2 - 1))
+    lab, spheres = random_spheres(nx, ny, nz, rmin=rmin, rmax=rmax, seed=seed)
     p = base_params(
         nx, ny, nz, mrt_rates(sc["tau"]), thermal=True,
         face_kind=[FACE_PERIODIC, FACE_PERIODIC, FACE_PERIODIC, FACE_PERIODIC, FACE_WALL, FACE_WALL],

@@ -1,0 +1,94 @@
+"""Shared helpers of the GPU tests: run a workload through the C ABI (HIP
+kernels) and through the CPU oracle on the same seeded inputs."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+from lattice_boltzmann_cfd_amd import binding, inputs
+
+
+def say(*args):
+    print(*args, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_run(w: inputs.Workload, submissions, dtype=4, streaming=binding.LBM_STREAM_AUTO, want_forces=True):
+    """Run the submissions (a list of step counts) on the GPU; returns the
+    macros at the end (fp64 numpy) and the latched forces after each one."""
+    import torch
+
+    thermal = bool(w.params.get("thermal"))
+    s = binding.Solver(w.params, w.labels, dtype=dtype, streaming=streaming)
+    try:
+        s.init(w.rho, w.u, w.T if thermal else None)
+        forces = []
+        for n in submissions:
+            s.step(n)
+            if want_forces:
+                forces.append(s.wall_force())
+        rho, u, T = s.macros()
+        torch.cuda.synchronize()
+        out = dict(rho=rho.cpu().double().numpy(), u=u.cpu().double().numpy(),
+                   T=T.cpu().double().numpy() if T is not None else None, forces=forces, time=s.time,
+                   links19=s.num_links(19), links7=s.num_links(7))
+        s.wall_force()  # raises LBM_E_UNSTABLE if the read-back saw a non-finite value
+        return out
+    finally:
+        s.close()
+
+
+def oracle_run(w: inputs.Workload, steps, want_diag=False, window=None):
+    thermal = bool(w.params.get("thermal"))
+    if window is None:
+        return oracle.run(w.params, steps, w.rho, w.u, w.T if thermal else None, labels=w.labels,
+                          want_diag=want_diag)
+    lo, n = window
+    idx = window_indices(w.shape, lo, n)
+    T = w.T[idx] if thermal else None
+    return oracle.run(w.params, steps, w.rho[idx], w.u[:, idx], T, labels=w.labels, window=window)
+
+
+def window_indices(shape, lo, n):
+    nx, ny, nz = shape
+    z = (lo[2] + np.arange(n[2])) % nz
+    y = (lo[1] + np.arange(n[1])) % ny
+    x = (lo[0] + np.arange(n[0])) % nx
+    Z, Y, X = np.meshgrid(z, y, x, indexing="ij")
+    return (X + nx * (Y + ny * Z)).reshape(-1)
+
+
+def window_valid(params, lo, n, steps):
+    """Mask of window cells that no NaN from a cut window edge can reach in `steps` steps."""
+    shape = (params["nx"], params["ny"], params["nz"])
+    masks = []
+    for a in range(3):
+        i = np.arange(n[a])
+        if n[a] == shape[a]:
+            m = np.ones(n[a], bool)
+        else:
+            wall = params["face_kind"][2 * a] == 1
+            lo_cut = not (wall and lo[a] == 0)
+            hi_cut = not (wall and lo[a] + n[a] == shape[a])
+            m = np.ones(n[a], bool)
+            if lo_cut:
+                m &= i >= steps
+            if hi_cut:
+                m &= i < n[a] - steps
+        masks.append(m)
+    Z, Y, X = np.meshgrid(masks[2], masks[1], masks[0], indexing="ij")
+    return (X & Y & Z).reshape(-1)
+
+
+def max_diffs(g, o, mask):
+    d = dict(rho=np.abs(g["rho"][mask] - o["rho"][mask]).max(),
+             u=np.abs(g["u"][:, mask] - o["u"][:, mask]).max())
+    if g.get("T") is not None:
+        d["T"] = np.abs(g["T"][mask] - o["T"][mask]).max()
+    return d
+
+
+def fluid_mask(w):
+    return np.ones(w.cells, bool) if w.labels is None else (w.labels == 0)
