@@ -71,6 +71,32 @@ def load_traffic(workload: str, dtype: int, streaming: int):
     return rec.get("hbm_bytes_per_launch")
 
 
+def device_ceilings(nbytes: int = 19 * (1 << 24) * 4, reps: int = 10):
+    """Bandwidth of torch's own device copy (read A, write B) and in-place
+    multiply (read and write A) on buffers the size of the 256^3 D3Q19 fp32
+    population array: the practical ceilings of a copy-like and of an
+    in-place access pattern on this GPU."""
+    import torch
+
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    out = {}
+    for name, fn in (("copy", lambda: b.copy_(a)), ("inplace_rmw", lambda: a.mul_(1.0))):
+        for _ in range(3):
+            fn()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        out[name + "_GBps"] = round(2 * nbytes * reps / (s.elapsed_time(e) / 1e3) / 1e9, 1)
+    del a, b
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, steps: int):
     import oracle
 
@@ -94,6 +120,8 @@ def main(argv=None):
     ap.add_argument("--dtype", type=int, default=4, choices=(4, 8))
     ap.add_argument("--streaming", type=int, default=1, choices=(1, 2), help="1 in place (AA), 2 two buffers")
     ap.add_argument("--cpu-steps", type=int, default=6, help="oracle steps for the CPU baseline (0: skip)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run torch's device copy of 1 GiB 10 times (reference kernel for HBM counters)")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -103,6 +131,17 @@ def main(argv=None):
         return 2
 
     import torch
+
+    if args.calibrate_copy:
+        # a plain copy of known size: 1 GiB read and 1 GiB written per dispatch
+        a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(10):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read": a.numel() * 4, "bytes_written": b.numel() * 4,
+                          "dispatches": 10}), flush=True)
+        return 0
 
     from lattice_boltzmann_cfd_amd import binding, inputs
 
@@ -152,7 +191,9 @@ def main(argv=None):
         "roofline": roofline,
     }
     solver.close()
-    del rho
+    del rho, solver
+    torch.cuda.empty_cache()
+    roofline["practical"] = device_ceilings()
     if args.cpu_steps > 0:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_steps)
     print(json.dumps(line), flush=True)
