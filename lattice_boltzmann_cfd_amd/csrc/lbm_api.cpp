@@ -36,7 +36,7 @@ struct lbm_ctx {
     double* wall_T = nullptr;
     double* accum = nullptr;
     int32_t* unstable = nullptr;
-    int64_t n_f = 0, n_g = 0;
+    int64_t n_f = 0, n_g = 0, n_wall = 0;
     int64_t t = 0;
     bool initialised = false;
     std::string err;
@@ -224,6 +224,7 @@ int64_t build_links(const lbm_params* p, const uint8_t* labels, bool d3q7, LinkL
                         if (!out) continue;
                         uint32_t meta = (uint32_t)(i + 1) | ((uint32_t)grp << LINK_GROUP_SHIFT);
                         if (d3q7) {
+                            meta |= LINK_D3Q7;
                             const int dir = grp < 6 ? p->face_thermal[grp] : p->solid_thermal;
                             if (dir == LBM_DIRICHLET) meta |= LINK_DIRICHLET;
                         }
@@ -242,22 +243,47 @@ int64_t build_links(const lbm_params* p, const uint8_t* labels, bool d3q7, LinkL
     for (auto c : counts) total += c;
     if (!out) return total;
 
-    // stable counting sort by group
-    std::vector<int64_t> bucket(LBM_MAX_GROUPS + 1, 0);
-    for (auto& L : parts)
-        for (uint32_t m : L.meta) ++bucket[((m >> LINK_GROUP_SHIFT) & LINK_GROUP_MASK) + 1];
-    for (int g = 0; g < LBM_MAX_GROUPS; ++g) bucket[g + 1] += bucket[g];
+    out->cell.reserve(total);
+    out->cellw.reserve(total);
+    out->meta.reserve(total);
+    for (auto& L : parts) {
+        out->cell.insert(out->cell.end(), L.cell.begin(), L.cell.end());
+        out->cellw.insert(out->cellw.end(), L.cellw.begin(), L.cellw.end());
+        out->meta.insert(out->meta.end(), L.meta.begin(), L.meta.end());
+    }
+    return total;
+}
+
+// Order both lattices' links for the passes: a stable counting sort by
+// (group, lattice, direction) keeps cell order inside each bucket, so wall
+// links (groups 0..5) come first and neighbouring lanes of a wavefront read
+// one population plane at nearby cells, and a wavefront rarely spans two
+// groups (the force reduction).
+int64_t order_links(const LinkList& f, const LinkList& g, LinkList* out)
+{
+    constexpr int NB = LBM_MAX_GROUPS * 2 * 32;
+    auto bucket_of = [](uint32_t m) {
+        const uint32_t grp = (m >> LINK_GROUP_SHIFT) & LINK_GROUP_MASK;
+        return (int)((grp * 2 + ((m & LINK_D3Q7) ? 1 : 0)) * 32 + (m & LINK_DIR_MASK));
+    };
+    std::vector<int64_t> start(NB + 1, 0);
+    for (const LinkList* L : {&f, &g})
+        for (uint32_t m : L->meta) ++start[bucket_of(m) + 1];
+    for (int b = 0; b < NB; ++b) start[b + 1] += start[b];
+    const int64_t total = start[NB];
     out->cell.resize(total);
     out->cellw.resize(total);
     out->meta.resize(total);
-    for (auto& L : parts)
-        for (size_t i = 0; i < L.meta.size(); ++i) {
-            const int64_t pos = bucket[(L.meta[i] >> LINK_GROUP_SHIFT) & LINK_GROUP_MASK]++;
-            out->cell[pos] = L.cell[i];
-            out->cellw[pos] = L.cellw[i];
-            out->meta[pos] = L.meta[i];
+    for (const LinkList* L : {&f, &g})
+        for (size_t i = 0; i < L->meta.size(); ++i) {
+            const int64_t pos = start[bucket_of(L->meta[i])]++;
+            out->cell[pos] = L->cell[i];
+            out->cellw[pos] = L->cellw[i];
+            out->meta[pos] = L->meta[i];
         }
-    return total;
+    int64_t n_wall = 0;
+    while (n_wall < total && ((out->meta[n_wall] >> LINK_GROUP_SHIFT) & LINK_GROUP_MASK) < 6) ++n_wall;
+    return n_wall;
 }
 
 bool any_solid(const lbm_params* p, const uint8_t* labels)
@@ -327,8 +353,8 @@ LinkArgs<R> link_args(lbm_ctx* c, int mode, bool accumulate, char* fsrc, char* f
     a.f_dst = (R*)fdst;
     a.g_src = (R*)gsrc;
     a.g_dst = (R*)gdst;
-    a.n_f = c->n_f;
-    a.n_total = c->n_f + c->n_g;
+    a.begin = 0;
+    a.end = c->n_f + c->n_g;
     a.omega = (6.0 + c->p.a_T) / 21.0;
     a.mode = mode;
     a.accumulate = accumulate ? 1 : 0;
@@ -361,8 +387,15 @@ lbm_status step_impl(lbm_ctx* c, int64_t n)
             if (links) {
                 const int mode = parity == 0 ? LINK_AA_AFTER_EVEN : LINK_AA_AFTER_ODD;
                 LinkArgs<R> la = link_args<R>(c, mode, last, c->f, c->f, c->g, c->g);
+                // wall links: gather every source, then scatter
+                la.begin = 0;
+                la.end = c->n_wall;
                 LBM_HIP(c, launch_link_gather<R>(la, c->stream), "link gather kernel");
                 LBM_HIP(c, launch_link_scatter<R>(la, c->stream), "link scatter kernel");
+                // solid links: one direct pass
+                la.begin = c->n_wall;
+                la.end = c->n_f + c->n_g;
+                LBM_HIP(c, launch_link_direct<R>(la, c->stream), "solid link kernel");
             }
         } else {
             char* fa = parity ? c->f2 : c->f;
@@ -376,9 +409,9 @@ lbm_status step_impl(lbm_ctx* c, int64_t n)
             LBM_HIP(c, launch_ab_collide<R>(s, c->thermal, c->stream), "A-B collide kernel");
             LBM_HIP(c, launch_ab_pull<R>(s, c->thermal, c->stream), "A-B pull kernel");
             if (links) {
+                // sources in one buffer, destinations in the other: one pass
                 LinkArgs<R> la = link_args<R>(c, LINK_AB, last, fa, fb, ga, gb);
-                LBM_HIP(c, launch_link_gather<R>(la, c->stream), "link gather kernel");
-                LBM_HIP(c, launch_link_scatter<R>(la, c->stream), "link scatter kernel");
+                LBM_HIP(c, launch_link_direct<R>(la, c->stream), "link kernel");
             }
         }
         c->t += 1;
@@ -493,15 +526,14 @@ lbm_status lbm_create(const lbm_params* p, const uint8_t* solid_labels, void* de
         c->colf = make_collision<float>(p);
         c->cold = make_collision<double>(p);
 
-        // concatenate D3Q19 then D3Q7 links and upload
-        std::vector<int32_t> cell(nl), cellw(nl);
-        std::vector<uint32_t> meta(nl);
-        std::copy(lf.cell.begin(), lf.cell.end(), cell.begin());
-        std::copy(lf.cellw.begin(), lf.cellw.end(), cellw.begin());
-        std::copy(lf.meta.begin(), lf.meta.end(), meta.begin());
-        std::copy(lg.cell.begin(), lg.cell.end(), cell.begin() + c->n_f);
-        std::copy(lg.cellw.begin(), lg.cellw.end(), cellw.begin() + c->n_f);
-        std::copy(lg.meta.begin(), lg.meta.end(), meta.begin() + c->n_f);
+        // order the links of both lattices and upload
+        LinkList all;
+        c->n_wall = order_links(lf, lg, &all);
+        lf = LinkList();
+        lg = LinkList();
+        std::vector<int32_t>& cell = all.cell;
+        std::vector<int32_t>& cellw = all.cellw;
+        std::vector<uint32_t>& meta = all.meta;
         std::vector<double> wallT(LBM_MAX_GROUPS, 0.0);
         for (int f = 0; f < 6; ++f) wallT[f] = p->face_T[f];
         for (int gidx = 6; gidx < LBM_MAX_GROUPS; ++gidx) wallT[gidx] = p->solid_T;

@@ -36,13 +36,16 @@ struct Geometry {
 // Link record (structure of arrays):
 //   cell  : the fluid cell x of the link
 //   cellw : the periodic image of x + c_p (where the population lands)
-//   meta  : bits 0..4 direction p (kernel order of the lattice),
-//           bits 5..13 force/heat group, bit 14 Dirichlet (D3Q7 only)
-// Links [0, n_f) belong to D3Q19, [n_f, n_f + n_g) to D3Q7.
+//   meta  : bits 0..4 direction p (kernel order of its lattice),
+//           bits 5..13 force/heat group, bit 14 Dirichlet (D3Q7 only),
+//           bit 15 the link belongs to the D3Q7 lattice
+// Links [0, n_wall) cross a wall face; [n_wall, n_total) end in a solid cell.
+// Each part is sorted by (group, lattice, direction, cell).
 constexpr uint32_t LINK_DIR_MASK = 31u;
 constexpr uint32_t LINK_GROUP_SHIFT = 5;
 constexpr uint32_t LINK_GROUP_MASK = 511u;
 constexpr uint32_t LINK_DIRICHLET = 1u << 14;
+constexpr uint32_t LINK_D3Q7 = 1u << 15;
 
 // Which slots a link pass reads and writes.
 enum LinkMode : int32_t {
@@ -76,8 +79,8 @@ struct LinkArgs {
     R* f_dst;
     R* g_src;
     R* g_dst;
-    int64_t n_f;
-    int64_t n_total;
+    int64_t begin;  // first link of the launch
+    int64_t end;    // one past the last link of the launch
     double omega;          // (6 + a_T)/21
     int32_t mode;
     int32_t accumulate;
@@ -108,6 +111,7 @@ template <typename R> hipError_t launch_ab_collide(const StepArgs<R>& a, bool th
 template <typename R> hipError_t launch_ab_pull(const StepArgs<R>& a, bool thermal, hipStream_t s);
 template <typename R> hipError_t launch_link_gather(const LinkArgs<R>& a, hipStream_t s);
 template <typename R> hipError_t launch_link_scatter(const LinkArgs<R>& a, hipStream_t s);
+template <typename R> hipError_t launch_link_direct(const LinkArgs<R>& a, hipStream_t s);
 template <typename R> hipError_t launch_init(const FieldArgs<R>& a, bool thermal, hipStream_t s);
 template <typename R> hipError_t launch_read(const FieldArgs<R>& a, bool thermal, hipStream_t s);
 hipError_t launch_zero_f64(double* p, int64_t n, hipStream_t s);

@@ -183,99 +183,163 @@ __device__ __forceinline__ double wave_sum(double v)
     return v;
 }
 
-// Gather: read every link's post-collision source into scratch.  On a
-// submission's last step, also sum the momentum exchange 2 c_p f_p^+ (D3Q19
-// links) and the heat w T_w - 2 g_p^+ (Dirichlet D3Q7 links) per group: a
-// wavefront whose links share one group reduces with shuffles and issues one
-// fp64 atomic per component; a mixed wavefront adds lane by lane.
-template <typename R>
-__global__ void __launch_bounds__(BLOCK) k_link_gather(LinkArgs<R> a)
+// The slots one link reads and writes.  p is the direction from the fluid
+// cell x towards the wall or solid; the population sent along p comes back
+// along opp(p).  In place, after an even step the collided f_p(x) sits in
+// (opp p, x) and must land where the next (odd) step reads f_opp(p)(x), which
+// is (p, x + c_p); after an odd step it sits in (p, x + c_p) and must land in
+// (opp p, x), which the next (even) step reads.  Two buffers: the collided
+// value is A(p, x) and the streamed one B(opp p, x).
+struct LinkSlots {
+    int32_t src_plane, src_idx, dst_plane, dst_idx;
+};
+
+__device__ __forceinline__ LinkSlots link_slots(int mode, int p, int32_t cell, int32_t cellw)
 {
-    const int64_t l = (int64_t)blockIdx.x * BLOCK + threadIdx.x;
-    const int64_t S = a.geo.stride;
-    double fx = 0.0, fy = 0.0, fz = 0.0, qh = 0.0;
-    int32_t grp = -1;
-    if (l < a.n_total) {
-        const bool isf = l < a.n_f;
-        const uint32_t meta = a.meta[l];
-        const int p = (int)(meta & LINK_DIR_MASK);
-        grp = (int32_t)((meta >> LINK_GROUP_SHIFT) & LINK_GROUP_MASK);
-        int32_t plane, idx;
-        if (a.mode == LINK_AA_AFTER_EVEN) {
-            plane = opp_rt(p);
-            idx = a.cell[l];
-        } else if (a.mode == LINK_AA_AFTER_ODD) {
-            plane = p;
-            idx = a.cellw[l];
-        } else {
-            plane = p;
-            idx = a.cell[l];
-        }
-        const R* src = isf ? a.f_src : a.g_src;
-        const R v = src[plane * S + idx];
-        a.scratch[l] = v;
-        if (a.accumulate) {
-            if (isf) {
-                const double fv = 2.0 * ((double)v + w19_rt(p));  // stored value is f - w
-                fx = dir_comp(CX19, p) * fv;
-                fy = dir_comp(CY19, p) * fv;
-                fz = dir_comp(CZ19, p) * fv;
-            } else if (meta & LINK_DIRICHLET) {
-                qh = a.omega * a.wall_T[grp] - 2.0 * (double)v;
-            }
-        }
+    LinkSlots s;
+    if (mode == LINK_AA_AFTER_EVEN) {
+        s.src_plane = opp_rt(p);
+        s.src_idx = cell;
+        s.dst_plane = p;
+        s.dst_idx = cellw;
+    } else if (mode == LINK_AA_AFTER_ODD) {
+        s.src_plane = p;
+        s.src_idx = cellw;
+        s.dst_plane = opp_rt(p);
+        s.dst_idx = cell;
+    } else {
+        s.src_plane = p;
+        s.src_idx = cell;
+        s.dst_plane = opp_rt(p);
+        s.dst_idx = cell;
     }
-    if (!a.accumulate) return;
+    return s;
+}
+
+// Per-link contribution to the group sums: the wall receives 2 c_p f_p^+
+// (D3Q19; the stored value is f - w), and a Dirichlet D3Q7 link passes
+// w T_w - 2 g_p^+ into the fluid.
+struct LinkSum {
+    double fx, fy, fz, q;
+};
+
+template <typename R>
+__device__ __forceinline__ LinkSum link_sum(const LinkArgs<R>& a, uint32_t meta, int p, int32_t grp, R v)
+{
+    LinkSum c{0.0, 0.0, 0.0, 0.0};
+    if (!(meta & LINK_D3Q7)) {
+        const double fv = 2.0 * ((double)v + w19_rt(p));
+        c.fx = dir_comp(CX19, p) * fv;
+        c.fy = dir_comp(CY19, p) * fv;
+        c.fz = dir_comp(CZ19, p) * fv;
+    } else if (meta & LINK_DIRICHLET) {
+        c.q = a.omega * a.wall_T[grp] - 2.0 * (double)v;
+    }
+    return c;
+}
+
+// Reduce the per-lane sums of one wavefront into the group accumulators: a
+// wavefront whose links share one group (links are sorted by group) sums with
+// shuffles and issues one fp64 atomic per component; a mixed wavefront adds
+// lane by lane.  grp < 0 marks lanes without a link.
+__device__ __forceinline__ void reduce_to_groups(double* accum, int32_t grp, LinkSum c)
+{
     const int32_t lead = __shfl(grp, 0, 64);
     const bool uniform = __all(grp == lead || grp < 0);
     if (uniform) {
-        fx = wave_sum(fx);
-        fy = wave_sum(fy);
-        fz = wave_sum(fz);
-        qh = wave_sum(qh);
+        c.fx = wave_sum(c.fx);
+        c.fy = wave_sum(c.fy);
+        c.fz = wave_sum(c.fz);
+        c.q = wave_sum(c.q);
         if ((threadIdx.x & 63) == 0 && lead >= 0) {
-            double* acc = a.accum + 4 * lead;
-            atomicAdd(acc + 0, fx);
-            atomicAdd(acc + 1, fy);
-            atomicAdd(acc + 2, fz);
-            atomicAdd(acc + 3, qh);
+            double* acc = accum + 4 * lead;
+            atomicAdd(acc + 0, c.fx);
+            atomicAdd(acc + 1, c.fy);
+            atomicAdd(acc + 2, c.fz);
+            atomicAdd(acc + 3, c.q);
         }
     } else if (grp >= 0) {
-        double* acc = a.accum + 4 * grp;
-        atomicAdd(acc + 0, fx);
-        atomicAdd(acc + 1, fy);
-        atomicAdd(acc + 2, fz);
-        atomicAdd(acc + 3, qh);
+        double* acc = accum + 4 * grp;
+        atomicAdd(acc + 0, c.fx);
+        atomicAdd(acc + 1, c.fy);
+        atomicAdd(acc + 2, c.fz);
+        atomicAdd(acc + 3, c.q);
     }
 }
 
-// Scatter: write each gathered value where the next step reads it --
-// bounce-back f_pbar = f_p^+ (no-slip), anti-bounce-back
+// Value a link writes: bounce-back f_pbar = f_p^+ (no-slip), anti-bounce-back
 // g_pbar = -g_p^+ + w T_w (Dirichlet T), bounce-back g_pbar = g_p^+ (adiabatic).
+template <typename R>
+__device__ __forceinline__ R link_value(const LinkArgs<R>& a, uint32_t meta, int32_t grp, R v)
+{
+    if ((meta & LINK_D3Q7) && (meta & LINK_DIRICHLET)) return (R)(a.omega * a.wall_T[grp]) - v;
+    return v;
+}
+
+// Gather (wall links): read every link's post-collision source into scratch
+// before any link writes.  A wall link's destination wraps through the
+// periodic addressing onto the source of its partner link on the opposite
+// face, so the two passes keep every source intact.  On a submission's last
+// step the gather also takes the momentum exchange and heat.
+template <typename R>
+__global__ void __launch_bounds__(BLOCK) k_link_gather(LinkArgs<R> a)
+{
+    const int64_t l = a.begin + (int64_t)blockIdx.x * BLOCK + threadIdx.x;
+    const int64_t S = a.geo.stride;
+    LinkSum c{0.0, 0.0, 0.0, 0.0};
+    int32_t grp = -1;
+    if (l < a.end) {
+        const uint32_t meta = a.meta[l];
+        const int p = (int)(meta & LINK_DIR_MASK);
+        grp = (int32_t)((meta >> LINK_GROUP_SHIFT) & LINK_GROUP_MASK);
+        const LinkSlots sl = link_slots(a.mode, p, a.cell[l], a.cellw[l]);
+        const R* src = (meta & LINK_D3Q7) ? a.g_src : a.f_src;
+        const R v = ld(src + sl.src_plane * S, sl.src_idx);
+        a.scratch[l] = v;
+        if (a.accumulate) c = link_sum(a, meta, p, grp, v);
+    }
+    if (a.accumulate) reduce_to_groups(a.accum, grp, c);
+}
+
+// Scatter (wall links): write each gathered value where the next step reads it.
 template <typename R>
 __global__ void __launch_bounds__(BLOCK) k_link_scatter(LinkArgs<R> a)
 {
-    const int64_t l = (int64_t)blockIdx.x * BLOCK + threadIdx.x;
-    if (l >= a.n_total) return;
+    const int64_t l = a.begin + (int64_t)blockIdx.x * BLOCK + threadIdx.x;
+    if (l >= a.end) return;
     const int64_t S = a.geo.stride;
-    const bool isf = l < a.n_f;
     const uint32_t meta = a.meta[l];
     const int p = (int)(meta & LINK_DIR_MASK);
-    R v = a.scratch[l];
-    if (!isf && (meta & LINK_DIRICHLET)) {
-        const int32_t grp = (int32_t)((meta >> LINK_GROUP_SHIFT) & LINK_GROUP_MASK);
-        v = (R)(a.omega * a.wall_T[grp]) - v;
+    const int32_t grp = (int32_t)((meta >> LINK_GROUP_SHIFT) & LINK_GROUP_MASK);
+    const LinkSlots sl = link_slots(a.mode, p, a.cell[l], a.cellw[l]);
+    R* dst = (meta & LINK_D3Q7) ? a.g_dst : a.f_dst;
+    st(dst + sl.dst_plane * S, sl.dst_idx, link_value(a, meta, grp, a.scratch[l]));
+}
+
+// Direct pass (solid links, and every link with two buffers): gather and
+// scatter in one pass.  A solid link's destination is a solid cell's slot
+// (after an even step) or a slot of its own fluid cell that only the solid
+// neighbour would read (after an odd step); neither is ever another link's
+// source, so no scratch is needed.  With two buffers sources and
+// destinations lie in different buffers.
+template <typename R>
+__global__ void __launch_bounds__(BLOCK) k_link_direct(LinkArgs<R> a)
+{
+    const int64_t l = a.begin + (int64_t)blockIdx.x * BLOCK + threadIdx.x;
+    const int64_t S = a.geo.stride;
+    LinkSum c{0.0, 0.0, 0.0, 0.0};
+    int32_t grp = -1;
+    if (l < a.end) {
+        const uint32_t meta = a.meta[l];
+        const int p = (int)(meta & LINK_DIR_MASK);
+        grp = (int32_t)((meta >> LINK_GROUP_SHIFT) & LINK_GROUP_MASK);
+        const LinkSlots sl = link_slots(a.mode, p, a.cell[l], a.cellw[l]);
+        const bool g7 = (meta & LINK_D3Q7) != 0;
+        const R v = ld((g7 ? a.g_src : a.f_src) + sl.src_plane * S, sl.src_idx);
+        st((g7 ? a.g_dst : a.f_dst) + sl.dst_plane * S, sl.dst_idx, link_value(a, meta, grp, v));
+        if (a.accumulate) c = link_sum(a, meta, p, grp, v);
     }
-    int32_t plane, idx;
-    if (a.mode == LINK_AA_AFTER_EVEN) {
-        plane = p;
-        idx = a.cellw[l];
-    } else {
-        plane = opp_rt(p);
-        idx = a.cell[l];
-    }
-    R* dst = isf ? a.f_dst : a.g_dst;
-    dst[plane * S + idx] = v;
+    if (a.accumulate) reduce_to_groups(a.accum, grp, c);
 }
 
 // ------------------------------------------------------ init / read
@@ -390,16 +454,24 @@ hipError_t launch_ab_pull(const StepArgs<R>& a, bool thermal, hipStream_t s)
 template <typename R>
 hipError_t launch_link_gather(const LinkArgs<R>& a, hipStream_t s)
 {
-    if (a.n_total == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_link_gather<R>), grid_for(a.n_total), dim3(BLOCK), 0, s, a);
+    if (a.end <= a.begin) return hipSuccess;
+    hipLaunchKernelGGL((k_link_gather<R>), grid_for(a.end - a.begin), dim3(BLOCK), 0, s, a);
     return hipGetLastError();
 }
 
 template <typename R>
 hipError_t launch_link_scatter(const LinkArgs<R>& a, hipStream_t s)
 {
-    if (a.n_total == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_link_scatter<R>), grid_for(a.n_total), dim3(BLOCK), 0, s, a);
+    if (a.end <= a.begin) return hipSuccess;
+    hipLaunchKernelGGL((k_link_scatter<R>), grid_for(a.end - a.begin), dim3(BLOCK), 0, s, a);
+    return hipGetLastError();
+}
+
+template <typename R>
+hipError_t launch_link_direct(const LinkArgs<R>& a, hipStream_t s)
+{
+    if (a.end <= a.begin) return hipSuccess;
+    hipLaunchKernelGGL((k_link_direct<R>), grid_for(a.end - a.begin), dim3(BLOCK), 0, s, a);
     return hipGetLastError();
 }
 
@@ -432,6 +504,7 @@ hipError_t launch_zero_f64(double* p, int64_t n, hipStream_t s)
     template hipError_t launch_ab_pull<R>(const StepArgs<R>&, bool, hipStream_t);        \
     template hipError_t launch_link_gather<R>(const LinkArgs<R>&, hipStream_t);          \
     template hipError_t launch_link_scatter<R>(const LinkArgs<R>&, hipStream_t);         \
+    template hipError_t launch_link_direct<R>(const LinkArgs<R>&, hipStream_t);          \
     template hipError_t launch_init<R>(const FieldArgs<R>&, bool, hipStream_t);          \
     template hipError_t launch_read<R>(const FieldArgs<R>&, bool, hipStream_t);
 

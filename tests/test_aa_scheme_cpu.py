@@ -5,7 +5,9 @@ describes the AA pattern: even steps read population q of cell x at (q, x)
 and write the collided value at (opposite(q), x); odd steps read it at
 (opposite(q), x - c_q) and write it at (q, x + c_q).  Wall links gather every
 link's post-collision source into scratch before a scatter writes, so that no
-link overwrites another's source.  This test runs that bookkeeping in numpy
+link overwrites another's source; solid links are applied in one direct pass,
+since no solid link's destination is ever a link source (checked below).  This
+test runs that bookkeeping in numpy
 (cells collided by the oracle's per-cell routine, every cell processed, solid
 cells carrying NaN) and checks that the populations equal the oracle's plain
 two-buffer collide-then-pull stepping bit for bit after odd and even step
@@ -69,6 +71,18 @@ def neighbour(shape, cset, sign):
     return np.stack([cell_index(x + sign * c[0], y + sign * c[1], z + sign * c[2], shape) for c in cset])
 
 
+def link_src(lk, opp, odd):
+    """Slot holding the collided population f_p(x) of link (x, p)."""
+    x, q, xw, _ = lk
+    return (q, xw) if odd else (opp[q], x)
+
+
+def link_dst(lk, opp, odd):
+    """Slot the next step reads f_opp(p)(x) from."""
+    x, q, xw, _ = lk
+    return (opp[q], x) if odd else (q, xw)
+
+
 class AAModel:
     def __init__(self, p, lab, rho, u, T):
         self.p = p
@@ -113,25 +127,28 @@ class AAModel:
         self._write(self.A, fp.T, OPP19, self.up19, odd)
         if self.th:
             self._write(self.B, gp.T, OPP7, self.up7, odd)
-        # links: gather every source first, then scatter
+        # wall links: gather every source first, then scatter; solid links: one
+        # direct pass, each link read and written immediately
         for S, links, opp, is_g in ((self.A, self.fl, OPP19, False), (self.B, self.gl, OPP7, True)):
             if not links:
                 continue
-            vals = []
-            for (x, q, xw, grp) in links:
-                src = (OPP19 if not is_g else OPP7)[q], x
-                if odd:
-                    src = (q, xw)
-                vals.append(S[src])
-            for (x, q, xw, grp), v in zip(links, vals):
-                dst = (q, xw) if not odd else (opp[q], x)
-                if is_g:
-                    dirichlet = self.p["face_thermal"][grp] if grp < 6 else self.p["solid_thermal"]
-                    if dirichlet:
-                        tw = self.p["face_T"][grp] if grp < 6 else self.p["solid_T"]
-                        v = -v + (6 + self.p["a_T"]) / 21 * tw
-                S[dst] = v
+            wall = [lk for lk in links if lk[3] < 6]
+            solid = [lk for lk in links if lk[3] >= 6]
+            vals = [S[link_src(lk, opp, odd)] for lk in wall]
+            for lk, v in zip(wall, vals):
+                S[link_dst(lk, opp, odd)] = self._rule(lk, v, is_g)
+            for lk in solid:
+                S[link_dst(lk, opp, odd)] = self._rule(lk, S[link_src(lk, opp, odd)], is_g)
         self.t += 1
+
+    def _rule(self, lk, v, is_g):
+        grp = lk[3]
+        if is_g:
+            dirichlet = self.p["face_thermal"][grp] if grp < 6 else self.p["solid_thermal"]
+            if dirichlet:
+                tw = self.p["face_T"][grp] if grp < 6 else self.p["solid_T"]
+                return -v + (6 + self.p["a_T"]) / 21 * tw
+        return v
 
     def populations(self):
         odd = self.t & 1
@@ -186,3 +203,20 @@ def test_aa_equals_two_buffer_bitwise(name):
             assert np.array_equal(g[:, fluid], ref["g"][:, fluid]), f"g differs after {n} steps"
         # no NaN from solid cells leaks into a fluid cell
         assert np.isfinite(f[:, fluid]).all()
+
+
+@pytest.mark.parametrize("name", ["walls_solids", "rb_spheres"])
+def test_solid_link_destinations_are_never_link_sources(name):
+    """The property that lets solid links skip the scratch: for both parities,
+    no solid link writes a slot that any link (wall or solid) reads."""
+    p, lab, rho, u, T = case(name)
+    for cset, opp in ((C19, OPP19), (C7, OPP7)):
+        links = build_links(p, lab, cset)
+        for odd in (0, 1):
+            sources = {link_src(lk, opp, odd) for lk in links}
+            solid_dst = {link_dst(lk, opp, odd) for lk in links if lk[3] >= 6}
+            assert solid_dst and not (solid_dst & sources)
+            # wall links do overlap: their gather must come first
+            wall_dst = {link_dst(lk, opp, odd) for lk in links if lk[3] < 6}
+            if name == "walls_solids":
+                assert wall_dst & sources
