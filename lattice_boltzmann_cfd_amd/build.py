@@ -26,6 +26,10 @@ def command(out=LIB, extra=()):
         HIPCC, "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         # packed fp32 instructions stay off (they are not used by hand either)
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # fuse a*b+c only inside one source expression: the same collision code
+        # then rounds identically in every kernel that inlines it, whatever
+        # branches surround it (in-place and two-buffer results agree bitwise)
+        "-ffp-contract=on",
         "-I", os.path.join(ROOT, "include"), "-I", CSRC,
         *extra, "-o", out, *SOURCES, "-lpthread",
     ]

@@ -28,7 +28,7 @@ struct lbm_ctx {
     char* g = nullptr;
     char* f2 = nullptr;
     char* g2 = nullptr;
-    uint8_t* labels = nullptr;
+    uint32_t* mask = nullptr;
     int32_t* lcell = nullptr;
     int32_t* lcellw = nullptr;
     uint32_t* lmeta = nullptr;
@@ -295,8 +295,53 @@ bool any_solid(const lbm_params* p, const uint8_t* labels)
     return false;
 }
 
+// Per-cell solid mask.  Fluid cell: bit q (kernel direction 1..18) when the
+// link (x, q) ends in a solid cell without crossing a wall face.  Solid cell:
+// MASK_SOLID, and bit q when (s + c_q, opp q) is such a link of a fluid cell.
+std::vector<uint32_t> build_mask(const lbm_params* p, const uint8_t* labels)
+{
+    const int64_t n = (int64_t)p->nx * p->ny * p->nz;
+    std::vector<uint32_t> mask((size_t)n, 0u);
+    const int nz = p->nz;
+    unsigned nthreads = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+    nthreads = std::min<unsigned>(nthreads, (unsigned)nz);
+    auto work = [&](unsigned tid) {
+        const int z0 = (int)((int64_t)nz * tid / nthreads), z1 = (int)((int64_t)nz * (tid + 1) / nthreads);
+        for (int z = z0; z < z1; ++z)
+            for (int y = 0; y < p->ny; ++y)
+                for (int x = 0; x < p->nx; ++x) {
+                    const int32_t cell = x + p->nx * (y + p->ny * z);
+                    uint32_t m = 0;
+                    for (int q = 1; q < Q19; ++q) {
+                        const int c[3] = {cx19(q), cy19(q), cz19(q)};
+                        int32_t image;
+                        if (!labels[cell]) {
+                            if (blocked_group(p, labels, x, y, z, c, &image) >= 6) m |= 1u << q;
+                            continue;
+                        }
+                        // solid cell: does the fluid neighbour at s + c_q bounce off s?
+                        const int t[3] = {x + c[0], y + c[1], z + c[2]};
+                        const int n3[3] = {p->nx, p->ny, p->nz};
+                        bool crosses = false;
+                        int w[3];
+                        for (int a = 0; a < 3; ++a) {
+                            if ((t[a] < 0 || t[a] >= n3[a]) && p->face_kind[2 * a] == LBM_FACE_WALL) crosses = true;
+                            w[a] = t[a] < 0 ? t[a] + n3[a] : (t[a] >= n3[a] ? t[a] - n3[a] : t[a]);
+                        }
+                        if (!crosses && !labels[w[0] + p->nx * (w[1] + p->ny * w[2])]) m |= 1u << q;
+                    }
+                    mask[cell] = labels[cell] ? (m | MASK_SOLID) : m;
+                }
+    };
+    std::vector<std::thread> pool;
+    for (unsigned t = 1; t < nthreads; ++t) pool.emplace_back(work, t);
+    work(0);
+    for (auto& th : pool) th.join();
+    return mask;
+}
+
 struct Layout {
-    size_t f, g, f2, g2, labels, lcell, lcellw, lmeta, scratch, wall_T, accum, unstable, total;
+    size_t f, g, f2, g2, mask, lcell, lcellw, lmeta, scratch, wall_T, accum, unstable, total;
     int64_t stride;
 };
 
@@ -314,7 +359,7 @@ Layout make_layout(const lbm_params* p, bool solids, int64_t n_links)
     L.g = off; off += gb;
     L.f2 = off; off += ab ? fb : 0;
     L.g2 = off; off += ab ? gb : 0;
-    L.labels = off; off += solids ? align_up((size_t)n) : 0;
+    L.mask = off; off += solids ? align_up(4 * (size_t)n) : 0;
     L.lcell = off; off += align_up(4 * (size_t)n_links);
     L.lcellw = off; off += align_up(4 * (size_t)n_links);
     L.lmeta = off; off += align_up(4 * (size_t)n_links);
@@ -339,7 +384,7 @@ lbm_status device_error(lbm_ctx* ctx, hipError_t e, const char* what)
     } while (0)
 
 template <typename R>
-LinkArgs<R> link_args(lbm_ctx* c, int mode, bool accumulate, char* fsrc, char* fdst, char* gsrc, char* gdst)
+LinkArgs<R> link_args(lbm_ctx* c, int mode, char* fsrc, char* fdst, char* gsrc, char* gdst)
 {
     LinkArgs<R> a{};
     a.geo = c->geo;
@@ -357,7 +402,6 @@ LinkArgs<R> link_args(lbm_ctx* c, int mode, bool accumulate, char* fsrc, char* f
     a.end = c->n_f + c->n_g;
     a.omega = (6.0 + c->p.a_T) / 21.0;
     a.mode = mode;
-    a.accumulate = accumulate ? 1 : 0;
     return a;
 }
 
@@ -371,31 +415,30 @@ const Collision<double>& collision<double>(const lbm_ctx* c) { return c->cold; }
 template <typename R>
 lbm_status step_impl(lbm_ctx* c, int64_t n)
 {
-    const bool links = (c->n_f + c->n_g) > 0;
+    const int64_t n_links = c->n_f + c->n_g;
     for (int64_t k = 0; k < n; ++k) {
         const bool last = (k == n - 1);
-        if (last) LBM_HIP(c, launch_zero_f64(c->accum, 4 * LBM_MAX_GROUPS, c->stream), "zero accumulators");
         const int parity = (int)(c->t & 1);
         StepArgs<R> s{};
         s.geo = c->geo;
         s.col = collision<R>(c);
+        s.mask = c->mask;
+        s.solid_gw = (R)((6.0 + c->p.a_T) / 21.0 * c->p.solid_T);
+        s.solid_dirichlet = c->p.solid_thermal == LBM_DIRICHLET ? 1 : 0;
+        LinkArgs<R> la;
         if (!c->ab) {
+            // one in-place kernel: collision, streaming and solid bounce-back
             s.f = (R*)c->f;
             s.g = (R*)c->g;
             s.parity = parity;
             LBM_HIP(c, launch_aa_step<R>(s, c->thermal, c->stream), "AA step kernel");
-            if (links) {
-                const int mode = parity == 0 ? LINK_AA_AFTER_EVEN : LINK_AA_AFTER_ODD;
-                LinkArgs<R> la = link_args<R>(c, mode, last, c->f, c->f, c->g, c->g);
+            la = link_args<R>(c, parity == 0 ? LINK_AA_AFTER_EVEN : LINK_AA_AFTER_ODD, c->f, c->f, c->g, c->g);
+            if (c->n_wall > 0) {
                 // wall links: gather every source, then scatter
                 la.begin = 0;
                 la.end = c->n_wall;
                 LBM_HIP(c, launch_link_gather<R>(la, c->stream), "link gather kernel");
                 LBM_HIP(c, launch_link_scatter<R>(la, c->stream), "link scatter kernel");
-                // solid links: one direct pass
-                la.begin = c->n_wall;
-                la.end = c->n_f + c->n_g;
-                LBM_HIP(c, launch_link_direct<R>(la, c->stream), "solid link kernel");
             }
         } else {
             char* fa = parity ? c->f2 : c->f;
@@ -408,11 +451,21 @@ lbm_status step_impl(lbm_ctx* c, int64_t n)
             s.g2 = (R*)gb;
             LBM_HIP(c, launch_ab_collide<R>(s, c->thermal, c->stream), "A-B collide kernel");
             LBM_HIP(c, launch_ab_pull<R>(s, c->thermal, c->stream), "A-B pull kernel");
-            if (links) {
+            la = link_args<R>(c, LINK_AB, fa, fb, ga, gb);
+            if (c->n_wall > 0) {
                 // sources in one buffer, destinations in the other: one pass
-                LinkArgs<R> la = link_args<R>(c, LINK_AB, last, fa, fb, ga, gb);
+                la.begin = 0;
+                la.end = c->n_wall;
                 LBM_HIP(c, launch_link_direct<R>(la, c->stream), "link kernel");
             }
+        }
+        if (last) {
+            // forces and heat of the submission's last step, read from every
+            // link's destination slot
+            LBM_HIP(c, launch_zero_f64(c->accum, 4 * LBM_MAX_GROUPS, c->stream), "zero accumulators");
+            la.begin = 0;
+            la.end = n_links;
+            LBM_HIP(c, launch_link_force<R>(la, c->stream), "force kernel");
         }
         c->t += 1;
     }
@@ -427,10 +480,12 @@ FieldArgs<R> field_args(lbm_ctx* c)
     const bool second = c->ab && (c->t & 1);
     a.f = (R*)(second ? c->f2 : c->f);
     a.g = (R*)(second ? c->g2 : c->g);
-    a.labels = c->labels;
+    a.mask = c->mask;
     a.unstable = c->unstable;
     a.parity = (int32_t)(c->t & 1);
     a.ab = c->ab ? 1 : 0;
+    a.solid_gw = (R)((6.0 + c->p.a_T) / 21.0 * c->p.solid_T);
+    a.solid_dirichlet = c->p.solid_thermal == LBM_DIRICHLET ? 1 : 0;
     a.col = collision<R>(c);
     return a;
 }
@@ -515,7 +570,7 @@ lbm_status lbm_create(const lbm_params* p, const uint8_t* solid_labels, void* de
         c->g = c->thermal ? base + L.g : nullptr;
         c->f2 = c->ab ? base + L.f2 : nullptr;
         c->g2 = (c->ab && c->thermal) ? base + L.g2 : nullptr;
-        c->labels = solids ? (uint8_t*)(base + L.labels) : nullptr;
+        c->mask = solids ? (uint32_t*)(base + L.mask) : nullptr;
         c->lcell = (int32_t*)(base + L.lcell);
         c->lcellw = (int32_t*)(base + L.lcellw);
         c->lmeta = (uint32_t*)(base + L.lmeta);
@@ -543,8 +598,10 @@ lbm_status lbm_create(const lbm_params* p, const uint8_t* solid_labels, void* de
             if (e == hipSuccess) e = hipMemcpyAsync(c->lcellw, cellw.data(), 4 * nl, hipMemcpyHostToDevice, c->stream);
             if (e == hipSuccess) e = hipMemcpyAsync(c->lmeta, meta.data(), 4 * nl, hipMemcpyHostToDevice, c->stream);
         }
+        std::vector<uint32_t> mask;
+        if (solids) mask = build_mask(p, solid_labels);
         if (e == hipSuccess && solids)
-            e = hipMemcpyAsync(c->labels, solid_labels, (size_t)G.ncell, hipMemcpyHostToDevice, c->stream);
+            e = hipMemcpyAsync(c->mask, mask.data(), 4 * (size_t)G.ncell, hipMemcpyHostToDevice, c->stream);
         if (e == hipSuccess)
             e = hipMemcpyAsync(c->wall_T, wallT.data(), 8 * LBM_MAX_GROUPS, hipMemcpyHostToDevice, c->stream);
         if (e == hipSuccess) e = launch_zero_f64(c->accum, 4 * LBM_MAX_GROUPS, c->stream);

@@ -47,6 +47,15 @@ constexpr uint32_t LINK_GROUP_MASK = 511u;
 constexpr uint32_t LINK_DIRICHLET = 1u << 14;
 constexpr uint32_t LINK_D3Q7 = 1u << 15;
 
+// Per-cell solid mask (only when the box has solid cells).  On a fluid cell,
+// bit q (1..18) is set when x + c_q is a solid cell reached without crossing
+// a wall face (a solid link).  On a solid cell, MASK_SOLID is set and bit q
+// marks that (s + c_q, opp q) is such a solid link of a fluid neighbour, whose
+// bounce-back store claims the slot the solid cell would store direction q
+// to.  D3Q7 direction k (1..6) is the D3Q19 axis direction k, so bits 1..6
+// serve both lattices.
+constexpr uint32_t MASK_SOLID = 1u << 31;
+
 // Which slots a link pass reads and writes.
 enum LinkMode : int32_t {
     LINK_AA_AFTER_EVEN = 0,  // src (opp p, x), dst (p, x + c_p)
@@ -61,8 +70,10 @@ struct StepArgs {
     R* g;  // D3Q7 populations or null
     R* f2; // AB: destination buffer of the pull
     R* g2;
+    const uint32_t* mask;  // solid mask, or null when the box has no solid cell
+    R solid_gw;            // w T_solid (anti-bounce-back constant of the solids)
+    int32_t solid_dirichlet;
     int32_t parity;
-    int32_t pad0;
     Collision<R> col;
 };
 
@@ -83,7 +94,7 @@ struct LinkArgs {
     int64_t end;    // one past the last link of the launch
     double omega;          // (6 + a_T)/21
     int32_t mode;
-    int32_t accumulate;
+    int32_t pad0;
 };
 
 template <typename R>
@@ -91,7 +102,7 @@ struct FieldArgs {
     Geometry geo;
     R* f;
     R* g;
-    const uint8_t* labels;  // null when there are no solids
+    const uint32_t* mask;  // solid mask, or null when there are no solids
     const R* rho;
     const R* u;
     const R* T;
@@ -101,6 +112,8 @@ struct FieldArgs {
     int32_t* unstable;
     int32_t parity;
     int32_t ab;  // populations in natural layout (two-buffer mode)
+    R solid_gw;  // w T_solid
+    int32_t solid_dirichlet;
     Collision<R> col;
 };
 
@@ -112,6 +125,7 @@ template <typename R> hipError_t launch_ab_pull(const StepArgs<R>& a, bool therm
 template <typename R> hipError_t launch_link_gather(const LinkArgs<R>& a, hipStream_t s);
 template <typename R> hipError_t launch_link_scatter(const LinkArgs<R>& a, hipStream_t s);
 template <typename R> hipError_t launch_link_direct(const LinkArgs<R>& a, hipStream_t s);
+template <typename R> hipError_t launch_link_force(const LinkArgs<R>& a, hipStream_t s);
 template <typename R> hipError_t launch_init(const FieldArgs<R>& a, bool thermal, hipStream_t s);
 template <typename R> hipError_t launch_read(const FieldArgs<R>& a, bool thermal, hipStream_t s);
 hipError_t launch_zero_f64(double* p, int64_t n, hipStream_t s);

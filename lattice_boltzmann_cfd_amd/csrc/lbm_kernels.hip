@@ -16,6 +16,8 @@
 // overwritten by a link scatter before any fluid cell reads it.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "lbm_internal.hpp"
 
 namespace lbm {
@@ -23,6 +25,7 @@ namespace lbm {
 namespace {
 
 constexpr int BLOCK = 256;
+constexpr int LBM_GROUPS = 261;  // 6 faces + 255 solid labels
 
 // Run-time direction tables packed into 64-bit constants: 2 bits per
 // direction holding c + 1.
@@ -87,7 +90,31 @@ __device__ __forceinline__ void st(R* plane, int32_t idx, R v)
 
 // ------------------------------------------------------------ AA step
 
-template <typename R, bool TH>
+// Value a D3Q7 population takes when it bounces off a solid cell:
+// anti-bounce-back -g^+ + w T_solid (Dirichlet) or g^+ (adiabatic).
+template <typename R>
+__device__ __forceinline__ R solid_rule(const StepArgs<R>& a, R v)
+{
+    return a.solid_dirichlet ? a.solid_gw - v : v;
+}
+
+// One fused time step in place.  With SOLID the fluid cells next to solid
+// cells apply half-way bounce-back themselves ("Multi-GPU thermal lattice
+// Boltzmann simulations using OpenACC and MPI", Sec. 2), and all of it happens
+// in the odd step, so the even step stays the plain kernel for every cell:
+//  * even step: each cell stores f_p^+ at (opp p, x) as usual, solid cells
+//    included (on NaN; nobody reads a solid cell's slots in the odd step);
+//  * odd step, inflow: a population q whose upstream cell x - c_q is solid is
+//    the bounce of f_opp(q)^+(x) from the even step, which sits in (q, x) of
+//    the cell itself -- it is read there instead;
+//  * odd step, outflow: f_p^+ for a direction p that points at a solid cell is
+//    stored, besides its usual slot (read next only by the solid cell), at
+//    (opp p, x), where the next (even) step reads it.
+// A solid cell's usual odd-step store of direction q lands in (q, s + c_q);
+// when s + c_q is a fluid cell bouncing off s that slot is the fluid cell's
+// re-read and bounce-back slot, so the solid cell skips it (its mask bit q).
+// No other slot is touched by two cells in one step.
+template <typename R, bool TH, bool SOLID>
 __global__ void __launch_bounds__(BLOCK) k_aa_step(StepArgs<R> a)
 {
     const Geometry& G = a.geo;
@@ -113,6 +140,9 @@ __global__ void __launch_bounds__(BLOCK) k_aa_step(StepArgs<R> a)
             for (int k = 0; k < Q7; ++k) st(gg + opp7(k) * S, cell, g[k]);
         }
     } else {
+        const uint32_t m = SOLID ? a.mask[cell] : 0u;
+        const bool solid = SOLID && (m & MASK_SOLID);
+        const bool near = SOLID && !solid && m != 0;
         const Nbr nb(G, cell);
 #pragma unroll
         for (int q = 0; q < Q19; ++q) h[q] = ld(f + opp19(q) * S, cell + nb.at(-cx19(q), -cy19(q), -cz19(q)));
@@ -120,12 +150,34 @@ __global__ void __launch_bounds__(BLOCK) k_aa_step(StepArgs<R> a)
 #pragma unroll
             for (int k = 0; k < Q7; ++k) g[k] = ld(gg + opp7(k) * S, cell + nb.at(-cx7(k), -cy7(k), -cz7(k)));
         }
+        if (near) {
+#pragma unroll
+            for (int q = 1; q < Q19; ++q)
+                if ((m >> opp19(q)) & 1u) h[q] = ld(f + q * S, cell);
+            if (TH) {
+#pragma unroll
+                for (int k = 1; k < Q7; ++k)
+                    if ((m >> opp7(k)) & 1u) g[k] = solid_rule(a, ld(gg + k * S, cell));
+            }
+        }
         collide<R, TH>(h, g, a.col);
 #pragma unroll
-        for (int q = 0; q < Q19; ++q) st(f + q * S, cell + nb.at(cx19(q), cy19(q), cz19(q)), h[q]);
+        for (int q = 0; q < Q19; ++q)
+            if (!solid || !((m >> q) & 1u)) st(f + q * S, cell + nb.at(cx19(q), cy19(q), cz19(q)), h[q]);
         if (TH) {
 #pragma unroll
-            for (int k = 0; k < Q7; ++k) st(gg + k * S, cell + nb.at(cx7(k), cy7(k), cz7(k)), g[k]);
+            for (int k = 0; k < Q7; ++k)
+                if (!solid || !((m >> k) & 1u)) st(gg + k * S, cell + nb.at(cx7(k), cy7(k), cz7(k)), g[k]);
+        }
+        if (near) {
+#pragma unroll
+            for (int q = 1; q < Q19; ++q)
+                if ((m >> q) & 1u) st(f + opp19(q) * S, cell, h[q]);
+            if (TH) {
+#pragma unroll
+                for (int k = 1; k < Q7; ++k)
+                    if ((m >> k) & 1u) st(gg + opp7(k) * S, cell, solid_rule(a, g[k]));
+            }
         }
     }
 }
@@ -133,44 +185,60 @@ __global__ void __launch_bounds__(BLOCK) k_aa_step(StepArgs<R> a)
 // ------------------------------------------------- two buffers (A-B)
 
 // Collide in place: every population stays in its own slot.
-template <typename R, bool TH>
+template <typename R, bool TH, bool SOLID>
 __global__ void __launch_bounds__(BLOCK) k_ab_collide(StepArgs<R> a)
 {
     const Geometry& G = a.geo;
     const int32_t cell = (int32_t)(blockIdx.x * BLOCK + threadIdx.x);
     if (cell >= G.ncell) return;
+    // solid cells collide NaN in their own slots: nothing else writes this
+    // buffer in this kernel and no fluid cell pulls from a solid slot
     const int64_t S = G.stride;
     R h[Q19];
     R g[Q7];
 #pragma unroll
-    for (int q = 0; q < Q19; ++q) h[q] = a.f[q * S + cell];
+    for (int q = 0; q < Q19; ++q) h[q] = ld(a.f + q * S, cell);
     if (TH) {
 #pragma unroll
-        for (int k = 0; k < Q7; ++k) g[k] = a.g[k * S + cell];
+        for (int k = 0; k < Q7; ++k) g[k] = ld(a.g + k * S, cell);
     }
     collide<R, TH>(h, g, a.col);
 #pragma unroll
-    for (int q = 0; q < Q19; ++q) a.f[q * S + cell] = h[q];
+    for (int q = 0; q < Q19; ++q) st(a.f + q * S, cell, h[q]);
     if (TH) {
 #pragma unroll
-        for (int k = 0; k < Q7; ++k) a.g[k * S + cell] = g[k];
+        for (int k = 0; k < Q7; ++k) st(a.g + k * S, cell, g[k]);
     }
 }
 
-// Pull into the other buffer: B(q, x) = A(q, x - c_q).
-template <typename R, bool TH>
+// Pull into the other buffer: B(q, x) = A(q, x - c_q); when x - c_q is a
+// solid cell the population comes back from x itself: B(q, x) = A(opp q, x)
+// (anti-bounce-back for a Dirichlet D3Q7 population).
+template <typename R, bool TH, bool SOLID>
 __global__ void __launch_bounds__(BLOCK) k_ab_pull(StepArgs<R> a)
 {
     const Geometry& G = a.geo;
     const int32_t cell = (int32_t)(blockIdx.x * BLOCK + threadIdx.x);
     if (cell >= G.ncell) return;
+    // a solid cell pulls garbage into its own slots of the other buffer, which
+    // no fluid cell reads; its mask bits are never those of a fluid cell's
+    const uint32_t m = SOLID ? a.mask[cell] : 0u;
+    const bool solid = SOLID && (m & MASK_SOLID);
     const int64_t S = G.stride;
     const Nbr nb(G, cell);
 #pragma unroll
-    for (int q = 0; q < Q19; ++q) a.f2[q * S + cell] = a.f[q * S + (cell + nb.at(-cx19(q), -cy19(q), -cz19(q)))];
+    for (int q = 0; q < Q19; ++q) {
+        R v = ld(a.f + q * S, cell + nb.at(-cx19(q), -cy19(q), -cz19(q)));
+        if (SOLID && !solid && ((m >> opp19(q)) & 1u)) v = ld(a.f + opp19(q) * S, cell);
+        st(a.f2 + q * S, cell, v);
+    }
     if (TH) {
 #pragma unroll
-        for (int k = 0; k < Q7; ++k) a.g2[k * S + cell] = a.g[k * S + (cell + nb.at(-cx7(k), -cy7(k), -cz7(k)))];
+        for (int k = 0; k < Q7; ++k) {
+            R v = ld(a.g + k * S, cell + nb.at(-cx7(k), -cy7(k), -cz7(k)));
+            if (SOLID && !solid && ((m >> opp7(k)) & 1u)) v = solid_rule(a, ld(a.g + opp7(k) * S, cell));
+            st(a.g2 + k * S, cell, v);
+        }
     }
 }
 
@@ -238,35 +306,6 @@ __device__ __forceinline__ LinkSum link_sum(const LinkArgs<R>& a, uint32_t meta,
     return c;
 }
 
-// Reduce the per-lane sums of one wavefront into the group accumulators: a
-// wavefront whose links share one group (links are sorted by group) sums with
-// shuffles and issues one fp64 atomic per component; a mixed wavefront adds
-// lane by lane.  grp < 0 marks lanes without a link.
-__device__ __forceinline__ void reduce_to_groups(double* accum, int32_t grp, LinkSum c)
-{
-    const int32_t lead = __shfl(grp, 0, 64);
-    const bool uniform = __all(grp == lead || grp < 0);
-    if (uniform) {
-        c.fx = wave_sum(c.fx);
-        c.fy = wave_sum(c.fy);
-        c.fz = wave_sum(c.fz);
-        c.q = wave_sum(c.q);
-        if ((threadIdx.x & 63) == 0 && lead >= 0) {
-            double* acc = accum + 4 * lead;
-            atomicAdd(acc + 0, c.fx);
-            atomicAdd(acc + 1, c.fy);
-            atomicAdd(acc + 2, c.fz);
-            atomicAdd(acc + 3, c.q);
-        }
-    } else if (grp >= 0) {
-        double* acc = accum + 4 * grp;
-        atomicAdd(acc + 0, c.fx);
-        atomicAdd(acc + 1, c.fy);
-        atomicAdd(acc + 2, c.fz);
-        atomicAdd(acc + 3, c.q);
-    }
-}
-
 // Value a link writes: bounce-back f_pbar = f_p^+ (no-slip), anti-bounce-back
 // g_pbar = -g_p^+ + w T_w (Dirichlet T), bounce-back g_pbar = g_p^+ (adiabatic).
 template <typename R>
@@ -279,26 +318,17 @@ __device__ __forceinline__ R link_value(const LinkArgs<R>& a, uint32_t meta, int
 // Gather (wall links): read every link's post-collision source into scratch
 // before any link writes.  A wall link's destination wraps through the
 // periodic addressing onto the source of its partner link on the opposite
-// face, so the two passes keep every source intact.  On a submission's last
-// step the gather also takes the momentum exchange and heat.
+// face, so the two passes keep every source intact.
 template <typename R>
 __global__ void __launch_bounds__(BLOCK) k_link_gather(LinkArgs<R> a)
 {
     const int64_t l = a.begin + (int64_t)blockIdx.x * BLOCK + threadIdx.x;
+    if (l >= a.end) return;
     const int64_t S = a.geo.stride;
-    LinkSum c{0.0, 0.0, 0.0, 0.0};
-    int32_t grp = -1;
-    if (l < a.end) {
-        const uint32_t meta = a.meta[l];
-        const int p = (int)(meta & LINK_DIR_MASK);
-        grp = (int32_t)((meta >> LINK_GROUP_SHIFT) & LINK_GROUP_MASK);
-        const LinkSlots sl = link_slots(a.mode, p, a.cell[l], a.cellw[l]);
-        const R* src = (meta & LINK_D3Q7) ? a.g_src : a.f_src;
-        const R v = ld(src + sl.src_plane * S, sl.src_idx);
-        a.scratch[l] = v;
-        if (a.accumulate) c = link_sum(a, meta, p, grp, v);
-    }
-    if (a.accumulate) reduce_to_groups(a.accum, grp, c);
+    const uint32_t meta = a.meta[l];
+    const LinkSlots sl = link_slots(a.mode, (int)(meta & LINK_DIR_MASK), a.cell[l], a.cellw[l]);
+    const R* src = (meta & LINK_D3Q7) ? a.g_src : a.f_src;
+    a.scratch[l] = ld(src + sl.src_plane * S, sl.src_idx);
 }
 
 // Scatter (wall links): write each gathered value where the next step reads it.
@@ -309,37 +339,92 @@ __global__ void __launch_bounds__(BLOCK) k_link_scatter(LinkArgs<R> a)
     if (l >= a.end) return;
     const int64_t S = a.geo.stride;
     const uint32_t meta = a.meta[l];
-    const int p = (int)(meta & LINK_DIR_MASK);
     const int32_t grp = (int32_t)((meta >> LINK_GROUP_SHIFT) & LINK_GROUP_MASK);
-    const LinkSlots sl = link_slots(a.mode, p, a.cell[l], a.cellw[l]);
+    const LinkSlots sl = link_slots(a.mode, (int)(meta & LINK_DIR_MASK), a.cell[l], a.cellw[l]);
     R* dst = (meta & LINK_D3Q7) ? a.g_dst : a.f_dst;
     st(dst + sl.dst_plane * S, sl.dst_idx, link_value(a, meta, grp, a.scratch[l]));
 }
 
-// Direct pass (solid links, and every link with two buffers): gather and
-// scatter in one pass.  A solid link's destination is a solid cell's slot
-// (after an even step) or a slot of its own fluid cell that only the solid
-// neighbour would read (after an odd step); neither is ever another link's
-// source, so no scratch is needed.  With two buffers sources and
-// destinations lie in different buffers.
+// Direct pass (wall links with two buffers): sources lie in one buffer and
+// destinations in the other, so gather and scatter merge into one pass.
 template <typename R>
 __global__ void __launch_bounds__(BLOCK) k_link_direct(LinkArgs<R> a)
 {
     const int64_t l = a.begin + (int64_t)blockIdx.x * BLOCK + threadIdx.x;
+    if (l >= a.end) return;
     const int64_t S = a.geo.stride;
-    LinkSum c{0.0, 0.0, 0.0, 0.0};
-    int32_t grp = -1;
-    if (l < a.end) {
-        const uint32_t meta = a.meta[l];
-        const int p = (int)(meta & LINK_DIR_MASK);
-        grp = (int32_t)((meta >> LINK_GROUP_SHIFT) & LINK_GROUP_MASK);
-        const LinkSlots sl = link_slots(a.mode, p, a.cell[l], a.cellw[l]);
-        const bool g7 = (meta & LINK_D3Q7) != 0;
-        const R v = ld((g7 ? a.g_src : a.f_src) + sl.src_plane * S, sl.src_idx);
-        st((g7 ? a.g_dst : a.f_dst) + sl.dst_plane * S, sl.dst_idx, link_value(a, meta, grp, v));
-        if (a.accumulate) c = link_sum(a, meta, p, grp, v);
+    const uint32_t meta = a.meta[l];
+    const int32_t grp = (int32_t)((meta >> LINK_GROUP_SHIFT) & LINK_GROUP_MASK);
+    const LinkSlots sl = link_slots(a.mode, (int)(meta & LINK_DIR_MASK), a.cell[l], a.cellw[l]);
+    const bool g7 = (meta & LINK_D3Q7) != 0;
+    const R v = ld((g7 ? a.g_src : a.f_src) + sl.src_plane * S, sl.src_idx);
+    st((g7 ? a.g_dst : a.f_dst) + sl.dst_plane * S, sl.dst_idx, link_value(a, meta, grp, v));
+}
+
+// Force pass, on a submission's last step only, over every link.  It reads
+// the bounced population f_p^+ of each link where the step left it: for a
+// wall link its scatter destination; for a solid link (opp p, x) in place
+// (the even step's usual store, or the odd step's bounce-back store) and
+// B(opp p, x) with two buffers.  Values a D3Q7 Dirichlet link stores after
+// anti-bounce-back are converted back.  It sums the momentum exchange
+// 2 c_p f_p^+ and the heat w T_w - 2 g_p^+ per group: wavefront shuffles, then
+// fp64 LDS atomics per block, then one global atomic per block and touched
+// group; a grid-stride loop keeps the block count (and the global atomics)
+// small.
+template <typename R>
+__global__ void __launch_bounds__(BLOCK) k_link_force(LinkArgs<R> a)
+{
+    __shared__ double acc[4 * LBM_GROUPS];
+    for (int i = threadIdx.x; i < 4 * LBM_GROUPS; i += BLOCK) acc[i] = 0.0;
+    __syncthreads();
+    const int64_t S = a.geo.stride;
+    for (int64_t base = a.begin + (int64_t)blockIdx.x * BLOCK; base < a.end; base += (int64_t)gridDim.x * BLOCK) {
+        const int64_t l = base + threadIdx.x;
+        LinkSum c{0.0, 0.0, 0.0, 0.0};
+        int32_t grp = -1;
+        if (l < a.end) {
+            const uint32_t meta = a.meta[l];
+            const int p = (int)(meta & LINK_DIR_MASK);
+            grp = (int32_t)((meta >> LINK_GROUP_SHIFT) & LINK_GROUP_MASK);
+            const bool g7 = (meta & LINK_D3Q7) != 0;
+            int32_t plane, idx;
+            bool transformed;
+            if (grp < 6 || a.mode == LINK_AB) {
+                const LinkSlots sl = link_slots(a.mode, p, a.cell[l], a.cellw[l]);
+                plane = sl.dst_plane;
+                idx = sl.dst_idx;
+                transformed = true;
+            } else {
+                plane = opp_rt(p);
+                idx = a.cell[l];
+                transformed = a.mode == LINK_AA_AFTER_ODD;
+            }
+            R v = ld((g7 ? a.g_dst : a.f_dst) + plane * S, idx);
+            if (transformed && g7 && (meta & LINK_DIRICHLET)) v = (R)(a.omega * a.wall_T[grp]) - v;
+            c = link_sum(a, meta, p, grp, v);
+        }
+        const int32_t lead = __shfl(grp, 0, 64);
+        if (__all(grp == lead || grp < 0)) {
+            c.fx = wave_sum(c.fx);
+            c.fy = wave_sum(c.fy);
+            c.fz = wave_sum(c.fz);
+            c.q = wave_sum(c.q);
+            if ((threadIdx.x & 63) == 0 && lead >= 0) {
+                atomicAdd(&acc[4 * lead + 0], c.fx);
+                atomicAdd(&acc[4 * lead + 1], c.fy);
+                atomicAdd(&acc[4 * lead + 2], c.fz);
+                atomicAdd(&acc[4 * lead + 3], c.q);
+            }
+        } else if (grp >= 0) {
+            atomicAdd(&acc[4 * grp + 0], c.fx);
+            atomicAdd(&acc[4 * grp + 1], c.fy);
+            atomicAdd(&acc[4 * grp + 2], c.fz);
+            atomicAdd(&acc[4 * grp + 3], c.q);
+        }
     }
-    if (a.accumulate) reduce_to_groups(a.accum, grp, c);
+    __syncthreads();
+    for (int i = threadIdx.x; i < 4 * LBM_GROUPS; i += BLOCK)
+        if (acc[i] != 0.0) atomicAdd(a.accum + i, acc[i]);
 }
 
 // ------------------------------------------------------ init / read
@@ -353,7 +438,7 @@ __global__ void __launch_bounds__(BLOCK) k_init(FieldArgs<R> a)
     const int64_t S = G.stride;
     R h[Q19];
     R g[Q7];
-    if (a.labels && a.labels[cell]) {
+    if (a.mask && (a.mask[cell] & MASK_SOLID)) {
         const R nan = (R)__builtin_nan("");
 #pragma unroll
         for (int q = 0; q < Q19; ++q) h[q] = nan;
@@ -397,9 +482,25 @@ __global__ void __launch_bounds__(BLOCK) k_read(FieldArgs<R> a)
 #pragma unroll
             for (int k = 0; k < Q7; ++k) g[k] = a.g[opp7(k) * S + (cell + nb.at(-cx7(k), -cy7(k), -cz7(k)))];
         }
+        // an inflow from a solid neighbour is the bounce of the cell's own
+        // even-step output, kept in (q, x) (see k_aa_step)
+        const uint32_t mk = a.mask ? a.mask[cell] : 0u;
+        if (mk != 0 && !(mk & MASK_SOLID)) {
+#pragma unroll
+            for (int q = 1; q < Q19; ++q)
+                if ((mk >> opp19(q)) & 1u) h[q] = a.f[q * S + cell];
+            if (TH) {
+#pragma unroll
+                for (int k = 1; k < Q7; ++k)
+                    if ((mk >> opp7(k)) & 1u) {
+                        const R v = a.g[k * S + cell];
+                        g[k] = a.solid_dirichlet ? a.solid_gw - v : v;
+                    }
+            }
+        }
     }
     Macro<R> m;
-    if (a.labels && a.labels[cell]) {
+    if (a.mask && (a.mask[cell] & MASK_SOLID)) {
         const R nan = (R)__builtin_nan("");
         m.rho = m.ux = m.uy = m.uz = m.T = nan;
     } else {
@@ -427,27 +528,35 @@ inline dim3 grid_for(int64_t n) { return dim3((unsigned)((n + BLOCK - 1) / BLOCK
 
 }  // namespace
 
+// Pick the <thermal, solid> instance of a cell kernel.
+#define LBM_CELL_LAUNCH(KERNEL, a, thermal, s)                                                              \
+    do {                                                                                                    \
+        const dim3 grid_ = grid_for((a).geo.ncell);                                                         \
+        const bool solid_ = (a).mask != nullptr;                                                            \
+        if (thermal && solid_) hipLaunchKernelGGL((KERNEL<R, true, true>), grid_, dim3(BLOCK), 0, s, a);    \
+        else if (thermal) hipLaunchKernelGGL((KERNEL<R, true, false>), grid_, dim3(BLOCK), 0, s, a);        \
+        else if (solid_) hipLaunchKernelGGL((KERNEL<R, false, true>), grid_, dim3(BLOCK), 0, s, a);         \
+        else hipLaunchKernelGGL((KERNEL<R, false, false>), grid_, dim3(BLOCK), 0, s, a);                    \
+    } while (0)
+
 template <typename R>
 hipError_t launch_aa_step(const StepArgs<R>& a, bool thermal, hipStream_t s)
 {
-    if (thermal) hipLaunchKernelGGL((k_aa_step<R, true>), grid_for(a.geo.ncell), dim3(BLOCK), 0, s, a);
-    else hipLaunchKernelGGL((k_aa_step<R, false>), grid_for(a.geo.ncell), dim3(BLOCK), 0, s, a);
+    LBM_CELL_LAUNCH(k_aa_step, a, thermal, s);
     return hipGetLastError();
 }
 
 template <typename R>
 hipError_t launch_ab_collide(const StepArgs<R>& a, bool thermal, hipStream_t s)
 {
-    if (thermal) hipLaunchKernelGGL((k_ab_collide<R, true>), grid_for(a.geo.ncell), dim3(BLOCK), 0, s, a);
-    else hipLaunchKernelGGL((k_ab_collide<R, false>), grid_for(a.geo.ncell), dim3(BLOCK), 0, s, a);
+    LBM_CELL_LAUNCH(k_ab_collide, a, thermal, s);
     return hipGetLastError();
 }
 
 template <typename R>
 hipError_t launch_ab_pull(const StepArgs<R>& a, bool thermal, hipStream_t s)
 {
-    if (thermal) hipLaunchKernelGGL((k_ab_pull<R, true>), grid_for(a.geo.ncell), dim3(BLOCK), 0, s, a);
-    else hipLaunchKernelGGL((k_ab_pull<R, false>), grid_for(a.geo.ncell), dim3(BLOCK), 0, s, a);
+    LBM_CELL_LAUNCH(k_ab_pull, a, thermal, s);
     return hipGetLastError();
 }
 
@@ -472,6 +581,15 @@ hipError_t launch_link_direct(const LinkArgs<R>& a, hipStream_t s)
 {
     if (a.end <= a.begin) return hipSuccess;
     hipLaunchKernelGGL((k_link_direct<R>), grid_for(a.end - a.begin), dim3(BLOCK), 0, s, a);
+    return hipGetLastError();
+}
+
+template <typename R>
+hipError_t launch_link_force(const LinkArgs<R>& a, hipStream_t s)
+{
+    if (a.end <= a.begin) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((a.end - a.begin + BLOCK - 1) / BLOCK, 1024);
+    hipLaunchKernelGGL((k_link_force<R>), dim3((unsigned)blocks), dim3(BLOCK), 0, s, a);
     return hipGetLastError();
 }
 
@@ -505,6 +623,7 @@ hipError_t launch_zero_f64(double* p, int64_t n, hipStream_t s)
     template hipError_t launch_link_gather<R>(const LinkArgs<R>&, hipStream_t);          \
     template hipError_t launch_link_scatter<R>(const LinkArgs<R>&, hipStream_t);         \
     template hipError_t launch_link_direct<R>(const LinkArgs<R>&, hipStream_t);          \
+    template hipError_t launch_link_force<R>(const LinkArgs<R>&, hipStream_t);           \
     template hipError_t launch_init<R>(const FieldArgs<R>&, bool, hipStream_t);          \
     template hipError_t launch_read<R>(const FieldArgs<R>&, bool, hipStream_t);
 

@@ -84,7 +84,14 @@ def link_dst(lk, opp, odd):
 
 
 class AAModel:
-    def __init__(self, p, lab, rho, u, T):
+    """scheme "links": every cell processed (solids carry NaN), wall links by
+    gather/scatter, solid links by a direct pass.  scheme "inkernel": solid
+    cells skipped, a fluid cell stores a population it sends towards a solid
+    neighbour at the slot the next step reads it from ((p, x + c_p) after an
+    even step, (opp p, x) after an odd one); wall links by gather/scatter."""
+
+    def __init__(self, p, lab, rho, u, T, scheme="links"):
+        self.scheme = scheme
         self.p = p
         self.shape = (p["nx"], p["ny"], p["nz"])
         n = rho.size
@@ -103,6 +110,26 @@ class AAModel:
         self.up7, self.dn7 = neighbour(self.shape, C7, +1), neighbour(self.shape, C7, -1)
         self.t = 0
         self.n = n
+        self.fluid = np.ones(n, bool) if lab is None else (lab == 0)
+        # blocked-by-solid masks per direction (wall crossings excluded)
+        def solid_block(cset, links):
+            m = np.zeros((len(cset), n), bool)
+            for (x, q, xw, grp) in links:
+                if grp >= 6:
+                    m[q, x] = True
+            return m
+        self.sb19 = solid_block(C19, self.fl)
+        self.sb7 = solid_block(C7, self.gl) if self.th else None
+
+        # solid cell s, direction q: (s + c_q, opp q) is a solid link
+        def claims(cset, opp, links):
+            m = np.zeros((len(cset), n), bool)
+            for (x, q, xw, grp) in links:
+                if grp >= 6:
+                    m[opp[q], xw] = True
+            return m
+        self.claim19 = claims(C19, OPP19, self.fl)
+        self.claim7 = claims(C7, OPP7, self.gl) if self.th else None
 
     def _read(self, S, opp, dn, odd):
         Q = S.shape[0]
@@ -110,30 +137,69 @@ class AAModel:
             return S.copy()
         return np.stack([S[opp[q], dn[q]] for q in range(Q)])
 
-    def _write(self, S, vals, opp, up, odd):
+    def _write(self, S, vals, opp, up, odd, sb=None, is_g=False):
         Q = S.shape[0]
         cells = np.arange(self.n)
+        if self.scheme == "links" or not odd:
+            # plain AA stores for every cell (solid cells store their NaN)
+            for q in range(Q):
+                if not odd:
+                    S[opp[q], cells] = vals[q]
+                else:
+                    S[q, up[q]] = vals[q]
+            return
+        # odd step of the in-kernel scheme: fluid cells store every population
+        # at its usual slot, then bounce the ones aimed at a solid neighbour
+        # into (opp p, x); solid cells store everything but their claimed
+        # slots -- applied last, so a wrong claim would overwrite a bounced
+        # value and break the equality
+        fl = self.fluid
         for q in range(Q):
-            if not odd:
-                S[opp[q], cells] = vals[q]
-            else:
-                S[q, up[q]] = vals[q]
+            S[q, up[q][fl]] = vals[q][fl]
+        for q in range(Q):
+            blk = fl & sb[q]
+            vb = vals[q][blk]
+            if is_g:
+                vb = self._solid_rule(vb)
+            S[opp[q], cells[blk]] = vb
+        claimed = self.claim19 if not is_g else self.claim7
+        for q in range(Q):
+            sol = ~fl & ~claimed[q]
+            S[q, up[q][sol]] = vals[q][sol]
+
+    def _solid_rule(self, v):
+        if self.p["solid_thermal"]:
+            return -v + (6 + self.p["a_T"]) / 21 * self.p["solid_T"]
+        return v
+
+    def _reread(self, S, vals, opp, sb, is_g):
+        """odd step: an inflow q whose upstream cell is solid is the bounce of
+        the cell's own even-step output, which sits in (q, x)."""
+        cells = np.arange(self.n)
+        for q in range(S.shape[0]):
+            blk = self.fluid & sb[opp[q]]
+            v = S[q, cells[blk]]
+            vals[q][blk] = self._solid_rule(v) if is_g else v
 
     def step(self):
         odd = self.t & 1
         f = self._read(self.A, OPP19, self.dn19, odd)
         g = self._read(self.B, OPP7, self.dn7, odd) if self.th else None
+        if self.scheme == "inkernel" and odd:
+            self._reread(self.A, f, OPP19, self.sb19, False)
+            if self.th:
+                self._reread(self.B, g, OPP7, self.sb7, True)
         fp, gp, _ = oracle.collide(self.p, f.T.copy(), g.T.copy() if self.th else None)
-        self._write(self.A, fp.T, OPP19, self.up19, odd)
+        self._write(self.A, fp.T, OPP19, self.up19, odd, self.sb19)
         if self.th:
-            self._write(self.B, gp.T, OPP7, self.up7, odd)
+            self._write(self.B, gp.T, OPP7, self.up7, odd, self.sb7, is_g=True)
         # wall links: gather every source first, then scatter; solid links: one
         # direct pass, each link read and written immediately
         for S, links, opp, is_g in ((self.A, self.fl, OPP19, False), (self.B, self.gl, OPP7, True)):
             if not links:
                 continue
             wall = [lk for lk in links if lk[3] < 6]
-            solid = [lk for lk in links if lk[3] >= 6]
+            solid = [lk for lk in links if lk[3] >= 6] if self.scheme == "links" else []
             vals = [S[link_src(lk, opp, odd)] for lk in wall]
             for lk, v in zip(wall, vals):
                 S[link_dst(lk, opp, odd)] = self._rule(lk, v, is_g)
@@ -154,6 +220,10 @@ class AAModel:
         odd = self.t & 1
         f = self._read(self.A, OPP19, self.dn19, odd)
         g = self._read(self.B, OPP7, self.dn7, odd) if self.th else None
+        if self.scheme == "inkernel" and odd:
+            self._reread(self.A, f, OPP19, self.sb19, False)
+            if self.th:
+                self._reread(self.B, g, OPP7, self.sb7, True)
         return f, g
 
 
@@ -186,13 +256,19 @@ def case(name):
         rho, u = inputs.taylor_green(nx, ny, nz, u0=0.03, seed=14)
         T = np.random.default_rng(15).uniform(-0.5, 0.5, nx * ny * nz)
         return p, lab, rho, u, T
+    if name == "dirichlet_solid":
+        p, lab, rho, u, T = case("rb_spheres")
+        p = dict(p, solid_thermal=1, solid_T=-0.3, face_kind=[WALL] * 6, face_thermal=[1, 1, 0, 0, 1, 1],
+                 face_T=[0.1, -0.1, 0, 0, 0.5, -0.5])
+        return p, lab, rho, u, T
     raise KeyError(name)
 
 
-@pytest.mark.parametrize("name", ["walls_solids", "cavity_thermal", "rb_spheres"])
-def test_aa_equals_two_buffer_bitwise(name):
+@pytest.mark.parametrize("scheme", ["links", "inkernel"])
+@pytest.mark.parametrize("name", ["walls_solids", "cavity_thermal", "rb_spheres", "dirichlet_solid"])
+def test_aa_equals_two_buffer_bitwise(name, scheme):
     p, lab, rho, u, T = case(name)
-    model = AAModel(p, lab, rho, u, T)
+    model = AAModel(p, lab, rho, u, T, scheme=scheme)
     fluid = np.ones(rho.size, bool) if lab is None else lab == 0
     for n in range(1, 8):
         model.step()
