@@ -78,6 +78,15 @@ enum { LBM_FACE_PERIODIC = 0, LBM_FACE_WALL = 1 };
 enum { LBM_ADIABATIC = 0, LBM_DIRICHLET = 1 };
 enum { LBM_STREAM_AUTO = 0, LBM_STREAM_AA = 1, LBM_STREAM_AB = 2 };
 enum { LBM_MAX_GROUPS = 261 }; /* 6 faces + 255 solid labels */
+/* Where half-way bounce-back happens.  IN_KERNEL: inside the step kernel (a
+ * fluid cell next to a wall or solid re-reads and re-stores the bounced
+ * populations in the odd step; solid cells are found from a per-cell mask,
+ * walls from coordinates).  PASSES: the step kernel streams every cell as if
+ * the box were periodic and separate link passes fix the blocked directions,
+ * a gather of every link's source into scratch, then a scatter (the design of
+ * "GPU lattice Boltzmann: streaming layout and performance").  Both give the
+ * same populations bit for bit; IN_KERNEL moves fewer bytes. */
+enum { LBM_LINKS_IN_KERNEL = 0, LBM_LINKS_PASSES = 1 };
 
 /* Faces are numbered 0..5 = x-, x+, y-, y+, z-, z+.  Force/heat group g is
  * face g for g < 6 and solid label g - 5 for g >= 6. */
@@ -90,7 +99,7 @@ typedef struct lbm_params {
     int32_t face_thermal[6]; /* LBM_ADIABATIC or LBM_DIRICHLET (wall faces) */
     double face_T[6];        /* Dirichlet wall temperature per face */
     int32_t solid_thermal;   /* thermal rule of every solid cell */
-    int32_t reserved0;       /* must be 0 */
+    int32_t links;           /* LBM_LINKS_IN_KERNEL (0) or LBM_LINKS_PASSES (1), see below */
     double solid_T;          /* Dirichlet temperature of the solids */
     double s19[19];          /* D3Q19 relaxation rates, row order above, each in [0, 2) */
     double s7[7];            /* D3Q7 relaxation rates, row order above, each in [0, 2) */

@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblbm_hip.
 LBM_OK, LBM_E_INVALID, LBM_E_NOMEM, LBM_E_DEVICE, LBM_E_UNSTABLE = 0, 1, 2, 3, 4
 STATUS_NAMES = {0: "LBM_OK", 1: "LBM_E_INVALID", 2: "LBM_E_NOMEM", 3: "LBM_E_DEVICE", 4: "LBM_E_UNSTABLE"}
 LBM_STREAM_AUTO, LBM_STREAM_AA, LBM_STREAM_AB = 0, 1, 2
+LBM_LINKS_IN_KERNEL, LBM_LINKS_PASSES = 0, 1
 MAX_GROUPS = 261
 
 # every function the header declares
@@ -38,7 +39,7 @@ class LbmParams(ctypes.Structure):
         ("dtype", ctypes.c_int32), ("streaming", ctypes.c_int32), ("thermal", ctypes.c_int32),
         ("face_kind", ctypes.c_int32 * 6), ("face_thermal", ctypes.c_int32 * 6),
         ("face_T", ctypes.c_double * 6),
-        ("solid_thermal", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+        ("solid_thermal", ctypes.c_int32), ("links", ctypes.c_int32),
         ("solid_T", ctypes.c_double),
         ("s19", ctypes.c_double * 19), ("s7", ctypes.c_double * 7),
         ("a_T", ctypes.c_double), ("accel", ctypes.c_double * 3), ("gbeta", ctypes.c_double * 3),
@@ -103,7 +104,7 @@ def to_params(d: dict, dtype: int = 4, streaming: int = LBM_STREAM_AUTO) -> LbmP
         p.face_thermal[i] = int(d.get("face_thermal", [0] * 6)[i])
         p.face_T[i] = float(d.get("face_T", [0.0] * 6)[i])
     p.solid_thermal = int(d.get("solid_thermal", 0))
-    p.reserved0 = 0
+    p.links = int(d.get("links", LBM_LINKS_IN_KERNEL))
     p.solid_T = float(d.get("solid_T", 0.0))
     for i in range(19):
         p.s19[i] = float(d["s19"][i])

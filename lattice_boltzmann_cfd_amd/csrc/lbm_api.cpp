@@ -39,6 +39,7 @@ struct lbm_ctx {
     int64_t n_f = 0, n_g = 0, n_wall = 0;
     int64_t t = 0;
     bool initialised = false;
+    bool in_kernel = false;  // bounce-back inside the step kernel
     std::string err;
     Collision<float> colf{};
     Collision<double> cold{};
@@ -94,7 +95,7 @@ std::string validate(const lbm_params* p)
         return "nx*ny*nz*dtype too large for 32-bit plane offsets";
     if (p->streaming < 0 || p->streaming > 2) return "streaming must be 0, 1 or 2";
     if (p->thermal != 0 && p->thermal != 1) return "thermal must be 0 or 1";
-    if (p->reserved0 != 0) return "reserved0 must be 0";
+    if (p->links != LBM_LINKS_IN_KERNEL && p->links != LBM_LINKS_PASSES) return "links must be 0 or 1";
     for (int f = 0; f < 6; ++f) {
         if (p->face_kind[f] != LBM_FACE_PERIODIC && p->face_kind[f] != LBM_FACE_WALL) return "bad face_kind";
         if (p->face_thermal[f] != LBM_ADIABATIC && p->face_thermal[f] != LBM_DIRICHLET) return "bad face_thermal";
@@ -149,6 +150,22 @@ Collision<R> make_collision(const lbm_params* p)
     c.T0 = (R)p->T0;
     c.a_T = (R)p->a_T;
     return c;
+}
+
+template <typename R>
+Bounce<R> make_bounce(const lbm_params* p, bool in_kernel)
+{
+    Bounce<R> b{};
+    const double omega = (6.0 + p->a_T) / 21.0;
+    for (int f = 0; f < 6; ++f) {
+        b.face_gw[f] = (R)(omega * p->face_T[f]);
+        if (p->face_kind[f] == LBM_FACE_WALL) b.walls |= 1 << f;
+        if (p->face_thermal[f] == LBM_DIRICHLET) b.face_dirichlet |= 1 << f;
+    }
+    b.solid_gw = (R)(omega * p->solid_T);
+    b.solid_dirichlet = p->solid_thermal == LBM_DIRICHLET ? 1 : 0;
+    b.in_kernel = in_kernel ? 1 : 0;
+    return b;
 }
 
 // ------------------------------------------------------------- links
@@ -402,6 +419,7 @@ LinkArgs<R> link_args(lbm_ctx* c, int mode, char* fsrc, char* fdst, char* gsrc, 
     a.end = c->n_f + c->n_g;
     a.omega = (6.0 + c->p.a_T) / 21.0;
     a.mode = mode;
+    a.in_kernel = c->in_kernel ? 1 : 0;
     return a;
 }
 
@@ -416,6 +434,7 @@ template <typename R>
 lbm_status step_impl(lbm_ctx* c, int64_t n)
 {
     const int64_t n_links = c->n_f + c->n_g;
+    const bool passes = !c->in_kernel && n_links > 0;
     for (int64_t k = 0; k < n; ++k) {
         const bool last = (k == n - 1);
         const int parity = (int)(c->t & 1);
@@ -423,20 +442,19 @@ lbm_status step_impl(lbm_ctx* c, int64_t n)
         s.geo = c->geo;
         s.col = collision<R>(c);
         s.mask = c->mask;
-        s.solid_gw = (R)((6.0 + c->p.a_T) / 21.0 * c->p.solid_T);
-        s.solid_dirichlet = c->p.solid_thermal == LBM_DIRICHLET ? 1 : 0;
+        s.bb = make_bounce<R>(&c->p, c->in_kernel);
         LinkArgs<R> la;
         if (!c->ab) {
-            // one in-place kernel: collision, streaming and solid bounce-back
+            // one in-place kernel: collision, streaming (and bounce-back)
             s.f = (R*)c->f;
             s.g = (R*)c->g;
             s.parity = parity;
             LBM_HIP(c, launch_aa_step<R>(s, c->thermal, c->stream), "AA step kernel");
             la = link_args<R>(c, parity == 0 ? LINK_AA_AFTER_EVEN : LINK_AA_AFTER_ODD, c->f, c->f, c->g, c->g);
-            if (c->n_wall > 0) {
-                // wall links: gather every source, then scatter
+            if (passes) {
+                // link passes: gather every source, then scatter
                 la.begin = 0;
-                la.end = c->n_wall;
+                la.end = n_links;
                 LBM_HIP(c, launch_link_gather<R>(la, c->stream), "link gather kernel");
                 LBM_HIP(c, launch_link_scatter<R>(la, c->stream), "link scatter kernel");
             }
@@ -452,16 +470,16 @@ lbm_status step_impl(lbm_ctx* c, int64_t n)
             LBM_HIP(c, launch_ab_collide<R>(s, c->thermal, c->stream), "A-B collide kernel");
             LBM_HIP(c, launch_ab_pull<R>(s, c->thermal, c->stream), "A-B pull kernel");
             la = link_args<R>(c, LINK_AB, fa, fb, ga, gb);
-            if (c->n_wall > 0) {
+            if (passes) {
                 // sources in one buffer, destinations in the other: one pass
                 la.begin = 0;
-                la.end = c->n_wall;
+                la.end = n_links;
                 LBM_HIP(c, launch_link_direct<R>(la, c->stream), "link kernel");
             }
         }
         if (last) {
-            // forces and heat of the submission's last step, read from every
-            // link's destination slot
+            // forces and heat of the submission's last step, read where each
+            // link's bounced population was left
             LBM_HIP(c, launch_zero_f64(c->accum, 4 * LBM_MAX_GROUPS, c->stream), "zero accumulators");
             la.begin = 0;
             la.end = n_links;
@@ -484,8 +502,7 @@ FieldArgs<R> field_args(lbm_ctx* c)
     a.unstable = c->unstable;
     a.parity = (int32_t)(c->t & 1);
     a.ab = c->ab ? 1 : 0;
-    a.solid_gw = (R)((6.0 + c->p.a_T) / 21.0 * c->p.solid_T);
-    a.solid_dirichlet = c->p.solid_thermal == LBM_DIRICHLET ? 1 : 0;
+    a.bb = make_bounce<R>(&c->p, c->in_kernel);
     a.col = collision<R>(c);
     return a;
 }
@@ -580,6 +597,9 @@ lbm_status lbm_create(const lbm_params* p, const uint8_t* solid_labels, void* de
         c->unstable = (int32_t*)(base + L.unstable);
         c->colf = make_collision<float>(p);
         c->cold = make_collision<double>(p);
+        const bool walls = p->face_kind[0] == LBM_FACE_WALL || p->face_kind[2] == LBM_FACE_WALL ||
+                           p->face_kind[4] == LBM_FACE_WALL;
+        c->in_kernel = p->links == LBM_LINKS_IN_KERNEL && (walls || solids);
 
         // order the links of both lattices and upload
         LinkList all;

@@ -50,9 +50,9 @@ constexpr uint32_t LINK_D3Q7 = 1u << 15;
 // Per-cell solid mask (only when the box has solid cells).  On a fluid cell,
 // bit q (1..18) is set when x + c_q is a solid cell reached without crossing
 // a wall face (a solid link).  On a solid cell, MASK_SOLID is set and bit q
-// marks that (s + c_q, opp q) is such a solid link of a fluid neighbour, whose
-// bounce-back store claims the slot the solid cell would store direction q
-// to.  D3Q7 direction k (1..6) is the D3Q19 axis direction k, so bits 1..6
+// marks that (s + c_q, opp q) is such a solid link of a fluid neighbour,
+// which re-reads and re-stores the slot the solid cell's odd step would store
+// direction q to.  D3Q7 direction k (1..6) is the D3Q19 axis direction k, so bits 1..6
 // serve both lattices.
 constexpr uint32_t MASK_SOLID = 1u << 31;
 
@@ -63,6 +63,20 @@ enum LinkMode : int32_t {
     LINK_AB = 2,             // src A(p, x) post-collision, dst B(opp p, x)
 };
 
+// Bounce-back constants of the in-kernel boundary handling.  Wall faces are
+// numbered 0..5 = x-, x+, y-, y+, z-, z+; walls[f] is set for a no-slip face.
+// A D3Q7 population bouncing off face f becomes gw[f] - g (anti-bounce-back,
+// Dirichlet face) or g (adiabatic); off a solid, solid_gw - g or g.
+template <typename R>
+struct Bounce {
+    R face_gw[6];
+    R solid_gw;
+    int32_t walls;            // bit f: face f is a wall
+    int32_t face_dirichlet;   // bit f: face f has a Dirichlet temperature
+    int32_t solid_dirichlet;  // solids have a Dirichlet temperature
+    int32_t in_kernel;        // walls and solids are handled inside the step kernel
+};
+
 template <typename R>
 struct StepArgs {
     Geometry geo;
@@ -71,9 +85,9 @@ struct StepArgs {
     R* f2; // AB: destination buffer of the pull
     R* g2;
     const uint32_t* mask;  // solid mask, or null when the box has no solid cell
-    R solid_gw;            // w T_solid (anti-bounce-back constant of the solids)
-    int32_t solid_dirichlet;
+    Bounce<R> bb;
     int32_t parity;
+    int32_t pad0;
     Collision<R> col;
 };
 
@@ -94,7 +108,7 @@ struct LinkArgs {
     int64_t end;    // one past the last link of the launch
     double omega;          // (6 + a_T)/21
     int32_t mode;
-    int32_t pad0;
+    int32_t in_kernel;     // bounce-back happened inside the step kernel
 };
 
 template <typename R>
@@ -112,8 +126,7 @@ struct FieldArgs {
     int32_t* unstable;
     int32_t parity;
     int32_t ab;  // populations in natural layout (two-buffer mode)
-    R solid_gw;  // w T_solid
-    int32_t solid_dirichlet;
+    Bounce<R> bb;
     Collision<R> col;
 };
 

@@ -50,6 +50,7 @@ __device__ __forceinline__ double w19_rt(int q) { return q == 0 ? 1.0 / 3.0 : (q
 // once and each axis wraps with a compare and an add.
 struct Nbr {
     int32_t xm, xp, ym, yp, zm, zp;
+    uint32_t faces;  // bit f: the cell touches box face f (x-, x+, y-, y+, z-, z+)
 
     __device__ __forceinline__ Nbr(const Geometry& G, int32_t cell)
     {
@@ -63,6 +64,8 @@ struct Nbr {
         yp = (y == G.ny - 1) ? (1 - G.ny) * G.nx : G.nx;
         zm = ((int32_t)z == 0) ? (G.nz - 1) * G.nxy : -G.nxy;
         zp = ((int32_t)z == G.nz - 1) ? (1 - G.nz) * G.nxy : G.nxy;
+        faces = (x == 0 ? 1u : 0u) | (x == G.nx - 1 ? 2u : 0u) | (y == 0 ? 4u : 0u) | (y == G.ny - 1 ? 8u : 0u) |
+                ((int32_t)z == 0 ? 16u : 0u) | ((int32_t)z == G.nz - 1 ? 32u : 0u);
     }
     // offset of the cell at x + (cx, cy, cz), each component in {-1, 0, 1}
     __device__ __forceinline__ int32_t at(int cx, int cy, int cz) const
@@ -88,33 +91,82 @@ __device__ __forceinline__ void st(R* plane, int32_t idx, R v)
     *reinterpret_cast<R*>(reinterpret_cast<char*>(plane) + (uint32_t)idx * (uint32_t)sizeof(R)) = v;
 }
 
-// ------------------------------------------------------------ AA step
+// ------------------------------------------------------ boundaries
 
-// Value a D3Q7 population takes when it bounces off a solid cell:
-// anti-bounce-back -g^+ + w T_solid (Dirichlet) or g^+ (adiabatic).
-template <typename R>
-__device__ __forceinline__ R solid_rule(const StepArgs<R>& a, R v)
+// D3Q19 directions leaving the box through face f (x-, x+, y-, y+, z-, z+).
+__host__ __device__ constexpr uint32_t dirs_through(int f)
 {
-    return a.solid_dirichlet ? a.solid_gw - v : v;
+    uint32_t m = 0;
+    for (int q = 1; q < Q19; ++q) {
+        const int c = (f >> 1) == 0 ? cx19(q) : ((f >> 1) == 1 ? cy19(q) : cz19(q));
+        if ((f & 1) ? c > 0 : c < 0) m |= 1u << q;
+    }
+    return m;
 }
 
-// One fused time step in place.  With SOLID the fluid cells next to solid
-// cells apply half-way bounce-back themselves ("Multi-GPU thermal lattice
-// Boltzmann simulations using OpenACC and MPI", Sec. 2), and all of it happens
-// in the odd step, so the even step stays the plain kernel for every cell:
-//  * even step: each cell stores f_p^+ at (opp p, x) as usual, solid cells
-//    included (on NaN; nobody reads a solid cell's slots in the odd step);
-//  * odd step, inflow: a population q whose upstream cell x - c_q is solid is
-//    the bounce of f_opp(q)^+(x) from the even step, which sits in (q, x) of
-//    the cell itself -- it is read there instead;
-//  * odd step, outflow: f_p^+ for a direction p that points at a solid cell is
-//    stored, besides its usual slot (read next only by the solid cell), at
-//    (opp p, x), where the next (even) step reads it.
-// A solid cell's usual odd-step store of direction q lands in (q, s + c_q);
-// when s + c_q is a fluid cell bouncing off s that slot is the fluid cell's
-// re-read and bounce-back slot, so the solid cell skips it (its mask bit q).
-// No other slot is touched by two cells in one step.
-template <typename R, bool TH, bool SOLID>
+// Face crossed by D3Q7 direction k (1..6).
+__host__ __device__ constexpr int face7(int k) { return (k - 1) ^ 1; }
+
+// Blocked directions of one cell for the in-kernel bounce-back: `wall` holds
+// the directions that leave through a no-slip face (from the coordinates),
+// `solid` those whose neighbour is a solid cell (mask of a fluid cell), and
+// `claim` on a solid cell the directions whose odd-step slot a fluid
+// neighbour re-reads and re-stores (mask bits of a solid cell).
+struct Blocked {
+    uint32_t wall, solid, claim;
+    bool is_solid;
+};
+
+template <typename R>
+__device__ __forceinline__ Blocked blocked_dirs(const Bounce<R>& bb, const uint32_t* mask, int32_t cell,
+                                                uint32_t faces)
+{
+    Blocked b;
+    const uint32_t fw = faces & (uint32_t)bb.walls;
+    b.wall = ((fw & 1u) ? dirs_through(0) : 0u) | ((fw & 2u) ? dirs_through(1) : 0u) |
+             ((fw & 4u) ? dirs_through(2) : 0u) | ((fw & 8u) ? dirs_through(3) : 0u) |
+             ((fw & 16u) ? dirs_through(4) : 0u) | ((fw & 32u) ? dirs_through(5) : 0u);
+    const uint32_t m = mask ? mask[cell] : 0u;
+    b.is_solid = (m & MASK_SOLID) != 0;
+    b.solid = b.is_solid ? 0u : m;
+    b.claim = b.is_solid ? (m & ~MASK_SOLID) : 0u;
+    return b;
+}
+
+// The value a D3Q7 population takes when it bounces in direction k's face or
+// off a solid: anti-bounce-back gw - g (Dirichlet) or g (adiabatic).
+template <typename R>
+__device__ __forceinline__ R bounce7(const Bounce<R>& bb, const Blocked& b, int k, R v)
+{
+    if ((b.wall >> k) & 1u) {
+        const int f = face7(k);
+        return ((bb.face_dirichlet >> f) & 1) ? bb.face_gw[f] - v : v;
+    }
+    return bb.solid_dirichlet ? bb.solid_gw - v : v;
+}
+
+// ------------------------------------------------------------ AA step
+
+
+// One fused time step in place.  With BND the step also applies half-way
+// bounce-back at no-slip walls and solid cells ("Multi-GPU thermal lattice
+// Boltzmann simulations using OpenACC and MPI", Sec. 2); without it the box
+// streams as if periodic and link passes fix the blocked directions.
+// All bounce-back work happens in the odd step; the even step is the plain
+// kernel for every cell (solid cells compute on NaN in their own slots):
+//  * even step: every cell stores f_p^+ at (opp p, x);
+//  * odd step, inflow: a population q whose upstream cell x - c_q is across
+//    a wall or solid is the bounce of f_opp(q)^+(x) from the even step, which
+//    sits in (q, x) of the cell itself -- it is read there;
+//  * odd step, outflow: f_p^+ for a blocked direction p is stored at
+//    (opp p, x), where the next (even) step reads it.  Its usual slot is
+//    skipped when p leaves through a wall (the addressing wraps onto the cell
+//    across the box, whose slot that is) and kept when p points at a solid
+//    cell (only that solid cell reads it next).
+// A solid cell skips its odd-step stores into slots a fluid neighbour claims
+// this way (mask bits) and into wrapped slots across a wall.  No slot is
+// touched by two cells in one step.
+template <typename R, bool TH, bool BND>
 __global__ void __launch_bounds__(BLOCK) k_aa_step(StepArgs<R> a)
 {
     const Geometry& G = a.geo;
@@ -139,60 +191,61 @@ __global__ void __launch_bounds__(BLOCK) k_aa_step(StepArgs<R> a)
 #pragma unroll
             for (int k = 0; k < Q7; ++k) st(gg + opp7(k) * S, cell, g[k]);
         }
-    } else {
-        const uint32_t m = SOLID ? a.mask[cell] : 0u;
-        const bool solid = SOLID && (m & MASK_SOLID);
-        const bool near = SOLID && !solid && m != 0;
-        const Nbr nb(G, cell);
+        return;
+    }
+    const Nbr nb(G, cell);
+    Blocked b{0u, 0u, 0u, false};
+    if (BND) b = blocked_dirs(a.bb, a.mask, cell, nb.faces);
+    const uint32_t blk = b.wall | b.solid;           // a fluid cell's bounced directions
+    const uint32_t skip = b.wall | b.claim;          // usual odd-step stores to leave out
+    const bool near = BND && !b.is_solid && blk != 0;
 #pragma unroll
-        for (int q = 0; q < Q19; ++q) h[q] = ld(f + opp19(q) * S, cell + nb.at(-cx19(q), -cy19(q), -cz19(q)));
+    for (int q = 0; q < Q19; ++q) h[q] = ld(f + opp19(q) * S, cell + nb.at(-cx19(q), -cy19(q), -cz19(q)));
+    if (TH) {
+#pragma unroll
+        for (int k = 0; k < Q7; ++k) g[k] = ld(gg + opp7(k) * S, cell + nb.at(-cx7(k), -cy7(k), -cz7(k)));
+    }
+    if (near) {
+#pragma unroll
+        for (int q = 1; q < Q19; ++q)
+            if ((blk >> opp19(q)) & 1u) h[q] = ld(f + q * S, cell);
         if (TH) {
 #pragma unroll
-            for (int k = 0; k < Q7; ++k) g[k] = ld(gg + opp7(k) * S, cell + nb.at(-cx7(k), -cy7(k), -cz7(k)));
+            for (int k = 1; k < Q7; ++k)
+                if ((blk >> opp7(k)) & 1u) g[k] = bounce7(a.bb, b, opp7(k), ld(gg + k * S, cell));
         }
-        if (near) {
+    }
+    collide<R, TH>(h, g, a.col);
 #pragma unroll
-            for (int q = 1; q < Q19; ++q)
-                if ((m >> opp19(q)) & 1u) h[q] = ld(f + q * S, cell);
-            if (TH) {
+    for (int q = 0; q < Q19; ++q)
+        if (!BND || !((skip >> q) & 1u)) st(f + q * S, cell + nb.at(cx19(q), cy19(q), cz19(q)), h[q]);
+    if (TH) {
 #pragma unroll
-                for (int k = 1; k < Q7; ++k)
-                    if ((m >> opp7(k)) & 1u) g[k] = solid_rule(a, ld(gg + k * S, cell));
-            }
-        }
-        collide<R, TH>(h, g, a.col);
+        for (int k = 0; k < Q7; ++k)
+            if (!BND || !((skip >> k) & 1u)) st(gg + k * S, cell + nb.at(cx7(k), cy7(k), cz7(k)), g[k]);
+    }
+    if (near) {
 #pragma unroll
-        for (int q = 0; q < Q19; ++q)
-            if (!solid || !((m >> q) & 1u)) st(f + q * S, cell + nb.at(cx19(q), cy19(q), cz19(q)), h[q]);
+        for (int q = 1; q < Q19; ++q)
+            if ((blk >> q) & 1u) st(f + opp19(q) * S, cell, h[q]);
         if (TH) {
 #pragma unroll
-            for (int k = 0; k < Q7; ++k)
-                if (!solid || !((m >> k) & 1u)) st(gg + k * S, cell + nb.at(cx7(k), cy7(k), cz7(k)), g[k]);
-        }
-        if (near) {
-#pragma unroll
-            for (int q = 1; q < Q19; ++q)
-                if ((m >> q) & 1u) st(f + opp19(q) * S, cell, h[q]);
-            if (TH) {
-#pragma unroll
-                for (int k = 1; k < Q7; ++k)
-                    if ((m >> k) & 1u) st(gg + opp7(k) * S, cell, solid_rule(a, g[k]));
-            }
+            for (int k = 1; k < Q7; ++k)
+                if ((blk >> k) & 1u) st(gg + opp7(k) * S, cell, bounce7(a.bb, b, k, g[k]));
         }
     }
 }
 
 // ------------------------------------------------- two buffers (A-B)
 
-// Collide in place: every population stays in its own slot.
-template <typename R, bool TH, bool SOLID>
+// Collide in place: every population stays in its own slot (solid cells
+// compute on NaN in theirs; no fluid cell pulls from a solid slot).
+template <typename R, bool TH, bool BND>
 __global__ void __launch_bounds__(BLOCK) k_ab_collide(StepArgs<R> a)
 {
     const Geometry& G = a.geo;
     const int32_t cell = (int32_t)(blockIdx.x * BLOCK + threadIdx.x);
     if (cell >= G.ncell) return;
-    // solid cells collide NaN in their own slots: nothing else writes this
-    // buffer in this kernel and no fluid cell pulls from a solid slot
     const int64_t S = G.stride;
     R h[Q19];
     R g[Q7];
@@ -211,32 +264,31 @@ __global__ void __launch_bounds__(BLOCK) k_ab_collide(StepArgs<R> a)
     }
 }
 
-// Pull into the other buffer: B(q, x) = A(q, x - c_q); when x - c_q is a
-// solid cell the population comes back from x itself: B(q, x) = A(opp q, x)
-// (anti-bounce-back for a Dirichlet D3Q7 population).
-template <typename R, bool TH, bool SOLID>
+// Pull into the other buffer: B(q, x) = A(q, x - c_q).  With BND, when
+// x - c_q is across a wall or a solid cell the population comes back from x
+// itself: B(q, x) = A(opp q, x) (anti-bounce-back for a Dirichlet D3Q7 one).
+template <typename R, bool TH, bool BND>
 __global__ void __launch_bounds__(BLOCK) k_ab_pull(StepArgs<R> a)
 {
     const Geometry& G = a.geo;
     const int32_t cell = (int32_t)(blockIdx.x * BLOCK + threadIdx.x);
     if (cell >= G.ncell) return;
-    // a solid cell pulls garbage into its own slots of the other buffer, which
-    // no fluid cell reads; its mask bits are never those of a fluid cell's
-    const uint32_t m = SOLID ? a.mask[cell] : 0u;
-    const bool solid = SOLID && (m & MASK_SOLID);
     const int64_t S = G.stride;
     const Nbr nb(G, cell);
+    Blocked b{0u, 0u, 0u, false};
+    if (BND) b = blocked_dirs(a.bb, a.mask, cell, nb.faces);
+    const uint32_t blk = b.is_solid ? 0u : (b.wall | b.solid);
 #pragma unroll
     for (int q = 0; q < Q19; ++q) {
         R v = ld(a.f + q * S, cell + nb.at(-cx19(q), -cy19(q), -cz19(q)));
-        if (SOLID && !solid && ((m >> opp19(q)) & 1u)) v = ld(a.f + opp19(q) * S, cell);
+        if (BND && ((blk >> opp19(q)) & 1u)) v = ld(a.f + opp19(q) * S, cell);
         st(a.f2 + q * S, cell, v);
     }
     if (TH) {
 #pragma unroll
         for (int k = 0; k < Q7; ++k) {
             R v = ld(a.g + k * S, cell + nb.at(-cx7(k), -cy7(k), -cz7(k)));
-            if (SOLID && !solid && ((m >> opp7(k)) & 1u)) v = solid_rule(a, ld(a.g + opp7(k) * S, cell));
+            if (BND && ((blk >> opp7(k)) & 1u)) v = bounce7(a.bb, b, opp7(k), ld(a.g + opp7(k) * S, cell));
             st(a.g2 + k * S, cell, v);
         }
     }
@@ -362,10 +414,10 @@ __global__ void __launch_bounds__(BLOCK) k_link_direct(LinkArgs<R> a)
 }
 
 // Force pass, on a submission's last step only, over every link.  It reads
-// the bounced population f_p^+ of each link where the step left it: for a
-// wall link its scatter destination; for a solid link (opp p, x) in place
-// (the even step's usual store, or the odd step's bounce-back store) and
-// B(opp p, x) with two buffers.  Values a D3Q7 Dirichlet link stores after
+// the bounced population f_p^+ of each link where the step left it: with
+// in-kernel bounce-back (opp p, x) in place (the even step's usual store or
+// the odd step's bounce-back store); with link passes the scatter
+// destination; with two buffers B(opp p, x).  Values a D3Q7 Dirichlet link stores after
 // anti-bounce-back are converted back.  It sums the momentum exchange
 // 2 c_p f_p^+ and the heat w T_w - 2 g_p^+ per group: wavefront shuffles, then
 // fp64 LDS atomics per block, then one global atomic per block and touched
@@ -389,15 +441,17 @@ __global__ void __launch_bounds__(BLOCK) k_link_force(LinkArgs<R> a)
             const bool g7 = (meta & LINK_D3Q7) != 0;
             int32_t plane, idx;
             bool transformed;
-            if (grp < 6 || a.mode == LINK_AB) {
+            if (a.in_kernel && a.mode != LINK_AB) {
+                // even step: the usual store; odd step: the bounce-back store
+                plane = opp_rt(p);
+                idx = a.cell[l];
+                transformed = a.mode == LINK_AA_AFTER_ODD;
+            } else {
+                // link passes, or the two-buffer pull: the link's destination
                 const LinkSlots sl = link_slots(a.mode, p, a.cell[l], a.cellw[l]);
                 plane = sl.dst_plane;
                 idx = sl.dst_idx;
                 transformed = true;
-            } else {
-                plane = opp_rt(p);
-                idx = a.cell[l];
-                transformed = a.mode == LINK_AA_AFTER_ODD;
             }
             R v = ld((g7 ? a.g_dst : a.f_dst) + plane * S, idx);
             if (transformed && g7 && (meta & LINK_DIRICHLET)) v = (R)(a.omega * a.wall_T[grp]) - v;
@@ -482,20 +536,20 @@ __global__ void __launch_bounds__(BLOCK) k_read(FieldArgs<R> a)
 #pragma unroll
             for (int k = 0; k < Q7; ++k) g[k] = a.g[opp7(k) * S + (cell + nb.at(-cx7(k), -cy7(k), -cz7(k)))];
         }
-        // an inflow from a solid neighbour is the bounce of the cell's own
-        // even-step output, kept in (q, x) (see k_aa_step)
-        const uint32_t mk = a.mask ? a.mask[cell] : 0u;
-        if (mk != 0 && !(mk & MASK_SOLID)) {
+        // with in-kernel bounce-back, an inflow from across a wall or a solid
+        // is the bounce of the cell's own even-step output, kept in (q, x)
+        if (a.bb.in_kernel) {
+            const Blocked b = blocked_dirs(a.bb, a.mask, cell, nb.faces);
+            const uint32_t blk = b.is_solid ? 0u : (b.wall | b.solid);
+            if (blk != 0) {
 #pragma unroll
-            for (int q = 1; q < Q19; ++q)
-                if ((mk >> opp19(q)) & 1u) h[q] = a.f[q * S + cell];
-            if (TH) {
+                for (int q = 1; q < Q19; ++q)
+                    if ((blk >> opp19(q)) & 1u) h[q] = a.f[q * S + cell];
+                if (TH) {
 #pragma unroll
-                for (int k = 1; k < Q7; ++k)
-                    if ((mk >> opp7(k)) & 1u) {
-                        const R v = a.g[k * S + cell];
-                        g[k] = a.solid_dirichlet ? a.solid_gw - v : v;
-                    }
+                    for (int k = 1; k < Q7; ++k)
+                        if ((blk >> opp7(k)) & 1u) g[k] = bounce7(a.bb, b, opp7(k), a.g[k * S + cell]);
+                }
             }
         }
     }
@@ -528,11 +582,11 @@ inline dim3 grid_for(int64_t n) { return dim3((unsigned)((n + BLOCK - 1) / BLOCK
 
 }  // namespace
 
-// Pick the <thermal, solid> instance of a cell kernel.
+// Pick the <thermal, in-kernel bounce-back> instance of a cell kernel.
 #define LBM_CELL_LAUNCH(KERNEL, a, thermal, s)                                                              \
     do {                                                                                                    \
         const dim3 grid_ = grid_for((a).geo.ncell);                                                         \
-        const bool solid_ = (a).mask != nullptr;                                                            \
+        const bool solid_ = (a).bb.in_kernel != 0;                                                          \
         if (thermal && solid_) hipLaunchKernelGGL((KERNEL<R, true, true>), grid_, dim3(BLOCK), 0, s, a);    \
         else if (thermal) hipLaunchKernelGGL((KERNEL<R, true, false>), grid_, dim3(BLOCK), 0, s, a);        \
         else if (solid_) hipLaunchKernelGGL((KERNEL<R, false, true>), grid_, dim3(BLOCK), 0, s, a);         \

@@ -84,11 +84,13 @@ def link_dst(lk, opp, odd):
 
 
 class AAModel:
-    """scheme "links": every cell processed (solids carry NaN), wall links by
-    gather/scatter, solid links by a direct pass.  scheme "inkernel": solid
-    cells skipped, a fluid cell stores a population it sends towards a solid
-    neighbour at the slot the next step reads it from ((p, x + c_p) after an
-    even step, (opp p, x) after an odd one); wall links by gather/scatter."""
+    """scheme "links": every cell streams as if the box were periodic (solids
+    carry NaN) and every link is fixed by a gather then a scatter pass.
+    scheme "inkernel": the even step is plain AA for every cell; in the odd
+    step a fluid cell reads an inflow from across a wall or solid at its own
+    slot (q, x), stores the populations aimed at a wall or solid at (opp p, x),
+    and skips usual stores that would wrap across a wall; solid cells skip
+    those and the slots fluid neighbours claim."""
 
     def __init__(self, p, lab, rho, u, T, scheme="links"):
         self.scheme = scheme
@@ -111,25 +113,30 @@ class AAModel:
         self.t = 0
         self.n = n
         self.fluid = np.ones(n, bool) if lab is None else (lab == 0)
-        # blocked-by-solid masks per direction (wall crossings excluded)
-        def solid_block(cset, links):
-            m = np.zeros((len(cset), n), bool)
-            for (x, q, xw, grp) in links:
-                if grp >= 6:
-                    m[q, x] = True
-            return m
-        self.sb19 = solid_block(C19, self.fl)
-        self.sb7 = solid_block(C7, self.gl) if self.th else None
 
-        # solid cell s, direction q: (s + c_q, opp q) is a solid link
-        def claims(cset, opp, links):
-            m = np.zeros((len(cset), n), bool)
-            for (x, q, xw, grp) in links:
-                if grp >= 6:
-                    m[opp[q], xw] = True
-            return m
-        self.claim19 = claims(C19, OPP19, self.fl)
-        self.claim7 = claims(C7, OPP7, self.gl) if self.th else None
+        # per direction and cell: the group of a fluid cell's blocked link (-1
+        # if none); whether the step leaves through a wall face (any cell); on a
+        # solid cell, whether a fluid neighbour's solid link claims the slot
+        def tables(cset, opp, links):
+            grp = np.full((len(cset), n), -1)
+            claim = np.zeros((len(cset), n), bool)
+            for (x, q, xw, g) in links:
+                grp[q, x] = g
+                if g >= 6:
+                    claim[opp[q], xw] = True
+            cross = np.zeros((len(cset), n), bool)
+            nx, ny, nz = self.shape
+            z, y, x = np.meshgrid(np.arange(nz), np.arange(ny), np.arange(nx), indexing="ij")
+            xyz = (x.reshape(-1), y.reshape(-1), z.reshape(-1))
+            for q, c in enumerate(cset):
+                for a in range(3):
+                    if p["face_kind"][2 * a]:
+                        t = xyz[a] + c[a]
+                        cross[q] |= (t < 0) | (t >= self.shape[a])
+            return grp, claim, cross
+        self.grp19, self.claim19, self.cross19 = tables(C19, OPP19, self.fl)
+        if self.th:
+            self.grp7, self.claim7, self.cross7 = tables(C7, OPP7, self.gl)
 
     def _read(self, S, opp, dn, odd):
         Q = S.shape[0]
@@ -137,7 +144,7 @@ class AAModel:
             return S.copy()
         return np.stack([S[opp[q], dn[q]] for q in range(Q)])
 
-    def _write(self, S, vals, opp, up, odd, sb=None, is_g=False):
+    def _write(self, S, vals, opp, up, odd, is_g=False):
         Q = S.shape[0]
         cells = np.arange(self.n)
         if self.scheme == "links" or not odd:
@@ -148,82 +155,79 @@ class AAModel:
                 else:
                     S[q, up[q]] = vals[q]
             return
-        # odd step of the in-kernel scheme: fluid cells store every population
-        # at its usual slot, then bounce the ones aimed at a solid neighbour
-        # into (opp p, x); solid cells store everything but their claimed
-        # slots -- applied last, so a wrong claim would overwrite a bounced
-        # value and break the equality
+        # odd step of the in-kernel scheme: fluid cells bounce the blocked
+        # populations into (opp p, x) and store every population at its usual
+        # slot except across a wall; solid cells store everything but slots
+        # across a wall and slots a fluid neighbour claims
+        grp, claim, cross = (self.grp7, self.claim7, self.cross7) if is_g else (self.grp19, self.claim19, self.cross19)
         fl = self.fluid
+        # bounce-back stores first: any usual store that lands on the same slot
+        # (which the kernel must never do) then corrupts it
         for q in range(Q):
-            S[q, up[q][fl]] = vals[q][fl]
-        for q in range(Q):
-            blk = fl & sb[q]
+            blk = fl & (grp[q] >= 0)
             vb = vals[q][blk]
             if is_g:
-                vb = self._solid_rule(vb)
+                vb = self._rule(grp[q][blk], vb)
             S[opp[q], cells[blk]] = vb
-        claimed = self.claim19 if not is_g else self.claim7
         for q in range(Q):
-            sol = ~fl & ~claimed[q]
+            keep = fl & ~cross[q]
+            S[q, up[q][keep]] = vals[q][keep]
+        for q in range(Q):
+            sol = ~fl & ~claim[q] & ~cross[q]
             S[q, up[q][sol]] = vals[q][sol]
 
-    def _solid_rule(self, v):
-        if self.p["solid_thermal"]:
-            return -v + (6 + self.p["a_T"]) / 21 * self.p["solid_T"]
-        return v
+    def _rule(self, groups, v):
+        """D3Q7 value after bouncing off the given groups (vectorised)."""
+        out = v.copy()
+        for i, grp in enumerate(groups):
+            dirichlet = self.p["face_thermal"][grp] if grp < 6 else self.p["solid_thermal"]
+            if dirichlet:
+                tw = self.p["face_T"][grp] if grp < 6 else self.p["solid_T"]
+                out[i] = -v[i] + (6 + self.p["a_T"]) / 21 * tw
+        return out
 
-    def _reread(self, S, vals, opp, sb, is_g):
-        """odd step: an inflow q whose upstream cell is solid is the bounce of
-        the cell's own even-step output, which sits in (q, x)."""
+    def _reread(self, S, vals, opp, is_g):
+        """odd step: an inflow q whose upstream cell is across a wall or solid
+        is the bounce of the cell's own even-step output, kept in (q, x)."""
+        grp = self.grp7 if is_g else self.grp19
         cells = np.arange(self.n)
         for q in range(S.shape[0]):
-            blk = self.fluid & sb[opp[q]]
+            g = grp[opp[q]]
+            blk = self.fluid & (g >= 0)
             v = S[q, cells[blk]]
-            vals[q][blk] = self._solid_rule(v) if is_g else v
+            vals[q][blk] = self._rule(g[blk], v) if is_g else v
 
     def step(self):
         odd = self.t & 1
         f = self._read(self.A, OPP19, self.dn19, odd)
         g = self._read(self.B, OPP7, self.dn7, odd) if self.th else None
         if self.scheme == "inkernel" and odd:
-            self._reread(self.A, f, OPP19, self.sb19, False)
+            self._reread(self.A, f, OPP19, False)
             if self.th:
-                self._reread(self.B, g, OPP7, self.sb7, True)
+                self._reread(self.B, g, OPP7, True)
         fp, gp, _ = oracle.collide(self.p, f.T.copy(), g.T.copy() if self.th else None)
-        self._write(self.A, fp.T, OPP19, self.up19, odd, self.sb19)
+        self._write(self.A, fp.T, OPP19, self.up19, odd)
         if self.th:
-            self._write(self.B, gp.T, OPP7, self.up7, odd, self.sb7, is_g=True)
-        # wall links: gather every source first, then scatter; solid links: one
-        # direct pass, each link read and written immediately
-        for S, links, opp, is_g in ((self.A, self.fl, OPP19, False), (self.B, self.gl, OPP7, True)):
-            if not links:
-                continue
-            wall = [lk for lk in links if lk[3] < 6]
-            solid = [lk for lk in links if lk[3] >= 6] if self.scheme == "links" else []
-            vals = [S[link_src(lk, opp, odd)] for lk in wall]
-            for lk, v in zip(wall, vals):
-                S[link_dst(lk, opp, odd)] = self._rule(lk, v, is_g)
-            for lk in solid:
-                S[link_dst(lk, opp, odd)] = self._rule(lk, S[link_src(lk, opp, odd)], is_g)
+            self._write(self.B, gp.T, OPP7, self.up7, odd, is_g=True)
+        # links scheme: every link by gather then scatter (the in-kernel
+        # scheme bounced everything inside the step already)
+        if self.scheme == "links":
+            for S, links, opp, is_g in ((self.A, self.fl, OPP19, False), (self.B, self.gl, OPP7, True)):
+                if not links:
+                    continue
+                vals = [S[link_src(lk, opp, odd)] for lk in links]
+                for lk, v in zip(links, vals):
+                    S[link_dst(lk, opp, odd)] = self._rule(np.array([lk[3]]), np.array([v]))[0] if is_g else v
         self.t += 1
-
-    def _rule(self, lk, v, is_g):
-        grp = lk[3]
-        if is_g:
-            dirichlet = self.p["face_thermal"][grp] if grp < 6 else self.p["solid_thermal"]
-            if dirichlet:
-                tw = self.p["face_T"][grp] if grp < 6 else self.p["solid_T"]
-                return -v + (6 + self.p["a_T"]) / 21 * tw
-        return v
 
     def populations(self):
         odd = self.t & 1
         f = self._read(self.A, OPP19, self.dn19, odd)
         g = self._read(self.B, OPP7, self.dn7, odd) if self.th else None
         if self.scheme == "inkernel" and odd:
-            self._reread(self.A, f, OPP19, self.sb19, False)
+            self._reread(self.A, f, OPP19, False)
             if self.th:
-                self._reread(self.B, g, OPP7, self.sb7, True)
+                self._reread(self.B, g, OPP7, True)
         return f, g
 
 

@@ -194,3 +194,33 @@ def test_invalid_step_count():
         assert s.time == 0
     finally:
         s.close()
+
+
+@pytest.mark.parametrize("dtype", [4, 8])
+def test_link_passes_parity(dtype):
+    """The pages' design: the step kernel streams as if periodic and a gather
+    pass then a scatter pass fix every wall and solid link."""
+    say(f"CASE link passes (gather/scatter) dtype={dtype}")
+    w = dirichlet_spheres_case()
+    w.params["links"] = binding.LBM_LINKS_PASSES
+    g = gpu_run(w, [51], dtype=dtype)
+    o = oracle_run(w, 51, want_diag=True)
+    check_fields(g, o, w, dtype, "passes")
+    check_forces(g["forces"][-1], o["diag"][-1], dtype, g["links19"] + g["links7"], "passes")
+
+
+@pytest.mark.parametrize("streaming", [binding.LBM_STREAM_AA, binding.LBM_STREAM_AB])
+@pytest.mark.parametrize("dtype", [4, 8])
+def test_in_kernel_equals_link_passes_bitwise(dtype, streaming):
+    say(f"CASE in-kernel vs link passes dtype={dtype} streaming={streaming}")
+    for name, w in (("spheres", dirichlet_spheres_case()), ("cavity", inputs.cavity256(shape=(22, 19, 17)))):
+        for steps in (1, 2, 7, 12):
+            w.params["links"] = binding.LBM_LINKS_IN_KERNEL
+            a = gpu_run(w, [steps], dtype=dtype, streaming=streaming)
+            w.params["links"] = binding.LBM_LINKS_PASSES
+            b = gpu_run(w, [steps], dtype=dtype, streaming=streaming)
+            fl = fluid_mask(w)
+            for k in ("rho", "u", "T"):
+                x, y = a[k][..., fl], b[k][..., fl]
+                assert np.array_equal(x, y), f"{name}: {k} differs after {steps} steps: {np.abs(x - y).max():.3e}"
+            assert np.allclose(a["forces"][-1], b["forces"][-1], rtol=1e-6, atol=1e-9)
