@@ -40,6 +40,17 @@ struct lbm_ctx {
     int64_t t = 0;
     bool initialised = false;
     bool in_kernel = false;  // bounce-back inside the step kernel
+    // replay of one even+odd pair of steps as a HIP graph (captured once on a
+    // private stream, launched on the caller's)
+    hipStream_t capture_stream = nullptr;
+    hipGraphExec_t pair = nullptr;
+    int pair_steps = 0;  // steps per replay (an even number)
+    bool pair_failed = false;
+    ~lbm_ctx()
+    {
+        if (pair) (void)hipGraphExecDestroy(pair);
+        if (capture_stream) (void)hipStreamDestroy(capture_stream);
+    }
     std::string err;
     Collision<float> colf{};
     Collision<double> cold{};
@@ -430,62 +441,123 @@ const Collision<float>& collision<float>(const lbm_ctx* c) { return c->colf; }
 template <>
 const Collision<double>& collision<double>(const lbm_ctx* c) { return c->cold; }
 
+// Enqueue one time step (parity from c->t) on `stream` and advance c->t;
+// `last` adds the force/heat pass of a submission's last step.
 template <typename R>
-lbm_status step_impl(lbm_ctx* c, int64_t n)
+lbm_status enqueue_step(lbm_ctx* c, hipStream_t stream, bool last)
 {
     const int64_t n_links = c->n_f + c->n_g;
     const bool passes = !c->in_kernel && n_links > 0;
-    for (int64_t k = 0; k < n; ++k) {
-        const bool last = (k == n - 1);
-        const int parity = (int)(c->t & 1);
-        StepArgs<R> s{};
-        s.geo = c->geo;
-        s.col = collision<R>(c);
-        s.mask = c->mask;
-        s.bb = make_bounce<R>(&c->p, c->in_kernel);
-        LinkArgs<R> la;
-        if (!c->ab) {
-            // one in-place kernel: collision, streaming (and bounce-back)
-            s.f = (R*)c->f;
-            s.g = (R*)c->g;
-            s.parity = parity;
-            LBM_HIP(c, launch_aa_step<R>(s, c->thermal, c->stream), "AA step kernel");
-            la = link_args<R>(c, parity == 0 ? LINK_AA_AFTER_EVEN : LINK_AA_AFTER_ODD, c->f, c->f, c->g, c->g);
-            if (passes) {
-                // link passes: gather every source, then scatter
-                la.begin = 0;
-                la.end = n_links;
-                LBM_HIP(c, launch_link_gather<R>(la, c->stream), "link gather kernel");
-                LBM_HIP(c, launch_link_scatter<R>(la, c->stream), "link scatter kernel");
-            }
-        } else {
-            char* fa = parity ? c->f2 : c->f;
-            char* fb = parity ? c->f : c->f2;
-            char* ga = parity ? c->g2 : c->g;
-            char* gb = parity ? c->g : c->g2;
-            s.f = (R*)fa;
-            s.g = (R*)ga;
-            s.f2 = (R*)fb;
-            s.g2 = (R*)gb;
-            LBM_HIP(c, launch_ab_collide<R>(s, c->thermal, c->stream), "A-B collide kernel");
-            LBM_HIP(c, launch_ab_pull<R>(s, c->thermal, c->stream), "A-B pull kernel");
-            la = link_args<R>(c, LINK_AB, fa, fb, ga, gb);
-            if (passes) {
-                // sources in one buffer, destinations in the other: one pass
-                la.begin = 0;
-                la.end = n_links;
-                LBM_HIP(c, launch_link_direct<R>(la, c->stream), "link kernel");
-            }
-        }
-        if (last) {
-            // forces and heat of the submission's last step, read where each
-            // link's bounced population was left
-            LBM_HIP(c, launch_zero_f64(c->accum, 4 * LBM_MAX_GROUPS, c->stream), "zero accumulators");
+    const int parity = (int)(c->t & 1);
+    StepArgs<R> s{};
+    s.geo = c->geo;
+    s.col = collision<R>(c);
+    s.mask = c->mask;
+    s.bb = make_bounce<R>(&c->p, c->in_kernel);
+    LinkArgs<R> la;
+    if (!c->ab) {
+        // one in-place kernel: collision, streaming (and bounce-back)
+        s.f = (R*)c->f;
+        s.g = (R*)c->g;
+        s.parity = parity;
+        LBM_HIP(c, launch_aa_step<R>(s, c->thermal, stream), "AA step kernel");
+        la = link_args<R>(c, parity == 0 ? LINK_AA_AFTER_EVEN : LINK_AA_AFTER_ODD, c->f, c->f, c->g, c->g);
+        if (passes) {
+            // link passes: gather every source, then scatter
             la.begin = 0;
             la.end = n_links;
-            LBM_HIP(c, launch_link_force<R>(la, c->stream), "force kernel");
+            LBM_HIP(c, launch_link_gather<R>(la, stream), "link gather kernel");
+            LBM_HIP(c, launch_link_scatter<R>(la, stream), "link scatter kernel");
         }
-        c->t += 1;
+    } else {
+        char* fa = parity ? c->f2 : c->f;
+        char* fb = parity ? c->f : c->f2;
+        char* ga = parity ? c->g2 : c->g;
+        char* gb = parity ? c->g : c->g2;
+        s.f = (R*)fa;
+        s.g = (R*)ga;
+        s.f2 = (R*)fb;
+        s.g2 = (R*)gb;
+        LBM_HIP(c, launch_ab_collide<R>(s, c->thermal, stream), "A-B collide kernel");
+        LBM_HIP(c, launch_ab_pull<R>(s, c->thermal, stream), "A-B pull kernel");
+        la = link_args<R>(c, LINK_AB, fa, fb, ga, gb);
+        if (passes) {
+            // sources in one buffer, destinations in the other: one pass
+            la.begin = 0;
+            la.end = n_links;
+            LBM_HIP(c, launch_link_direct<R>(la, stream), "link kernel");
+        }
+    }
+    if (last) {
+        // forces and heat of the submission's last step, read where each
+        // link's bounced population was left
+        LBM_HIP(c, launch_zero_f64(c->accum, 4 * LBM_MAX_GROUPS, stream), "zero accumulators");
+        la.begin = 0;
+        la.end = n_links;
+        LBM_HIP(c, launch_link_force<R>(la, stream), "force kernel");
+    }
+    c->t += 1;
+    return LBM_OK;
+}
+
+// Capture even/odd step pairs (kernel arguments and all) as one graph, once
+// per context: 8 pairs for boxes up to 2^21 cells, where launch overhead is
+// comparable to a step, else 1.  Any failure leaves the context on per-step
+// launches.
+template <typename R>
+void capture_pair(lbm_ctx* c)
+{
+    if (c->pair || c->pair_failed) return;
+    c->pair_failed = true;
+    if (hipStreamCreateWithFlags(&c->capture_stream, hipStreamNonBlocking) != hipSuccess) {
+        c->capture_stream = nullptr;
+        return;
+    }
+    const int64_t t_saved = c->t;
+    const std::string err_saved = c->err;
+    c->t = 0;
+    hipGraph_t graph = nullptr;
+    const int steps = c->geo.ncell <= (1 << 21) ? 16 : 2;
+    bool ok = hipStreamBeginCapture(c->capture_stream, hipStreamCaptureModeThreadLocal) == hipSuccess;
+    if (ok) {
+        bool launched = true;
+        for (int i = 0; i < steps && launched; ++i) launched = enqueue_step<R>(c, c->capture_stream, false) == LBM_OK;
+        ok = hipStreamEndCapture(c->capture_stream, &graph) == hipSuccess && launched && graph;
+    }
+    c->t = t_saved;
+    c->err = err_saved;
+    hipGraphExec_t exec = nullptr;
+    if (ok && hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) == hipSuccess) {
+        c->pair = exec;
+        c->pair_steps = steps;
+        c->pair_failed = false;
+    }
+    if (graph) (void)hipGraphDestroy(graph);
+    (void)hipGetLastError();  // a failed capture leaves no sticky error for the caller
+}
+
+// n steps: an odd first step alone, then replays of the step-pair graph,
+// then the remaining steps (the very last with the force pass) launched
+// directly.  Short submissions launch every step directly.
+template <typename R>
+lbm_status step_impl(lbm_ctx* c, int64_t n)
+{
+    int64_t left = n;
+    if (left >= 6) capture_pair<R>(c);
+    if (c->pair && left > c->pair_steps + 1) {
+        if (c->t & 1) {
+            if (lbm_status st = enqueue_step<R>(c, c->stream, false)) return st;
+            --left;
+        }
+        while (left > c->pair_steps) {
+            LBM_HIP(c, hipGraphLaunch(c->pair, c->stream), "graph launch");
+            c->t += c->pair_steps;
+            left -= c->pair_steps;
+        }
+    }
+    while (left > 0) {
+        if (lbm_status st = enqueue_step<R>(c, c->stream, left == 1)) return st;
+        --left;
     }
     return LBM_OK;
 }
