@@ -3,8 +3,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A "step" is one pass of the whole fused step (the in-place AA kernel for
-D3Q19 (+D3Q7), plus the link gather/scatter kernels when the box has walls or
-solids) over the resident population buffer.  W untimed steps, then exactly
+D3Q19 (+D3Q7), bounce-back at walls and solids included; the wall-force pass
+on the last step of the submission) over the resident population buffer.  W untimed steps, then exactly
 K timed steps in one submission, bracketed by stream synchronisation; HIP
 events on the library's stream (torch's current stream) time the region.
 
@@ -72,16 +72,16 @@ def load_traffic(workload: str, dtype: int, streaming: int):
 
 
 def device_ceilings(nbytes: int = 19 * (1 << 24) * 4, reps: int = 10):
-    """Bandwidth of torch's own device copy (read A, write B) and in-place
-    multiply (read and write A) on buffers the size of the 256^3 D3Q19 fp32
-    population array: the practical ceilings of a copy-like and of an
-    in-place access pattern on this GPU."""
+    """Bandwidth of torch's vectorized elementwise kernel out of place (read
+    A, write B) and in place (read and write A) on buffers the size of the
+    256^3 D3Q19 fp32 population array: the practical ceilings of a copy-like
+    and of an in-place access pattern on this GPU."""
     import torch
 
     a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
     out = {}
-    for name, fn in (("copy", lambda: b.copy_(a)), ("inplace_rmw", lambda: a.mul_(1.0))):
+    for name, fn in (("copy", lambda: torch.mul(a, 1.0, out=b)), ("inplace_rmw", lambda: a.mul_(1.0))):
         for _ in range(3):
             fn()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

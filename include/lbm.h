@@ -91,7 +91,7 @@ enum { LBM_LINKS_IN_KERNEL = 0, LBM_LINKS_PASSES = 1 };
 /* Faces are numbered 0..5 = x-, x+, y-, y+, z-, z+.  Force/heat group g is
  * face g for g < 6 and solid label g - 5 for g >= 6. */
 typedef struct lbm_params {
-    int32_t nx, ny, nz;      /* cells per axis, each >= 1; nx*ny*nz*dtype < 2^32 - 2^20 */
+    int32_t nx, ny, nz;      /* cells per axis, each >= 1; (nx*ny*nz + 1088) * dtype < 2^32 - 2^20 */
     int32_t dtype;           /* 4: fp32 populations and arithmetic, 8: fp64 */
     int32_t streaming;       /* LBM_STREAM_*; AUTO = in place (AA) */
     int32_t thermal;         /* 0: D3Q19 only, 1: D3Q19 + D3Q7 */

@@ -93,6 +93,15 @@ bool magic_ok(const DivMagic& m, uint32_t limit)
 
 bool finite(double v) { return std::isfinite(v); }
 
+// Elements between consecutive population planes: the cell count rounded up
+// to a wavefront, plus 1024.  With a power-of-two cell count the planes would
+// otherwise start at addresses that agree in every low bit, and the 19 (26)
+// accesses of one cell would meet in the same HBM channels and banks.  The
+// shift was chosen by measurement on MI355X: in fp32, 1-2 % faster steps at
+// 256^3 and 4-8 % at 512^3; in fp64 no change (a 512-element shift is 10-20 %
+// slower in either precision, so the value is not arbitrary).
+int64_t plane_stride(int64_t n) { return (n + 63) / 64 * 64 + 1024; }
+
 // Returns an empty string when the parameters are acceptable.
 std::string validate(const lbm_params* p)
 {
@@ -102,7 +111,7 @@ std::string validate(const lbm_params* p)
     if (n >= MAX_CELLS) return "nx*ny*nz too large for 32-bit cell indices";
     if (p->dtype != 4 && p->dtype != 8) return "dtype must be 4 or 8";
     // kernels address a population plane with 32-bit byte offsets
-    if ((n + 63) / 64 * 64 * (int64_t)p->dtype >= (int64_t(1) << 32) - (int64_t(1) << 20))
+    if (plane_stride(n) * (int64_t)p->dtype >= (int64_t(1) << 32) - (int64_t(1) << 20))
         return "nx*ny*nz*dtype too large for 32-bit plane offsets";
     if (p->streaming < 0 || p->streaming > 2) return "streaming must be 0, 1 or 2";
     if (p->thermal != 0 && p->thermal != 1) return "thermal must be 0 or 1";
@@ -377,7 +386,7 @@ Layout make_layout(const lbm_params* p, bool solids, int64_t n_links)
 {
     Layout L{};
     const int64_t n = (int64_t)p->nx * p->ny * p->nz;
-    L.stride = (n + 63) / 64 * 64;
+    L.stride = plane_stride(n);
     const size_t es = (size_t)p->dtype;
     const size_t fb = align_up(19 * (size_t)L.stride * es);
     const size_t gb = p->thermal ? align_up(7 * (size_t)L.stride * es) : 0;

@@ -12,8 +12,9 @@
 // (q, x) and write the collided value at (opposite(q), x); odd steps read at
 // (opposite(q), x - c_q) and write at (q, x + c_q).  Each cell writes exactly
 // the slots it read, so one buffer suffices and cells never race.  Solid cells
-// are processed like fluid ones (they hold NaN); every slot they write is
-// overwritten by a link scatter before any fluid cell reads it.
+// are processed like fluid ones (they hold NaN); no fluid cell ever reads a
+// value a solid cell wrote: the bounce-back in the odd step (or, in link-pass
+// mode, a link scatter) supplies every population that would come from one.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
