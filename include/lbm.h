@@ -5,7 +5,7 @@
  * Every call takes plain pointers and sizes; no C++ or framework types cross
  * this boundary.  All compute runs in the library's kernels on the caller's
  * HIP stream; calls are stream-ordered and asynchronous except
- * lbm_wall_force(), which synchronises the stream.
+ * lbm_wall_force() and lbm_diagnostics(), which synchronise the stream.
  *
  * What the library computes (the pages it follows):
  *  - "Multi-GPU thermal lattice Boltzmann simulations using OpenACC and MPI",
@@ -140,9 +140,11 @@ lbm_status lbm_create(const lbm_params* p, const uint8_t* solid_labels, void* de
 lbm_status lbm_init_fields(lbm_ctx* ctx, const void* rho, const void* u, const void* T);
 
 /* Enqueue n fused time steps (a "submission"): per step one in-place kernel
- * (collision + streaming of D3Q19 and, if thermal, D3Q7), then, when the box
- * has wall or solid links, the link gather and scatter kernels.  The forces
- * and heat of the submission's last step are latched for lbm_wall_force().
+ * (collision + streaming of D3Q19 and, if thermal, D3Q7, with the half-way
+ * bounce-back of wall and solid links inside it; with links =
+ * LBM_LINKS_PASSES, link gather and scatter kernels after it instead).  The
+ * forces and heat of the submission's last step are latched for
+ * lbm_wall_force().
  * n = 0 is a no-op; n < 0 is LBM_E_INVALID.  Asynchronous. */
 lbm_status lbm_step(lbm_ctx* ctx, int64_t n);
 
@@ -159,6 +161,40 @@ lbm_status lbm_read_macros(lbm_ctx* ctx, void* rho, void* u, void* T);
  * LBM_MAX_GROUPS are zero-filled.  Synchronises the stream; returns
  * LBM_E_UNSTABLE if a read-back saw a non-finite fluid value. */
 lbm_status lbm_wall_force(lbm_ctx* ctx, double* out, int32_t n_groups);
+
+/* Indices of the values lbm_diagnostics() returns. */
+enum {
+    LBM_DIAG_FLUID_CELLS = 0, /* number of fluid cells */
+    LBM_DIAG_MASS = 1,        /* sum of rho */
+    LBM_DIAG_MOM_X = 2,       /* sum of rho u_x (u with the half force, as read back) */
+    LBM_DIAG_MOM_Y = 3,
+    LBM_DIAG_MOM_Z = 4,
+    LBM_DIAG_KINETIC = 5,     /* sum of rho |u|^2 / 2 */
+    LBM_DIAG_UMAX = 6,        /* max |u| */
+    LBM_DIAG_HEAT = 7,        /* sum of T (0 unless thermal) */
+    LBM_DIAG_CONV_X = 8,      /* sum of u_x T: advective heat flux (0 unless thermal) */
+    LBM_DIAG_CONV_Y = 9,
+    LBM_DIAG_CONV_Z = 10,
+    LBM_DIAG_COUNT = 11
+};
+
+/* Volume diagnostics at the current time: sums over the fluid cells of the
+ * fields lbm_read_macros() returns, accumulated in fp64 on the device, written
+ * to out (host, n doubles; values past LBM_DIAG_COUNT are zero-filled).  They
+ * give the heat-transfer figures of a convection cell heated through the two
+ * faces of axis a, H cells apart (walls half-way, so H = the box extent),
+ * with temperature difference dT and thermal diffusivity alpha:
+ *   wall Nusselt number   Nu_w = Q * H / (alpha * dT * A), with Q the heat
+ *                          through one heated face per step (lbm_wall_force)
+ *                          and A its area in cells;
+ *   volume Nusselt number Nu_v = 1 + <u_a T> * H / (alpha * dT), with
+ *                          <u_a T> = out[LBM_DIAG_CONV_a] / fluid cells
+ *                          (a box without solid cells).
+ * At a steady state the hot and cold faces pass the same heat (Q_hot = -Q_cold),
+ * and Nu_v agrees with Nu_w up to the discretisation.
+ * Synchronises the stream; returns LBM_E_UNSTABLE if a fluid value was not
+ * finite (then the sums are not finite either). */
+lbm_status lbm_diagnostics(lbm_ctx* ctx, double* out, int32_t n);
 
 /* Current time step count (number of steps since lbm_init_fields). */
 int64_t lbm_time(const lbm_ctx* ctx);

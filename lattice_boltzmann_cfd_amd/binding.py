@@ -23,11 +23,13 @@ STATUS_NAMES = {0: "LBM_OK", 1: "LBM_E_INVALID", 2: "LBM_E_NOMEM", 3: "LBM_E_DEV
 LBM_STREAM_AUTO, LBM_STREAM_AA, LBM_STREAM_AB = 0, 1, 2
 LBM_LINKS_IN_KERNEL, LBM_LINKS_PASSES = 0, 1
 MAX_GROUPS = 261
+(LBM_DIAG_FLUID_CELLS, LBM_DIAG_MASS, LBM_DIAG_MOM_X, LBM_DIAG_MOM_Y, LBM_DIAG_MOM_Z, LBM_DIAG_KINETIC,
+ LBM_DIAG_UMAX, LBM_DIAG_HEAT, LBM_DIAG_CONV_X, LBM_DIAG_CONV_Y, LBM_DIAG_CONV_Z, LBM_DIAG_COUNT) = range(12)
 
 # every function the header declares
 ABI_FUNCTIONS = (
     "lbm_required_bytes", "lbm_create", "lbm_init_fields", "lbm_step", "lbm_read_macros",
-    "lbm_wall_force", "lbm_time", "lbm_num_links", "lbm_count_links", "lbm_last_error", "lbm_destroy",
+    "lbm_wall_force", "lbm_diagnostics", "lbm_time", "lbm_num_links", "lbm_count_links", "lbm_last_error", "lbm_destroy",
 )
 
 
@@ -78,6 +80,8 @@ def library():
         lib.lbm_read_macros.restype = ctypes.c_int
         lib.lbm_wall_force.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.c_int32]
         lib.lbm_wall_force.restype = ctypes.c_int
+        lib.lbm_diagnostics.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.c_int32]
+        lib.lbm_diagnostics.restype = ctypes.c_int
         lib.lbm_time.argtypes = [vp]
         lib.lbm_time.restype = ctypes.c_int64
         lib.lbm_num_links.argtypes = [vp, ctypes.c_int32]
@@ -171,6 +175,13 @@ def lbm_wall_force(ctx, n_groups: int = MAX_GROUPS) -> np.ndarray:
     return out
 
 
+def lbm_diagnostics(ctx, n: int = LBM_DIAG_COUNT) -> np.ndarray:
+    out = np.zeros(n, np.float64)
+    st = library().lbm_diagnostics(ctypes.c_void_p(ctx), out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), int(n))
+    _check(ctx, st)
+    return out
+
+
 def lbm_time(ctx) -> int:
     return int(library().lbm_time(ctypes.c_void_p(ctx)))
 
@@ -252,6 +263,9 @@ class Solver:
 
     def wall_force(self, n_groups: int = MAX_GROUPS) -> np.ndarray:
         return lbm_wall_force(self.ctx, n_groups)
+
+    def diagnostics(self) -> np.ndarray:
+        return lbm_diagnostics(self.ctx)
 
     @property
     def time(self) -> int:

@@ -35,6 +35,7 @@ struct lbm_ctx {
     char* scratch = nullptr;
     double* wall_T = nullptr;
     double* accum = nullptr;
+    double* diag = nullptr;
     int32_t* unstable = nullptr;
     int64_t n_f = 0, n_g = 0, n_wall = 0;
     int64_t t = 0;
@@ -378,7 +379,7 @@ std::vector<uint32_t> build_mask(const lbm_params* p, const uint8_t* labels)
 }
 
 struct Layout {
-    size_t f, g, f2, g2, mask, lcell, lcellw, lmeta, scratch, wall_T, accum, unstable, total;
+    size_t f, g, f2, g2, mask, lcell, lcellw, lmeta, scratch, wall_T, accum, diag, unstable, total;
     int64_t stride;
 };
 
@@ -403,6 +404,7 @@ Layout make_layout(const lbm_params* p, bool solids, int64_t n_links)
     L.scratch = off; off += align_up(es * (size_t)n_links);
     L.wall_T = off; off += align_up(8 * LBM_MAX_GROUPS);
     L.accum = off; off += align_up(8 * 4 * LBM_MAX_GROUPS);
+    L.diag = off; off += align_up(8 * LBM_DIAG_COUNT);
     L.unstable = off; off += ALIGN;
     L.total = off;
     return L;
@@ -675,6 +677,7 @@ lbm_status lbm_create(const lbm_params* p, const uint8_t* solid_labels, void* de
         c->scratch = base + L.scratch;
         c->wall_T = (double*)(base + L.wall_T);
         c->accum = (double*)(base + L.accum);
+        c->diag = (double*)(base + L.diag);
         c->unstable = (int32_t*)(base + L.unstable);
         c->colf = make_collision<float>(p);
         c->cold = make_collision<double>(p);
@@ -810,6 +813,36 @@ lbm_status lbm_wall_force(lbm_ctx* c, double* out, int32_t n_groups)
     LBM_HIP(c, hipStreamSynchronize(c->stream), "synchronise");
     for (int32_t i = 0; i < n_groups; ++i)
         for (int k = 0; k < 4; ++k) out[4 * i + k] = i < LBM_MAX_GROUPS ? acc[4 * i + k] : 0.0;
+    if (unstable) {
+        c->err = "a fluid cell's rho, u or T was not finite at a read-back";
+        return LBM_E_UNSTABLE;
+    }
+    return LBM_OK;
+}
+
+lbm_status lbm_diagnostics(lbm_ctx* c, double* out, int32_t n)
+{
+    if (!c) return LBM_E_INVALID;
+    if (n < 0 || (n > 0 && !out)) {
+        c->err = "bad output buffer";
+        return LBM_E_INVALID;
+    }
+    if (!c->initialised) {
+        c->err = "lbm_init_fields has not been called";
+        return LBM_E_INVALID;
+    }
+    LBM_HIP(c, launch_zero_f64(c->diag, LBM_DIAG_COUNT, c->stream), "clear diagnostics");
+    hipError_t e = c->es == 4 ? launch_diag<float>(field_args<float>(c), c->thermal, c->diag, c->stream)
+                              : launch_diag<double>(field_args<double>(c), c->thermal, c->diag, c->stream);
+    if (e != hipSuccess) return device_error(c, e, "diagnostics kernel");
+    double d[LBM_DIAG_COUNT];
+    int32_t unstable = 0;
+    LBM_HIP(c, hipMemcpyAsync(d, c->diag, sizeof d, hipMemcpyDeviceToHost, c->stream), "copy diagnostics");
+    LBM_HIP(c, hipMemcpyAsync(&unstable, c->unstable, sizeof(int32_t), hipMemcpyDeviceToHost, c->stream),
+            "copy flag");
+    LBM_HIP(c, hipStreamSynchronize(c->stream), "synchronise");
+    d[LBM_DIAG_UMAX] = std::sqrt(d[LBM_DIAG_UMAX]);  // the kernel reduces |u|^2
+    for (int32_t i = 0; i < n; ++i) out[i] = i < LBM_DIAG_COUNT ? d[i] : 0.0;
     if (unstable) {
         c->err = "a fluid cell's rho, u or T was not finite at a read-back";
         return LBM_E_UNSTABLE;

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "lbm.h"
 #include "lbm_lattice.hpp"
 
 namespace lbm {
@@ -141,6 +142,8 @@ template <typename R> hipError_t launch_link_direct(const LinkArgs<R>& a, hipStr
 template <typename R> hipError_t launch_link_force(const LinkArgs<R>& a, hipStream_t s);
 template <typename R> hipError_t launch_init(const FieldArgs<R>& a, bool thermal, hipStream_t s);
 template <typename R> hipError_t launch_read(const FieldArgs<R>& a, bool thermal, hipStream_t s);
+// Volume sums of lbm_diagnostics() into out[LBM_DIAG_COUNT] (cleared by the caller).
+template <typename R> hipError_t launch_diag(const FieldArgs<R>& a, bool thermal, double* out, hipStream_t s);
 hipError_t launch_zero_f64(double* p, int64_t n, hipStream_t s);
 
 }  // namespace lbm

@@ -512,16 +512,15 @@ __global__ void __launch_bounds__(BLOCK) k_init(FieldArgs<R> a)
     }
 }
 
+// Populations of `cell` at the current time: after an even number of steps
+// (or with two buffers) in the cell's own slots, after an odd number where
+// the last odd step stored them, (opposite(q), x - c_q), with in-kernel
+// bounce-back's re-read of blocked inflows.  Returns false for a solid cell.
 template <typename R, bool TH>
-__global__ void __launch_bounds__(BLOCK) k_read(FieldArgs<R> a)
+__device__ __forceinline__ bool load_cell(const FieldArgs<R>& a, int32_t cell, R* h, R* g)
 {
     const Geometry& G = a.geo;
-    const int32_t cell = (int32_t)(blockIdx.x * BLOCK + threadIdx.x);
-    if (cell >= G.ncell) return;
     const int64_t S = G.stride;
-    const int32_t n = G.ncell;
-    R h[Q19];
-    R g[Q7];
     if (a.ab || a.parity == 0) {
 #pragma unroll
         for (int q = 0; q < Q19; ++q) h[q] = a.f[q * S + cell];
@@ -554,15 +553,32 @@ __global__ void __launch_bounds__(BLOCK) k_read(FieldArgs<R> a)
             }
         }
     }
+    return !(a.mask && (a.mask[cell] & MASK_SOLID));
+}
+
+template <typename R>
+__device__ __forceinline__ bool finite_macros(const Macro<R>& m)
+{
+    return __builtin_isfinite(m.rho) && __builtin_isfinite(m.T) && __builtin_isfinite(m.ux) &&
+           __builtin_isfinite(m.uy) && __builtin_isfinite(m.uz);
+}
+
+template <typename R, bool TH>
+__global__ void __launch_bounds__(BLOCK) k_read(FieldArgs<R> a)
+{
+    const Geometry& G = a.geo;
+    const int32_t cell = (int32_t)(blockIdx.x * BLOCK + threadIdx.x);
+    if (cell >= G.ncell) return;
+    const int32_t n = G.ncell;
+    R h[Q19];
+    R g[Q7];
     Macro<R> m;
-    if (a.mask && (a.mask[cell] & MASK_SOLID)) {
+    if (!load_cell<R, TH>(a, cell, h, g)) {
         const R nan = (R)__builtin_nan("");
         m.rho = m.ux = m.uy = m.uz = m.T = nan;
     } else {
         m = macros<R, TH>(h, g, a.col);
-        const bool bad = !(__builtin_isfinite(m.rho) && __builtin_isfinite(m.T) && __builtin_isfinite(m.ux) &&
-                           __builtin_isfinite(m.uy) && __builtin_isfinite(m.uz));
-        if (bad) atomicOr(a.unstable, 1);
+        if (!finite_macros(m)) atomicOr(a.unstable, 1);
     }
     if (a.rho_out) a.rho_out[cell] = m.rho;
     if (a.u_out) {
@@ -571,6 +587,75 @@ __global__ void __launch_bounds__(BLOCK) k_read(FieldArgs<R> a)
         a.u_out[2 * n + cell] = m.uz;
     }
     if (TH && a.T_out) a.T_out[cell] = m.T;
+}
+
+// Sums over the fluid cells at the current time, in fp64: the cell count,
+// mass, momentum rho u, kinetic energy rho |u|^2 / 2, the largest |u|^2,
+// heat T and the advective heat flux u T (u with the half force, as in the
+// read-back).  Grid-stride over cells; wavefront shuffles, then LDS across
+// the block's wavefronts, then one global atomic per block and value (the
+// maximum through the ordering of non-negative doubles' bit patterns).
+template <typename R, bool TH>
+__global__ void __launch_bounds__(BLOCK) k_diag(FieldArgs<R> a, double* out)
+{
+    constexpr int NS = LBM_DIAG_COUNT;  // slot LBM_DIAG_UMAX holds max |u|^2
+    __shared__ double part[BLOCK / 64][NS];
+    double acc[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) acc[i] = 0.0;
+    const int32_t n = a.geo.ncell;
+    for (int32_t cell = (int32_t)(blockIdx.x * BLOCK + threadIdx.x); cell < n;
+         cell += (int32_t)(gridDim.x * BLOCK)) {
+        R h[Q19];
+        R g[Q7];
+        if (!load_cell<R, TH>(a, cell, h, g)) continue;
+        const Macro<R> m = macros<R, TH>(h, g, a.col);
+        if (!finite_macros(m)) atomicOr(a.unstable, 1);
+        const double rho = m.rho, ux = m.ux, uy = m.uy, uz = m.uz, T = TH ? (double)m.T : 0.0;
+        const double u2 = ux * ux + uy * uy + uz * uz;
+        acc[LBM_DIAG_FLUID_CELLS] += 1.0;
+        acc[LBM_DIAG_MASS] += rho;
+        acc[LBM_DIAG_MOM_X] += rho * ux;
+        acc[LBM_DIAG_MOM_Y] += rho * uy;
+        acc[LBM_DIAG_MOM_Z] += rho * uz;
+        acc[LBM_DIAG_KINETIC] += 0.5 * rho * u2;
+        acc[LBM_DIAG_UMAX] = (u2 > acc[LBM_DIAG_UMAX] || u2 != u2) ? u2 : acc[LBM_DIAG_UMAX];
+        acc[LBM_DIAG_HEAT] += T;
+        acc[LBM_DIAG_CONV_X] += ux * T;
+        acc[LBM_DIAG_CONV_Y] += uy * T;
+        acc[LBM_DIAG_CONV_Z] += uz * T;
+    }
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        double v = acc[i];
+        if (i == LBM_DIAG_UMAX) {
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) {
+                const double w = __shfl_xor(v, o, 64);
+                v = (w > v || w != w) ? w : v;
+            }
+        } else {
+            v = wave_sum(v);
+        }
+        if ((threadIdx.x & 63) == 0) part[wave][i] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < NS) {
+        const int i = threadIdx.x;
+        double v = part[0][i];
+        for (int w = 1; w < BLOCK / 64; ++w) {
+            const double x = part[w][i];
+            if (i == LBM_DIAG_UMAX) v = (x > v || x != x) ? x : v;
+            else v += x;
+        }
+        if (i == LBM_DIAG_UMAX) {
+            // a non-negative double (or NaN) orders like its bit pattern
+            atomicMax(reinterpret_cast<unsigned long long*>(out + i), (unsigned long long)__double_as_longlong(v));
+        } else if (v != 0.0) {
+            atomicAdd(out + i, v);
+        }
+    }
 }
 
 __global__ void __launch_bounds__(BLOCK) k_zero_f64(double* p, int64_t n)
@@ -664,6 +749,15 @@ hipError_t launch_read(const FieldArgs<R>& a, bool thermal, hipStream_t s)
     return hipGetLastError();
 }
 
+template <typename R>
+hipError_t launch_diag(const FieldArgs<R>& a, bool thermal, double* out, hipStream_t s)
+{
+    const unsigned blocks = (unsigned)std::min<int64_t>(((int64_t)a.geo.ncell + BLOCK - 1) / BLOCK, 2048);
+    if (thermal) hipLaunchKernelGGL((k_diag<R, true>), dim3(blocks), dim3(BLOCK), 0, s, a, out);
+    else hipLaunchKernelGGL((k_diag<R, false>), dim3(blocks), dim3(BLOCK), 0, s, a, out);
+    return hipGetLastError();
+}
+
 hipError_t launch_zero_f64(double* p, int64_t n, hipStream_t s)
 {
     if (n <= 0) return hipSuccess;
@@ -680,7 +774,8 @@ hipError_t launch_zero_f64(double* p, int64_t n, hipStream_t s)
     template hipError_t launch_link_direct<R>(const LinkArgs<R>&, hipStream_t);          \
     template hipError_t launch_link_force<R>(const LinkArgs<R>&, hipStream_t);           \
     template hipError_t launch_init<R>(const FieldArgs<R>&, bool, hipStream_t);          \
-    template hipError_t launch_read<R>(const FieldArgs<R>&, bool, hipStream_t);
+    template hipError_t launch_read<R>(const FieldArgs<R>&, bool, hipStream_t);          \
+    template hipError_t launch_diag<R>(const FieldArgs<R>&, bool, double*, hipStream_t);
 
 LBM_INSTANTIATE(float)
 LBM_INSTANTIATE(double)

@@ -15,9 +15,11 @@ def say(*args):
     sys.stdout.flush()
 
 
-def gpu_run(w: inputs.Workload, submissions, dtype=4, streaming=binding.LBM_STREAM_AUTO, want_forces=True):
+def gpu_run(w: inputs.Workload, submissions, dtype=4, streaming=binding.LBM_STREAM_AUTO, want_forces=True,
+            want_diag=False):
     """Run the submissions (a list of step counts) on the GPU; returns the
-    macros at the end (fp64 numpy) and the latched forces after each one."""
+    macros at the end (fp64 numpy), the latched forces after each one and,
+    if asked, the volume diagnostics at the end."""
     import torch
 
     thermal = bool(w.params.get("thermal"))
@@ -34,6 +36,8 @@ def gpu_run(w: inputs.Workload, submissions, dtype=4, streaming=binding.LBM_STRE
         out = dict(rho=rho.cpu().double().numpy(), u=u.cpu().double().numpy(),
                    T=T.cpu().double().numpy() if T is not None else None, forces=forces, time=s.time,
                    links19=s.num_links(19), links7=s.num_links(7))
+        if want_diag:
+            out["diag"] = s.diagnostics()
         s.wall_force()  # raises LBM_E_UNSTABLE if the read-back saw a non-finite value
         return out
     finally:
@@ -92,3 +96,17 @@ def max_diffs(g, o, mask):
 
 def fluid_mask(w):
     return np.ones(w.cells, bool) if w.labels is None else (w.labels == 0)
+
+
+def volume_sums(rho, u, T, fluid):
+    """The definition of lbm_diagnostics() written out over read-back fields
+    (fp64): values in LBM_DIAG_* order, and the sums of the terms' magnitudes
+    (the scale a rounding bound is taken against)."""
+    r = rho[fluid]
+    ux, uy, uz = u[0][fluid], u[1][fluid], u[2][fluid]
+    t = T[fluid] if T is not None else np.zeros_like(r)
+    u2 = ux * ux + uy * uy + uz * uz
+    terms = [np.ones_like(r), r, r * ux, r * uy, r * uz, 0.5 * r * u2, None, t, ux * t, uy * t, uz * t]
+    val = np.array([np.sqrt(u2.max()) if x is None else x.sum() for x in terms])
+    mag = np.array([np.sqrt(u2.max()) if x is None else np.abs(x).sum() for x in terms])
+    return val, mag

@@ -96,6 +96,17 @@ def test_too_small_buffer_is_nomem(lib):
     assert e.value.status == binding.LBM_E_NOMEM
 
 
+def test_null_context_calls_are_invalid(lib):
+    out = (binding.ctypes.c_double * 16)()
+    assert lib.lbm_init_fields(None, None, None, None) == binding.LBM_E_INVALID
+    assert lib.lbm_step(None, 1) == binding.LBM_E_INVALID
+    assert lib.lbm_read_macros(None, None, None, None) == binding.LBM_E_INVALID
+    assert lib.lbm_wall_force(None, out, 4) == binding.LBM_E_INVALID
+    assert lib.lbm_diagnostics(None, out, binding.LBM_DIAG_COUNT) == binding.LBM_E_INVALID
+    assert lib.lbm_time(None) == -1
+    assert lib.lbm_num_links(None, 19) == -1
+
+
 def test_box_too_large_rejected(lib):
     p = inputs.base_params(2048, 1024, 512, inputs.mrt_rates(0.6))
     assert binding.lbm_required_bytes(p) == 0

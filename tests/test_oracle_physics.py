@@ -11,7 +11,13 @@ fix, independently of the oracle's own code:
   * plane Poiseuille flow between half-way bounce-back plates matches the
     analytic parabola (wall exactly half-way, thermal-LBM page Sec. 2);
   * pure conduction between anti-bounce-back Dirichlet walls converges to the
-    exact linear profile (thermal-LBM page Sec. 2: w = (6 + a_T)/21);
+    exact linear profile (thermal-LBM page Sec. 2: w = (6 + a_T)/21), and the
+    heat through each wall is then exactly alpha dT A / H (wall Nusselt
+    number 1);
+  * a differentially heated cubical cavity (Ra = 1e4, Pr = 0.71) reaches a
+    steady state whose hot and cold walls pass the same heat, whose volume
+    and wall Nusselt numbers agree, and whose grid-extrapolated Nusselt
+    number matches the published benchmark value;
   * the heat budget: the change of total T equals the heat through the
     Dirichlet links; an all-adiabatic box keeps total T;
   * a 2D Taylor-Green vortex decays at the rate set by nu = (tau - 1/2)/3
@@ -141,10 +147,48 @@ def test_linear_conduction(a_T, alpha):
                            face_thermal=[inputs.DIRICHLET, inputs.DIRICHLET, 0, 0, 0, 0],
                            face_T=[0.5, -0.5, 0, 0, 0, 0], s7=inputs.thermal_rates(alpha, a_T=a_T), a_T=a_T)
     rho, u, T = inputs.rest(n, 2, 2)
-    o = oracle.run(p, 4000, rho, u, T)
+    o = oracle.run(p, 4000, rho, u, T, want_diag=True)
     x = np.arange(n * 4) % n
     exact = 0.5 - (x + 0.5) / n
     assert np.abs(o["T"] - exact).max() < 1e-12
+    # Fourier's law across the box: heat per step through each wall face
+    # (area 2 x 2 cells, H = n, dT = 1)
+    q_hot, q_cold = o["diag"][-1, 0, 3], o["diag"][-1, 1, 3]
+    assert abs(q_hot - alpha * 4 / n) < 1e-13
+    assert abs(q_cold + alpha * 4 / n) < 1e-13
+
+
+def cavity_nusselt(n, steps=4000):
+    """Wall (hot, cold) and volume Nusselt numbers of an n^3 differentially
+    heated cavity (x- hot, x+ cold, others adiabatic, no-slip everywhere) at
+    Ra = 1e4, Pr = 0.71, after `steps` steps from rest."""
+    w = inputs.cavity256(shape=(n, n, n), Ra=1e4, H=n)
+    alpha = w.info["scales"]["alpha"]
+    o = oracle.run(w.params, steps, w.rho, w.u, w.T, want_diag=True)
+    q = o["diag"][-1, :2, 3]
+    nu_wall = q * n / (alpha * n * n)
+    nu_vol = 1.0 + (o["u"][0] * o["T"]).mean() * n / alpha
+    return nu_wall, nu_vol
+
+
+@pytest.mark.slow
+def test_cavity_nusselt_ra1e4():
+    """Steady natural convection in a cube.  Exact at a steady state: the hot
+    wall takes in what the cold wall gives off.  Up to the discretisation:
+    the volume Nusselt number 1 + <u_x T> H / (alpha dT) equals the wall one.
+    Against the literature (benchmark solutions of this cavity at Ra = 1e4,
+    Pr = 0.71 put the mean Nusselt number at 2.05-2.06, e.g. Tric, Labrosse
+    and Betrouni 2000: 2.054; values quoted from memory, not from the
+    pages): the second-order Richardson extrapolation of 16^3 and 20^3 lies
+    within 1 %."""
+    (h16, c16), v16 = cavity_nusselt(16)
+    (h20, c20), v20 = cavity_nusselt(20)
+    for h, c, v in ((h16, c16, v16), (h20, c20, v20)):
+        assert abs(h + c) < 1e-4 * h
+        assert abs(v - h) < 1e-3 * h
+    assert 1.9 < h16 < h20 < 2.06  # converges from below
+    nu = (h20 * 400 - h16 * 256) / (400 - 256)
+    assert abs(nu - 2.054) < 0.01 * 2.054, nu
 
 
 def test_heat_budget_dirichlet_and_adiabatic():
