@@ -38,6 +38,9 @@ import numpy as np
 
 FACE_PERIODIC = 0
 FACE_WALL = 1
+FACE_SLIP = 2
+FACE_VELOCITY = 3
+FACE_PRESSURE = 4
 ADIABATIC = 0
 DIRICHLET = 1
 
@@ -98,7 +101,10 @@ def thermal_scales(H: float, Ra: float, Pr: float, U_f: float = U_FREEFALL) -> d
 
 def base_params(nx, ny, nz, s19, thermal=False, face_kind=None, face_thermal=None, face_T=None,
                 s7=None, a_T=A_T_DEFAULT, accel=(0.0, 0.0, 0.0), gbeta=(0.0, 0.0, 0.0), T0=0.0,
-                solid_thermal=ADIABATIC, solid_T=0.0) -> dict:
+                solid_thermal=ADIABATIC, solid_T=0.0, face_u=None, face_rho=None) -> dict:
+    """face_u: 6 wall velocities (3 components each) of VELOCITY faces;
+    face_rho: 6 wall densities of VELOCITY and PRESSURE faces."""
+    fu = [0.0] * 18 if face_u is None else [float(v) for v in np.asarray(face_u, dtype=float).reshape(-1)]
     return dict(
         nx=int(nx), ny=int(ny), nz=int(nz), thermal=int(bool(thermal)),
         face_kind=list(face_kind or [FACE_PERIODIC] * 6),
@@ -107,6 +113,7 @@ def base_params(nx, ny, nz, s19, thermal=False, face_kind=None, face_thermal=Non
         s19=list(s19), s7=list(s7 or [0.0] * 7), a_T=float(a_T),
         accel=list(accel), gbeta=list(gbeta), T0=float(T0),
         solid_thermal=int(solid_thermal), solid_T=float(solid_T),
+        face_u=fu, face_rho=list(face_rho or [1.0] * 6),
     )
 
 

@@ -58,8 +58,36 @@
  *      the first crossed axis in x, y, z order) or when the periodic image
  *      of x + c_p is a solid cell (group = 5 + its label).  Faces are
  *      numbered 0..5 = x-, x+, y-, y+, z-, z+.
- *  R9  Momentum exchange on a blocked f link: the wall receives 2 c_p f_p^+;
- *      heat into the fluid through a Dirichlet g link: w T_w - 2 g_p^+.
+ *  R9  Momentum exchange on a blocked f link: the boundary receives the
+ *      momentum the link carries out minus what it brings back,
+ *      c_p f_out - c_in f_in (2 c_p f_p^+ for a wall); heat into the fluid
+ *      through a Dirichlet g link: w T_w - 2 g_p^+.
+ *  R10 Face kinds ([AA] names wall, reflection and open-face rules as
+ *      per-link rules; the pages give no formulas, these are the textbook
+ *      half-way forms).  For a link (x, p) that leaves through face f:
+ *        WALL      f_pbar(x) = f_p^+(x)                  (no-slip, at rest)
+ *        SLIP      specular reflection: the normal part of c_p reverses,
+ *                  the tangential part c_t carries on, so the population
+ *                  arrives at x + c_t along q = p reflected:
+ *                  f_q(x + c_t) = f_p^+(x)               (free slip)
+ *        VELOCITY  bounce-back off a wall moving at u_w (Ladd):
+ *                  f_pbar(x) = f_p^+(x) - 6 w_p rho_w c_p.u_w
+ *                  (a velocity inlet when u_w crosses the face, a moving
+ *                  lid when it is tangential)
+ *        PRESSURE  anti-bounce-back at density rho_w with the cell's own
+ *                  velocity u(x) of that step:
+ *                  f_pbar(x) = -f_p^+(x)
+ *                              + 2 w_p rho_w [1 + 9/2 (c_p.u)^2 - 3/2 u.u]
+ *                  (an open outlet).
+ *      rho_w and u_w are per-face parameters.
+ *  R11 A link leaving through two faces takes the rule of the first crossed
+ *      axis in x, y, z order, with SLIP acting as WALL there (reflecting
+ *      both normal components is bounce-back).
+ *  R12 The D3Q7 lattice takes each non-periodic face's thermal rule
+ *      (Dirichlet anti-bounce-back or adiabatic bounce-back) whatever its
+ *      kind; an axis is periodic on both faces or on neither.
+ *  R13 No solid cell may lie in the first cell layer of a SLIP face (the
+ *      reflected population travels along that layer).
  *
  * Windows: the oracle can run on a window (a sub-box, possibly wrapping
  * through periodic faces) of the full box.  A population that would be
@@ -82,7 +110,7 @@
 typedef struct oracle_params {
     int32_t nx, ny, nz;
     int32_t thermal;          /* 0: flow only, 1: flow + D3Q7 temperature */
-    int32_t face_kind[6];     /* 0 periodic, 1 no-slip wall */
+    int32_t face_kind[6];     /* 0 periodic, 1 wall, 2 slip, 3 velocity, 4 pressure (R10) */
     int32_t face_thermal[6];  /* 0 adiabatic, 1 Dirichlet */
     double face_T[6];         /* Dirichlet wall temperature */
     int32_t solid_thermal;    /* 0 adiabatic, 1 Dirichlet (all solids) */
@@ -94,7 +122,11 @@ typedef struct oracle_params {
     double accel[3];
     double gbeta[3];
     double T0;
+    double face_u[18];        /* wall velocity u_w of each face (VELOCITY faces) */
+    double face_rho[6];       /* wall density rho_w of each face (VELOCITY, PRESSURE) */
 } oracle_params;
+
+enum { PERIODIC = 0, WALL = 1, SLIP = 2, VELOCITY = 3, PRESSURE = 4 };
 
 /* ------------------------------------------------------------------ tables */
 
@@ -411,6 +443,30 @@ static int blocked_group(const oracle_params* p, const uint8_t* labels, const in
     return -1;
 }
 
+/* R10-R11: group and rule of the link from global cell g along c when it
+ * leaves through a face (the solid case is blocked_group's), else -1.  *axis
+ * is the axis of the governing face. */
+static int face_rule(const oracle_params* p, const int* N, const int64_t* g, const int* c, int* rule,
+                     int* axis)
+{
+    int first = -1, crossed = 0;
+    for (int a = 0; a < 3; ++a) {
+        int64_t t = g[a] + c[a];
+        int f = -1;
+        if (t < 0 && p->face_kind[2 * a]) f = 2 * a;
+        if (t >= N[a] && p->face_kind[2 * a + 1]) f = 2 * a + 1;
+        if (f >= 0) {
+            if (first < 0) first = f;
+            ++crossed;
+        }
+    }
+    if (first < 0) return -1;
+    *rule = p->face_kind[first];
+    if (*rule == SLIP && crossed > 1) *rule = WALL;
+    *axis = first / 2;
+    return first;
+}
+
 static int is_solid(const uint8_t* labels, const int* N, const int64_t* g)
 {
     return labels && labels[g[0] + (int64_t)N[0] * (g[1] + (int64_t)N[1] * g[2])] != 0;
@@ -476,12 +532,28 @@ int oracle_run(const oracle_params* p, const uint8_t* labels, const int32_t* win
     for (int a = 0; a < 3; ++a) {
         if (w.N[a] <= 0 || win_n[a] <= 0 || win_n[a] > w.N[a] || win_lo[a] < 0 || win_lo[a] >= w.N[a])
             return -1;
-        if (p->face_kind[2 * a] != p->face_kind[2 * a + 1]) return -1;
+        for (int f = 2 * a; f <= 2 * a + 1; ++f)
+            if (p->face_kind[f] < PERIODIC || p->face_kind[f] > PRESSURE) return -1;
+        if ((p->face_kind[2 * a] == PERIODIC) != (p->face_kind[2 * a + 1] == PERIODIC)) return -1;
         w.lo[a] = win_lo[a];
         w.n[a] = win_n[a];
     }
     if (nsteps < 0) return -1;
     if (diag && ngroups < 6) return -1;
+    /* R13: the first layer of a slip face holds no solid */
+    if (labels) {
+        for (int f = 0; f < 6; ++f) {
+            if (p->face_kind[f] != SLIP) continue;
+            const int a = f / 2;
+            const int64_t layer = (f & 1) ? w.N[a] - 1 : 0;
+            for (int64_t k = 0; k < w.N[2]; ++k)
+                for (int64_t j = 0; j < w.N[1]; ++j)
+                    for (int64_t i = 0; i < w.N[0]; ++i) {
+                        const int64_t gc[3] = {i, j, k};
+                        if (gc[a] == layer && is_solid(labels, w.N, gc)) return -1;
+                    }
+        }
+    }
     w.cells = (int64_t)w.n[0] * w.n[1] * w.n[2];
     const int64_t n = w.cells;
     const int th = p->thermal;
@@ -496,8 +568,9 @@ int oracle_run(const oracle_params* p, const uint8_t* labels, const int32_t* win
     double* g = th ? (double*)malloc(sizeof(double) * Q7 * n) : NULL;
     double* gp = th ? (double*)malloc(sizeof(double) * Q7 * n) : NULL;
     uint8_t* solid = (uint8_t*)malloc(n);
-    if (!f || !fp || (th && (!g || !gp)) || !solid) {
-        free(f); free(fp); free(g); free(gp); free(solid);
+    double* uc = (double*)malloc(sizeof(double) * 3 * n); /* each cell's velocity in its last collision */
+    if (!f || !fp || (th && (!g || !gp)) || !solid || !uc) {
+        free(f); free(fp); free(g); free(gp); free(solid); free(uc);
         return -1;
     }
     const double nan = NAN;
@@ -536,7 +609,7 @@ int oracle_run(const oracle_params* p, const uint8_t* labels, const int32_t* win
     double* part = NULL;
     if (diag) {
         part = (double*)calloc((size_t)w.n[2] * ngroups * 4, sizeof(double));
-        if (!part) { free(f); free(fp); free(g); free(gp); free(solid); return -1; }
+        if (!part) { free(f); free(fp); free(g); free(gp); free(solid); free(uc); return -1; }
     }
     const int64_t plane = (int64_t)w.n[0] * w.n[1];
 
@@ -552,7 +625,9 @@ int oracle_run(const oracle_params* p, const uint8_t* labels, const int32_t* win
             }
             for (int q = 0; q < Q19; ++q) fl[q] = f[q * n + l];
             if (th) for (int k = 0; k < Q7; ++k) gl[k] = g[k * n + l];
-            collide_cell(p, fl, th ? gl : NULL, fo, th ? go : NULL, NULL);
+            double mac[5];
+            collide_cell(p, fl, th ? gl : NULL, fo, th ? go : NULL, mac);
+            for (int a = 0; a < 3; ++a) uc[a * n + l] = mac[1 + a];
             for (int q = 0; q < Q19; ++q) fp[q * n + l] = fo[q];
             if (th) for (int k = 0; k < Q7; ++k) gp[k * n + l] = go[k];
         }
@@ -568,13 +643,45 @@ int oracle_run(const oracle_params* p, const uint8_t* labels, const int32_t* win
                 local_to_global(&w, l, gc);
                 for (int q = 0; q < Q19; ++q) {
                     int o = OPP19[q];
-                    int grp = blocked_group(p, labels, w.N, gc, C19[o]);
-                    if (grp >= 0) {
-                        /* f_q(x, t+1) = f_o^+(x, t): the population sent along c_o comes back */
-                        double v = fp[o * n + l];
+                    int rule = WALL, axis = 0;
+                    int grp = face_rule(p, w.N, gc, C19[o], &rule, &axis);
+                    if (grp < 0) grp = blocked_group(p, labels, w.N, gc, C19[o]); /* a solid: WALL */
+                    if (grp >= 0 && rule == SLIP) {
+                        /* R10 SLIP: q arrives from y = x - c_t, sent along q with its normal
+                           component reversed (the tangential part c_t of c_q is kept) */
+                        int pr = -1, ct[3];
+                        for (int a = 0; a < 3; ++a) ct[a] = a == axis ? 0 : C19[q][a];
+                        for (int r = 0; r < Q19; ++r)
+                            if (C19[r][axis] == -C19[q][axis] && C19[r][(axis + 1) % 3] == C19[q][(axis + 1) % 3] &&
+                                C19[r][(axis + 2) % 3] == C19[q][(axis + 2) % 3])
+                                pr = r;
+                        int64_t src[3];
+                        for (int a = 0; a < 3; ++a) src[a] = wrap_coord(gc[a] - ct[a], w.N[a]);
+                        int64_t ls = global_to_local(&w, src);
+                        double v = ls >= 0 ? fp[pr * n + ls] : nan;
                         f[q * n + l] = v;
                         if (pd && grp < ngroups)
-                            for (int a = 0; a < 3; ++a) pd[grp * 4 + a] += 2.0 * C19[o][a] * v;
+                            for (int a = 0; a < 3; ++a) pd[grp * 4 + a] += (C19[pr][a] - C19[q][a]) * v;
+                    } else if (grp >= 0) {
+                        /* the population x sent along c_o comes back along c_q (R10) */
+                        double v = fp[o * n + l], vin = v;
+                        if (rule == VELOCITY) {
+                            double cu = 0.0;
+                            for (int a = 0; a < 3; ++a) cu += C19[o][a] * p->face_u[3 * grp + a];
+                            vin = v - 6.0 * W19[o] * p->face_rho[grp] * cu;
+                        } else if (rule == PRESSURE) {
+                            double cu = 0.0, uu = 0.0;
+                            for (int a = 0; a < 3; ++a) {
+                                double ua = uc[a * n + l];
+                                cu += C19[o][a] * ua;
+                                uu += ua * ua;
+                            }
+                            vin = -v + 2.0 * W19[o] * p->face_rho[grp] * (1.0 + 4.5 * cu * cu - 1.5 * uu);
+                        }
+                        f[q * n + l] = vin;
+                        /* R9: momentum out along c_o minus momentum back along c_q = -c_o */
+                        if (pd && grp < ngroups)
+                            for (int a = 0; a < 3; ++a) pd[grp * 4 + a] += C19[o][a] * (v + vin);
                     } else {
                         int64_t src[3];
                         for (int a = 0; a < 3; ++a) src[a] = wrap_coord(gc[a] - C19[q][a], w.N[a]);
@@ -632,7 +739,7 @@ int oracle_run(const oracle_params* p, const uint8_t* labels, const int32_t* win
     if (g_out && th) memcpy(g_out, g, sizeof(double) * Q7 * n);
 
     free(part);
-    free(f); free(fp); free(g); free(gp); free(solid);
+    free(f); free(fp); free(g); free(gp); free(solid); free(uc);
     return 0;
 }
 

@@ -42,6 +42,8 @@ class OracleParams(ctypes.Structure):
         ("accel", ctypes.c_double * 3),
         ("gbeta", ctypes.c_double * 3),
         ("T0", ctypes.c_double),
+        ("face_u", ctypes.c_double * 18),
+        ("face_rho", ctypes.c_double * 6),
     ]
 
 
@@ -118,6 +120,12 @@ def to_params(d: dict) -> OracleParams:
         p.accel[i] = float(d.get("accel", [0.0] * 3)[i])
         p.gbeta[i] = float(d.get("gbeta", [0.0] * 3)[i])
     p.T0 = float(d.get("T0", 0.0))
+    fu = np.asarray(d.get("face_u", np.zeros(18)), dtype=float).reshape(-1)
+    fr = d.get("face_rho", [1.0] * 6)
+    for i in range(18):
+        p.face_u[i] = float(fu[i])
+    for i in range(6):
+        p.face_rho[i] = float(fr[i])
     return p
 
 

@@ -1,0 +1,213 @@
+"""Pins of the oracle's slip, velocity and pressure faces (CPU only).
+
+The pages name wall, reflection and open-face rules as per-link rules but
+print no formulas; the oracle takes the textbook half-way forms (specular
+reflection, Ladd's moving-wall bounce-back, anti-bounce-back at a wall
+density).  Each test checks them against something the mathematics fixes:
+  * free slip exerts no tangential force, so a body-forced channel between
+    slip walls accelerates as one block, and a closed box of slip and no-slip
+    walls keeps its mass exactly;
+  * a shear wave between slip walls (zero gradient at the wall) decays at
+    the rate nu k^2 with k = pi / H;
+  * plane Couette flow between a resting wall and a wall moving at U is the
+    exact linear profile;
+  * uniform flow entering through a velocity face and leaving through a
+    pressure face is an exact fixed point (the equilibrium reproduces
+    itself through both rules), and so is a fluid at rest at the wall
+    density between two pressure faces;
+  * for every face kind the momentum handed to the boundary balances the
+    fluid's momentum budget exactly, step by step.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from lattice_boltzmann_cfd_amd import inputs
+
+TAB = oracle.tables()
+C = TAB["c19"].astype(float)
+PER, WALL, SLIP, VEL, PRES = (inputs.FACE_PERIODIC, inputs.FACE_WALL, inputs.FACE_SLIP, inputs.FACE_VELOCITY,
+                              inputs.FACE_PRESSURE)
+
+
+def momentum(f):
+    return (C.T @ f).sum(axis=1)
+
+
+def coords(nx, ny, nz):
+    i = np.arange(nx * ny * nz)
+    return i % nx, (i // nx) % ny, i // (nx * ny)
+
+
+def test_slip_channel_accelerates_as_one_block():
+    nx, ny, nz = 6, 8, 5
+    g = 1e-4
+    p = inputs.base_params(nx, ny, nz, inputs.mrt_rates(0.7), accel=(g, 0.0, 0.0),
+                           face_kind=[PER, PER, SLIP, SLIP, PER, PER])
+    rho, u, _ = inputs.rest(nx, ny, nz)
+    steps = 60
+    o = oracle.run(p, steps, rho, u, want_populations=True, want_diag=True)
+    # fp64 rounding: ~1e-16 of the O(1) populations per step
+    assert np.ptp(o["u"][0]) <= 1e-13
+    assert np.abs(o["u"][1:]).max() <= 1e-13
+    mass = o["f"].sum()
+    assert abs(mass - nx * ny * nz) <= 1e-12
+    # all the body force went into the fluid: no tangential force on the walls
+    assert abs(momentum(o["f"])[0] - steps * g * mass) <= 1e-14 * mass
+    assert np.abs(o["diag"][:, 2:4, 0]).max() <= 1e-18
+    assert np.abs(o["diag"][:, 2:4, 2]).max() <= 1e-18
+
+
+def test_closed_slip_and_wall_box_keeps_mass():
+    nx, ny, nz = 9, 8, 7
+    lab = inputs.sphere_labels(nx, ny, nz, 1.6, centre=(4.5, 4.0, 3.5))
+    p = inputs.base_params(nx, ny, nz, inputs.mrt_rates(0.6), accel=(1e-4, -5e-5, 2e-5),
+                           face_kind=[SLIP, SLIP, WALL, WALL, SLIP, SLIP])
+    rho, u = inputs.taylor_green(nx, ny, nz, u0=0.03, seed=11)
+    fluid = lab == 0
+    m0 = oracle.run(p, 0, rho, u, labels=lab, want_populations=True)["f"][:, fluid].sum()
+    o = oracle.run(p, 20, rho, u, labels=lab, want_populations=True)
+    assert abs(o["f"][:, fluid].sum() - m0) <= 1e-13 * m0
+
+
+def test_slip_shear_wave_decay():
+    """u_x = U cos(pi (y + 1/2) / H) has zero slope at both slip walls
+    (y = -1/2 and H - 1/2) and decays as exp(-nu (pi/H)^2 t)."""
+    H, tau, U = 16, 0.8, 1e-3
+    nu = (tau - 0.5) / 3.0
+    p = inputs.base_params(2, H, 2, inputs.mrt_rates(tau), face_kind=[PER, PER, SLIP, SLIP, PER, PER])
+    _, y, _ = coords(2, H, 2)
+    rho = np.ones(2 * H * 2)
+    mode = np.cos(math.pi * (y + 0.5) / H)
+    u = np.zeros((3, rho.size))
+    u[0] = U * mode
+    amp = []
+    for t in (100, 300):
+        o = oracle.run(p, t, rho, u)
+        amp.append((o["u"][0] * mode).sum() / (mode * mode).sum())
+    rate = math.log(amp[0] / amp[1]) / 200.0
+    expect = nu * (math.pi / H) ** 2
+    assert abs(rate - expect) <= 5e-3 * expect, (rate, expect)
+
+
+def couette_deviation(U, H=8):
+    fu = np.zeros((6, 3))
+    fu[3] = (U, 0.0, 0.0)  # y+ moves along x
+    p = inputs.base_params(2, H, 2, inputs.mrt_rates(0.9), face_kind=[PER, PER, WALL, VEL, PER, PER], face_u=fu)
+    rho, u, _ = inputs.rest(2, H, 2)
+    o = oracle.run(p, 5000, rho, u)
+    _, y, _ = coords(2, H, 2)
+    exact = U * (y + 0.5) / H
+    assert np.abs(o["u"][1:]).max() <= 1e-13
+    return np.abs(o["u"][0] - exact).max()
+
+
+def test_couette_between_resting_and_moving_wall():
+    """The steady profile is the exact line through u = 0 at y = -1/2 and
+    u = U at y = H - 1/2 up to the compressibility of the scheme, which
+    enters at O(U^3): halving U divides the deviation by 8.  A wrong wall
+    velocity, weight or sign would leave an O(U) error."""
+    d2, d1 = couette_deviation(0.02), couette_deviation(0.01)
+    assert d2 <= 2e-3 * 0.02 ** 3, d2
+    assert 6.0 < d2 / d1 < 10.0, (d2, d1)
+
+
+@pytest.mark.parametrize("U", [0.03, -0.02])
+def test_uniform_flow_through_inlet_and_outlet_is_a_fixed_point(U):
+    nx, ny, nz = 7, 4, 3
+    fu = np.zeros((6, 3))
+    fu[0] = (U, 0.0, 0.0)
+    p = inputs.base_params(nx, ny, nz, inputs.mrt_rates(0.7), face_kind=[VEL, PRES, PER, PER, PER, PER],
+                           face_u=fu, face_rho=[1.0] * 6)
+    rho = np.ones(nx * ny * nz)
+    u = np.zeros((3, rho.size))
+    u[0] = U
+    o = oracle.run(p, 200, rho, u)
+    # fp64 rounding accumulated over 200 steps
+    assert np.abs(o["u"][0] - U).max() <= 1e-13
+    assert np.abs(o["u"][1:]).max() <= 1e-13
+    assert np.abs(o["rho"] - 1.0).max() <= 1e-13
+
+
+def test_rest_between_pressure_faces_is_a_fixed_point():
+    n = 6
+    rw = 1.02
+    p = inputs.base_params(n, n, n, inputs.mrt_rates(0.6), face_kind=[PRES, PRES, PRES, PRES, WALL, WALL],
+                           face_rho=[rw] * 6)
+    rho = np.full(n ** 3, rw)
+    u = np.zeros((3, n ** 3))
+    o = oracle.run(p, 300, rho, u)
+    assert np.abs(o["u"]).max() <= 1e-13
+    assert np.abs(o["rho"] - rw).max() <= 1e-13
+
+
+def test_pressure_faces_drive_flow_from_high_to_low_density():
+    nx, ny, nz = 12, 7, 2
+    p = inputs.base_params(nx, ny, nz, inputs.mrt_rates(0.8), face_kind=[PRES, PRES, WALL, WALL, PER, PER],
+                           face_rho=[1.003, 0.997, 1, 1, 1, 1])
+    rho, u, _ = inputs.rest(nx, ny, nz)
+    o = oracle.run(p, 3000, rho, u)
+    x, y, _ = coords(nx, ny, nz)
+    assert (o["u"][0] > 0).all()
+    # density falls along the channel and the profile is symmetric about the axis
+    mid = o["rho"].reshape(nz, ny, nx)[0, ny // 2]
+    assert (np.diff(mid) < 0).all()
+    ux = o["u"][0].reshape(nz, ny, nx)
+    assert np.abs(ux - ux[:, ::-1, :]).max() <= 1e-12
+
+
+def test_solid_in_a_slip_layer_is_rejected():
+    n = 6
+    lab = np.zeros(n ** 3, np.uint8)
+    lab[n * 2 + 3] = 1  # a solid cell in the y = 0 layer... of z = 0
+    p = inputs.base_params(n, n, n, inputs.mrt_rates(0.6), face_kind=[PER, PER, SLIP, SLIP, PER, PER])
+    rho, u, _ = inputs.rest(n, n, n)
+    lab2 = np.zeros(n ** 3, np.uint8)
+    lab2[3 + n * 0 + n * n * 2] = 1  # y = 0
+    with pytest.raises(RuntimeError):
+        oracle.run(p, 1, rho, u, labels=lab2)
+    oracle.run(p, 1, rho, u, labels=lab)  # y = 2: fine
+
+
+def budget_case(thermal):
+    nx, ny, nz = 10, 9, 8
+    lab = inputs.sphere_labels(nx, ny, nz, 1.7, centre=(5.0, 4.5, 4.0))
+    fu = np.zeros((6, 3))
+    fu[0] = (0.02, 0.005, -0.003)  # oblique inflow
+    fu[5] = (0.03, 0.0, 0.0)      # moving lid on z+
+    kw = dict(face_kind=[VEL, PRES, SLIP, SLIP, WALL, VEL], face_u=fu, face_rho=[1.0, 0.995, 1, 1, 1, 1.01],
+              accel=(2e-5, -1e-5, 3e-5))
+    if thermal:
+        kw.update(thermal=True, s7=inputs.thermal_rates(0.05), gbeta=(0, 0, 1e-3), T0=0.1,
+                  face_thermal=[1, 0, 0, 0, 1, 0], face_T=[0.5, 0, 0, 0, -0.5, 0])
+    p = inputs.base_params(nx, ny, nz, inputs.mrt_rates(0.65), **kw)
+    rho, u = inputs.taylor_green(nx, ny, nz, u0=0.02, seed=4)
+    T = 0.3 * np.random.default_rng(5).uniform(-1, 1, rho.size) if thermal else None
+    return p, lab, rho, u, T
+
+
+@pytest.mark.parametrize("thermal", [False, True])
+def test_momentum_budget_every_face_kind(thermal):
+    """Per step: sum_fluid j(t+1) - sum_fluid j(t) = sum_fluid F(t) - (momentum
+    handed to every face and solid), with F = rho accel + rho gbeta (T - T0)
+    from the state at t."""
+    p, lab, rho, u, T = budget_case(thermal)
+    fluid = lab == 0
+    o = oracle.run(p, 0, rho, u, T, labels=lab, want_populations=True)
+    f, g = o["f"], o["g"]
+    accel, gb = np.array(p["accel"]), np.array(p["gbeta"])
+    for step in range(6):
+        r = f[:, fluid].sum(axis=0)
+        F = np.outer(accel, r)
+        if thermal:
+            F += np.outer(gb, r * (g[:, fluid].sum(axis=0) - p["T0"]))
+        o = oracle.run(p, 1, labels=lab, f0=f, g0=g, want_populations=True, want_diag=True)
+        dj = momentum(o["f"][:, fluid]) - momentum(f[:, fluid])
+        handed = o["diag"][0, :, :3].sum(axis=0)
+        assert np.abs(dj - (F.sum(axis=1) - handed)).max() <= 1e-15 * fluid.sum(), step
+        # every kind of face took part
+        for face in range(6):
+            assert np.abs(o["diag"][0, face, :3]).max() > 0, face
+        f, g = o["f"], o["g"]
