@@ -74,7 +74,26 @@ typedef enum lbm_status {
     LBM_E_UNSTABLE = 4, /* a fluid cell's rho or T was non-finite at a read-back */
 } lbm_status;
 
-enum { LBM_FACE_PERIODIC = 0, LBM_FACE_WALL = 1 };
+/* Face kinds.  Every non-periodic face is a half-way boundary between the
+ * last cell layer and the box face; a link (x, p) is a direction p of fluid
+ * cell x that leaves through it.  "GPU lattice Boltzmann: streaming layout
+ * and performance" names wall, reflection and open-face rules as per-link
+ * rules without formulas; these are the textbook half-way forms (f values,
+ * w_p the lattice weight, rho_w = face_rho, u_w = face_u of the face):
+ *   WALL      f_opp(p)(x) = f_p^+(x)                       no-slip, at rest
+ *             ("Multi-GPU thermal lattice Boltzmann ...", Sec. 2)
+ *   SLIP      specular reflection: the normal part of c_p reverses and the
+ *             tangential part c_t carries on, f_q(x + c_t) = f_p^+(x) with
+ *             q = p reflected                              free slip
+ *   VELOCITY  f_opp(p)(x) = f_p^+(x) - 6 w_p rho_w c_p.u_w  wall moving at
+ *             u_w (Ladd): a velocity inlet, or a moving lid
+ *   PRESSURE  f_opp(p)(x) = -f_p^+(x) + 2 w_p rho_w [1 + 9/2 (c_p.u)^2
+ *             - 3/2 u.u], u the cell's own velocity in that step: an outlet
+ *             held at density rho_w
+ * A link leaving through two faces takes the rule of the first crossed axis
+ * in x, y, z order, SLIP acting as WALL there.  The D3Q7 lattice takes each
+ * non-periodic face's thermal rule (face_thermal) whatever its kind. */
+enum { LBM_FACE_PERIODIC = 0, LBM_FACE_WALL = 1, LBM_FACE_SLIP = 2, LBM_FACE_VELOCITY = 3, LBM_FACE_PRESSURE = 4 };
 enum { LBM_ADIABATIC = 0, LBM_DIRICHLET = 1 };
 enum { LBM_STREAM_AUTO = 0, LBM_STREAM_AA = 1, LBM_STREAM_AB = 2 };
 enum { LBM_MAX_GROUPS = 261 }; /* 6 faces + 255 solid labels */
@@ -95,7 +114,7 @@ typedef struct lbm_params {
     int32_t dtype;           /* 4: fp32 populations and arithmetic, 8: fp64 */
     int32_t streaming;       /* LBM_STREAM_*; AUTO = in place (AA) */
     int32_t thermal;         /* 0: D3Q19 only, 1: D3Q19 + D3Q7 */
-    int32_t face_kind[6];    /* LBM_FACE_PERIODIC or LBM_FACE_WALL */
+    int32_t face_kind[6];    /* LBM_FACE_*; an axis is periodic on both faces or on neither */
     int32_t face_thermal[6]; /* LBM_ADIABATIC or LBM_DIRICHLET (wall faces) */
     double face_T[6];        /* Dirichlet wall temperature per face */
     int32_t solid_thermal;   /* thermal rule of every solid cell */
@@ -107,6 +126,8 @@ typedef struct lbm_params {
     double accel[3];         /* body acceleration: F = rho*accel + ... */
     double gbeta[3];         /* buoyancy vector g*beta_T: F = ... + rho*gbeta*(T - T0) */
     double T0;               /* reference temperature of the buoyancy term */
+    double face_u[6][3];     /* wall velocity u_w of each VELOCITY face */
+    double face_rho[6];      /* wall density rho_w of each VELOCITY and PRESSURE face, > 0 */
 } lbm_params;
 
 typedef struct lbm_ctx lbm_ctx;
@@ -115,7 +136,7 @@ typedef struct lbm_ctx lbm_ctx;
  * population buffer(s), link arrays, link scratch, force accumulators and a
  * copy of the labels.  solid_labels: host, nx*ny*nz bytes in the order
  * x + nx*(y + ny*z), 0 = fluid, l >= 1 = solid of group 5 + l; NULL = no
- * solids.  Returns 0 if the parameters are invalid. */
+ * solids.  Returns 0 if the parameters (or labels) are invalid. */
 size_t lbm_required_bytes(const lbm_params* p, const uint8_t* solid_labels);
 
 /* Validate the parameters, build the wall/solid link lists on the host
@@ -127,8 +148,10 @@ size_t lbm_required_bytes(const lbm_params* p, const uint8_t* solid_labels);
  * hip_stream: a hipStream_t (NULL = the null stream), BORROWED.
  * Host arrays are copied before the call returns.  On failure nothing is kept
  * and *out is NULL.  Errors: LBM_E_INVALID (bad sizes, a rate outside [0, 2),
- * a_T outside (-6, 1], one face of an axis periodic and the other a wall,
- * dtype not 4 or 8), LBM_E_NOMEM (device_bytes too small), LBM_E_DEVICE. */
+ * a_T outside (-6, 1], one face of an axis periodic and the other not,
+ * dtype not 4 or 8, a SLIP, VELOCITY or PRESSURE face with links =
+ * LBM_LINKS_PASSES, a solid cell in the first layer of a SLIP face),
+ * LBM_E_NOMEM (device_bytes too small), LBM_E_DEVICE. */
 lbm_status lbm_create(const lbm_params* p, const uint8_t* solid_labels, void* device_buf,
                       size_t device_bytes, void* hip_stream, lbm_ctx** out);
 
@@ -156,8 +179,10 @@ lbm_status lbm_step(lbm_ctx* ctx, int64_t n);
 lbm_status lbm_read_macros(lbm_ctx* ctx, void* rho, void* u, void* T);
 
 /* Copy the latched per-group sums of the last step of the last submission to
- * out (host, 4*n_groups doubles): (Fx, Fy, Fz) = force on the wall face or
- * solid, Q = heat into the fluid through its Dirichlet links.  Groups beyond
+ * out (host, 4*n_groups doubles): (Fx, Fy, Fz) = force on the face or solid,
+ * the momentum the fluid hands over through its links, c_p f_out - c_in f_in
+ * per link (2 c_p f_p^+ for a wall), Q = heat into the fluid through its
+ * Dirichlet links.  Groups beyond
  * LBM_MAX_GROUPS are zero-filled.  Synchronises the stream; returns
  * LBM_E_UNSTABLE if a read-back saw a non-finite fluid value. */
 lbm_status lbm_wall_force(lbm_ctx* ctx, double* out, int32_t n_groups);

@@ -22,6 +22,7 @@ LBM_OK, LBM_E_INVALID, LBM_E_NOMEM, LBM_E_DEVICE, LBM_E_UNSTABLE = 0, 1, 2, 3, 4
 STATUS_NAMES = {0: "LBM_OK", 1: "LBM_E_INVALID", 2: "LBM_E_NOMEM", 3: "LBM_E_DEVICE", 4: "LBM_E_UNSTABLE"}
 LBM_STREAM_AUTO, LBM_STREAM_AA, LBM_STREAM_AB = 0, 1, 2
 LBM_LINKS_IN_KERNEL, LBM_LINKS_PASSES = 0, 1
+LBM_FACE_PERIODIC, LBM_FACE_WALL, LBM_FACE_SLIP, LBM_FACE_VELOCITY, LBM_FACE_PRESSURE = 0, 1, 2, 3, 4
 MAX_GROUPS = 261
 (LBM_DIAG_FLUID_CELLS, LBM_DIAG_MASS, LBM_DIAG_MOM_X, LBM_DIAG_MOM_Y, LBM_DIAG_MOM_Z, LBM_DIAG_KINETIC,
  LBM_DIAG_UMAX, LBM_DIAG_HEAT, LBM_DIAG_CONV_X, LBM_DIAG_CONV_Y, LBM_DIAG_CONV_Z, LBM_DIAG_COUNT) = range(12)
@@ -46,6 +47,7 @@ class LbmParams(ctypes.Structure):
         ("s19", ctypes.c_double * 19), ("s7", ctypes.c_double * 7),
         ("a_T", ctypes.c_double), ("accel", ctypes.c_double * 3), ("gbeta", ctypes.c_double * 3),
         ("T0", ctypes.c_double),
+        ("face_u", ctypes.c_double * 18), ("face_rho", ctypes.c_double * 6),
     ]
 
 
@@ -119,6 +121,12 @@ def to_params(d: dict, dtype: int = 4, streaming: int = LBM_STREAM_AUTO) -> LbmP
         p.accel[i] = float(d.get("accel", [0.0] * 3)[i])
         p.gbeta[i] = float(d.get("gbeta", [0.0] * 3)[i])
     p.T0 = float(d.get("T0", 0.0))
+    fu = np.asarray(d.get("face_u", np.zeros(18)), dtype=float).reshape(-1)
+    fr = d.get("face_rho", [1.0] * 6)
+    for i in range(18):
+        p.face_u[i] = float(fu[i])
+    for i in range(6):
+        p.face_rho[i] = float(fr[i])
     return p
 
 

@@ -33,6 +33,7 @@ struct lbm_ctx {
     int32_t* lcellw = nullptr;
     uint32_t* lmeta = nullptr;
     char* scratch = nullptr;
+    char* face_vel = nullptr;  // PRESSURE faces: velocity planes
     double* wall_T = nullptr;
     double* accum = nullptr;
     double* diag = nullptr;
@@ -103,6 +104,28 @@ bool finite(double v) { return std::isfinite(v); }
 // slower in either precision, so the value is not arbitrary).
 int64_t plane_stride(int64_t n) { return (n + 63) / 64 * 64 + 1024; }
 
+inline bool nonperiodic(const lbm_params* p, int f) { return p->face_kind[f] != LBM_FACE_PERIODIC; }
+
+// A solid cell in the first cell layer of a SLIP face (not supported: the
+// reflected populations travel along that layer).
+bool solid_on_slip_layer(const lbm_params* p, const uint8_t* labels)
+{
+    if (!labels) return false;
+    const int n[3] = {p->nx, p->ny, p->nz};
+    for (int f = 0; f < 6; ++f) {
+        if (p->face_kind[f] != LBM_FACE_SLIP) continue;
+        const int a = f / 2;
+        const int layer = (f & 1) ? n[a] - 1 : 0;
+        for (int z = 0; z < n[2]; ++z)
+            for (int y = 0; y < n[1]; ++y)
+                for (int x = 0; x < n[0]; ++x) {
+                    const int c[3] = {x, y, z};
+                    if (c[a] == layer && labels[x + (int64_t)n[0] * (y + (int64_t)n[1] * z)]) return true;
+                }
+    }
+    return false;
+}
+
 // Returns an empty string when the parameters are acceptable.
 std::string validate(const lbm_params* p)
 {
@@ -117,14 +140,23 @@ std::string validate(const lbm_params* p)
     if (p->streaming < 0 || p->streaming > 2) return "streaming must be 0, 1 or 2";
     if (p->thermal != 0 && p->thermal != 1) return "thermal must be 0 or 1";
     if (p->links != LBM_LINKS_IN_KERNEL && p->links != LBM_LINKS_PASSES) return "links must be 0 or 1";
+    bool open = false;
     for (int f = 0; f < 6; ++f) {
-        if (p->face_kind[f] != LBM_FACE_PERIODIC && p->face_kind[f] != LBM_FACE_WALL) return "bad face_kind";
+        const int k = p->face_kind[f];
+        if (k < LBM_FACE_PERIODIC || k > LBM_FACE_PRESSURE) return "bad face_kind";
         if (p->face_thermal[f] != LBM_ADIABATIC && p->face_thermal[f] != LBM_DIRICHLET) return "bad face_thermal";
         if (!finite(p->face_T[f])) return "face_T must be finite";
+        for (int a = 0; a < 3; ++a)
+            if (!finite(p->face_u[f][a])) return "face_u must be finite";
+        if ((k == LBM_FACE_VELOCITY || k == LBM_FACE_PRESSURE) && !(finite(p->face_rho[f]) && p->face_rho[f] > 0.0))
+            return "face_rho of a VELOCITY or PRESSURE face must be finite and > 0";
+        open = open || k > LBM_FACE_WALL;
     }
     for (int a = 0; a < 3; ++a)
-        if (p->face_kind[2 * a] != p->face_kind[2 * a + 1])
-            return "the two faces of an axis must both be periodic or both be walls";
+        if ((p->face_kind[2 * a] == LBM_FACE_PERIODIC) != (p->face_kind[2 * a + 1] == LBM_FACE_PERIODIC))
+            return "the two faces of an axis must both be periodic or both be non-periodic";
+    if (open && p->links != LBM_LINKS_IN_KERNEL)
+        return "SLIP, VELOCITY and PRESSURE faces need links = LBM_LINKS_IN_KERNEL";
     if (p->solid_thermal != LBM_ADIABATIC && p->solid_thermal != LBM_DIRICHLET) return "bad solid_thermal";
     if (!finite(p->solid_T)) return "solid_T must be finite";
     for (int k = 0; k < 19; ++k)
@@ -173,16 +205,45 @@ Collision<R> make_collision(const lbm_params* p)
     return c;
 }
 
+// Cells of face f (x faces: ny*nz, y faces: nx*nz, z faces: nx*ny).
+int64_t face_area(const lbm_params* p, int f)
+{
+    const int a = f / 2;
+    return a == 0 ? (int64_t)p->ny * p->nz : (a == 1 ? (int64_t)p->nx * p->nz : (int64_t)p->nx * p->ny);
+}
+
+// Element offsets of the PRESSURE faces' velocity planes (3 planes of the
+// face's area each); returns the total element count.
+int64_t face_planes(const lbm_params* p, int64_t* off)
+{
+    int64_t total = 0;
+    for (int f = 0; f < 6; ++f) {
+        off[f] = -1;
+        if (p->face_kind[f] != LBM_FACE_PRESSURE) continue;
+        off[f] = total;
+        total += 3 * face_area(p, f);
+    }
+    return total;
+}
+
 template <typename R>
-Bounce<R> make_bounce(const lbm_params* p, bool in_kernel)
+Bounce<R> make_bounce(const lbm_params* p, bool in_kernel, void* face_vel)
 {
     Bounce<R> b{};
     const double omega = (6.0 + p->a_T) / 21.0;
     for (int f = 0; f < 6; ++f) {
         b.face_gw[f] = (R)(omega * p->face_T[f]);
-        if (p->face_kind[f] == LBM_FACE_WALL) b.walls |= 1 << f;
+        if (nonperiodic(p, f)) b.walls |= 1 << f;
+        if (p->face_kind[f] == LBM_FACE_SLIP) b.slip |= 1 << f;
+        if (p->face_kind[f] == LBM_FACE_VELOCITY) b.vel |= 1 << f;
+        if (p->face_kind[f] == LBM_FACE_PRESSURE) b.pres |= 1 << f;
         if (p->face_thermal[f] == LBM_DIRICHLET) b.face_dirichlet |= 1 << f;
+        b.face_rho[f] = (R)p->face_rho[f];
+        for (int a = 0; a < 3; ++a) b.face_u[f][a] = (R)p->face_u[f][a];
+        b.face_area[f] = face_area(p, f);
     }
+    face_planes(p, b.face_off);
+    b.face_vel = (R*)face_vel;
     b.solid_gw = (R)(omega * p->solid_T);
     b.solid_dirichlet = p->solid_thermal == LBM_DIRICHLET ? 1 : 0;
     b.in_kernel = in_kernel ? 1 : 0;
@@ -201,21 +262,37 @@ struct Dir {
 };
 
 // For fluid cell (x, y, z) and direction c: the group of the blocked link, or
-// -1.  A link is blocked when x + c leaves the box through a wall face (the
-// first crossed axis in x, y, z order) or its periodic image is solid.
+// -1.  A link is blocked when x + c leaves the box through a non-periodic
+// face (the first crossed axis in x, y, z order governs) or its periodic
+// image is solid.  *rule and *axis give the face's rule (a link crossing two
+// faces bounces back where the first one is SLIP) and the governing axis.
 inline int blocked_group(const lbm_params* p, const uint8_t* labels, int x, int y, int z, const int* c,
-                         int32_t* image)
+                         int32_t* image, uint32_t* rule = nullptr, int* axis = nullptr)
 {
     const int n[3] = {p->nx, p->ny, p->nz};
     int t[3] = {x + c[0], y + c[1], z + c[2]};
-    int grp = -1;
-    for (int a = 0; a < 3 && grp < 0; ++a) {
-        if (t[a] < 0 && p->face_kind[2 * a] == LBM_FACE_WALL) grp = 2 * a;
-        else if (t[a] >= n[a] && p->face_kind[2 * a + 1] == LBM_FACE_WALL) grp = 2 * a + 1;
+    int grp = -1, crossed = 0;
+    for (int a = 0; a < 3; ++a) {
+        int f = -1;
+        if (t[a] < 0 && nonperiodic(p, 2 * a)) f = 2 * a;
+        else if (t[a] >= n[a] && nonperiodic(p, 2 * a + 1)) f = 2 * a + 1;
+        if (f < 0) continue;
+        ++crossed;
+        if (grp < 0) grp = f;
     }
     for (int a = 0; a < 3; ++a) t[a] = t[a] < 0 ? t[a] + n[a] : (t[a] >= n[a] ? t[a] - n[a] : t[a]);
     *image = t[0] + p->nx * (t[1] + p->ny * t[2]);
-    if (grp >= 0) return grp;
+    if (rule) *rule = RULE_WALL;
+    if (axis) *axis = grp >= 0 ? grp / 2 : 0;
+    if (grp >= 0) {
+        const int k = p->face_kind[grp];
+        if (rule) {
+            *rule = k == LBM_FACE_SLIP ? (crossed > 1 ? RULE_WALL : RULE_SLIP)
+                  : k == LBM_FACE_VELOCITY ? RULE_VELOCITY
+                  : k == LBM_FACE_PRESSURE ? RULE_PRESSURE : RULE_WALL;
+        }
+        return grp;
+    }
     if (labels && labels[*image]) return 5 + labels[*image];
     return -1;
 }
@@ -237,9 +314,9 @@ int64_t build_links(const lbm_params* p, const uint8_t* labels, bool d3q7, LinkL
     nthreads = std::min<unsigned>(nthreads, (unsigned)nz);
     std::vector<LinkList> parts(nthreads);
     std::vector<int64_t> counts(nthreads, 0);
-    const bool walls_x = p->face_kind[0] == LBM_FACE_WALL;
-    const bool walls_y = p->face_kind[2] == LBM_FACE_WALL;
-    const bool walls_z = p->face_kind[4] == LBM_FACE_WALL;
+    const bool walls_x = nonperiodic(p, 0);
+    const bool walls_y = nonperiodic(p, 2);
+    const bool walls_z = nonperiodic(p, 4);
 
     auto work = [&](unsigned tid) {
         const int z0 = (int)((int64_t)nz * tid / nthreads), z1 = (int)((int64_t)nz * (tid + 1) / nthreads);
@@ -256,7 +333,9 @@ int64_t build_links(const lbm_params* p, const uint8_t* labels, bool d3q7, LinkL
                     if (!edge && !labels) continue;
                     for (size_t i = 0; i < dirs.size(); ++i) {
                         int32_t image;
-                        const int grp = blocked_group(p, labels, x, y, z, dirs[i].c, &image);
+                        uint32_t rule;
+                        int axis;
+                        const int grp = blocked_group(p, labels, x, y, z, dirs[i].c, &image, &rule, &axis);
                         if (grp < 0) continue;
                         ++cnt;
                         if (!out) continue;
@@ -265,6 +344,20 @@ int64_t build_links(const lbm_params* p, const uint8_t* labels, bool d3q7, LinkL
                             meta |= LINK_D3Q7;
                             const int dir = grp < 6 ? p->face_thermal[grp] : p->solid_thermal;
                             if (dir == LBM_DIRICHLET) meta |= LINK_DIRICHLET;
+                        } else {
+                            meta |= (rule << LINK_RULE_SHIFT) | ((uint32_t)axis << LINK_AXIS_SHIFT);
+                            if (rule == RULE_SLIP) {
+                                // the reflected population lands at x + c_t
+                                int t[3] = {x, y, z};
+                                const int n3[3] = {p->nx, p->ny, p->nz};
+                                for (int a = 0; a < 3; ++a) {
+                                    if (a != axis) t[a] += dirs[i].c[a];
+                                    t[a] = t[a] < 0 ? t[a] + n3[a] : (t[a] >= n3[a] ? t[a] - n3[a] : t[a]);
+                                }
+                                image = t[0] + p->nx * (t[1] + p->ny * t[2]);
+                            } else if (rule == RULE_PRESSURE) {
+                                image = axis == 0 ? y + p->ny * z : (axis == 1 ? x + p->nx * z : x + p->nx * y);
+                            }
                         }
                         L.cell.push_back(cell);
                         L.cellw.push_back(image);
@@ -363,7 +456,7 @@ std::vector<uint32_t> build_mask(const lbm_params* p, const uint8_t* labels)
                         bool crosses = false;
                         int w[3];
                         for (int a = 0; a < 3; ++a) {
-                            if ((t[a] < 0 || t[a] >= n3[a]) && p->face_kind[2 * a] == LBM_FACE_WALL) crosses = true;
+                            if ((t[a] < 0 || t[a] >= n3[a]) && nonperiodic(p, 2 * a)) crosses = true;
                             w[a] = t[a] < 0 ? t[a] + n3[a] : (t[a] >= n3[a] ? t[a] - n3[a] : t[a]);
                         }
                         if (!crosses && !labels[w[0] + p->nx * (w[1] + p->ny * w[2])]) m |= 1u << q;
@@ -379,7 +472,7 @@ std::vector<uint32_t> build_mask(const lbm_params* p, const uint8_t* labels)
 }
 
 struct Layout {
-    size_t f, g, f2, g2, mask, lcell, lcellw, lmeta, scratch, wall_T, accum, diag, unstable, total;
+    size_t f, g, f2, g2, mask, lcell, lcellw, lmeta, scratch, face_vel, wall_T, accum, diag, unstable, total;
     int64_t stride;
 };
 
@@ -402,6 +495,8 @@ Layout make_layout(const lbm_params* p, bool solids, int64_t n_links)
     L.lcellw = off; off += align_up(4 * (size_t)n_links);
     L.lmeta = off; off += align_up(4 * (size_t)n_links);
     L.scratch = off; off += align_up(es * (size_t)n_links);
+    int64_t face_off[6];
+    L.face_vel = off; off += align_up(es * (size_t)face_planes(p, face_off));
     L.wall_T = off; off += align_up(8 * LBM_MAX_GROUPS);
     L.accum = off; off += align_up(8 * 4 * LBM_MAX_GROUPS);
     L.diag = off; off += align_up(8 * LBM_DIAG_COUNT);
@@ -442,6 +537,7 @@ LinkArgs<R> link_args(lbm_ctx* c, int mode, char* fsrc, char* fdst, char* gsrc, 
     a.omega = (6.0 + c->p.a_T) / 21.0;
     a.mode = mode;
     a.in_kernel = c->in_kernel ? 1 : 0;
+    a.bb = make_bounce<R>(&c->p, c->in_kernel, c->face_vel);
     return a;
 }
 
@@ -464,7 +560,7 @@ lbm_status enqueue_step(lbm_ctx* c, hipStream_t stream, bool last)
     s.geo = c->geo;
     s.col = collision<R>(c);
     s.mask = c->mask;
-    s.bb = make_bounce<R>(&c->p, c->in_kernel);
+    s.bb = make_bounce<R>(&c->p, c->in_kernel, c->face_vel);
     LinkArgs<R> la;
     if (!c->ab) {
         // one in-place kernel: collision, streaming (and bounce-back)
@@ -585,7 +681,7 @@ FieldArgs<R> field_args(lbm_ctx* c)
     a.unstable = c->unstable;
     a.parity = (int32_t)(c->t & 1);
     a.ab = c->ab ? 1 : 0;
-    a.bb = make_bounce<R>(&c->p, c->in_kernel);
+    a.bb = make_bounce<R>(&c->p, c->in_kernel, c->face_vel);
     a.col = collision<R>(c);
     return a;
 }
@@ -597,7 +693,7 @@ extern "C" {
 size_t lbm_required_bytes(const lbm_params* p, const uint8_t* solid_labels)
 {
     try {
-        if (!validate(p).empty()) return 0;
+        if (!validate(p).empty() || solid_on_slip_layer(p, solid_labels)) return 0;
         const bool solids = any_solid(p, solid_labels);
         const uint8_t* lab = solids ? solid_labels : nullptr;
         int64_t nl = build_links(p, lab, false, nullptr);
@@ -624,6 +720,10 @@ lbm_status lbm_create(const lbm_params* p, const uint8_t* solid_labels, void* de
     }
     if (!device_buf) {
         g_create_error = "device_buf is NULL";
+        return LBM_E_INVALID;
+    }
+    if (solid_on_slip_layer(p, solid_labels)) {
+        g_create_error = "a solid cell lies in the first cell layer of a SLIP face";
         return LBM_E_INVALID;
     }
     lbm_ctx* c = nullptr;
@@ -675,14 +775,14 @@ lbm_status lbm_create(const lbm_params* p, const uint8_t* solid_labels, void* de
         c->lcellw = (int32_t*)(base + L.lcellw);
         c->lmeta = (uint32_t*)(base + L.lmeta);
         c->scratch = base + L.scratch;
+        c->face_vel = base + L.face_vel;
         c->wall_T = (double*)(base + L.wall_T);
         c->accum = (double*)(base + L.accum);
         c->diag = (double*)(base + L.diag);
         c->unstable = (int32_t*)(base + L.unstable);
         c->colf = make_collision<float>(p);
         c->cold = make_collision<double>(p);
-        const bool walls = p->face_kind[0] == LBM_FACE_WALL || p->face_kind[2] == LBM_FACE_WALL ||
-                           p->face_kind[4] == LBM_FACE_WALL;
+        const bool walls = nonperiodic(p, 0) || nonperiodic(p, 2) || nonperiodic(p, 4);
         c->in_kernel = p->links == LBM_LINKS_IN_KERNEL && (walls || solids);
 
         // order the links of both lattices and upload
@@ -855,7 +955,8 @@ int64_t lbm_time(const lbm_ctx* c) { return c ? c->t : -1; }
 int64_t lbm_count_links(const lbm_params* p, const uint8_t* solid_labels, int32_t lattice)
 {
     try {
-        if (!validate(p).empty() || (lattice != 19 && lattice != 7)) return -1;
+        if (!validate(p).empty() || (lattice != 19 && lattice != 7) || solid_on_slip_layer(p, solid_labels))
+            return -1;
         const uint8_t* lab = any_solid(p, solid_labels) ? solid_labels : nullptr;
         return build_links(p, lab, lattice == 7, nullptr);
     } catch (...) {

@@ -36,17 +36,25 @@ struct Geometry {
 
 // Link record (structure of arrays):
 //   cell  : the fluid cell x of the link
-//   cellw : the periodic image of x + c_p (where the population lands)
+//   cellw : the periodic image of x + c_p (where the population lands); for
+//           a SLIP link the image of x + c_t (where the reflected population
+//           lands, c_t the tangential part of c_p); for a PRESSURE link the
+//           cell's index on its face (see Bounce::face_vel)
 //   meta  : bits 0..4 direction p (kernel order of its lattice),
 //           bits 5..13 force/heat group, bit 14 Dirichlet (D3Q7 only),
-//           bit 15 the link belongs to the D3Q7 lattice
-// Links [0, n_wall) cross a wall face; [n_wall, n_total) end in a solid cell.
+//           bit 15 the link belongs to the D3Q7 lattice,
+//           bits 16..17 the D3Q19 rule (LinkRule), bits 18..19 the axis of
+//           the governing face
+// Links [0, n_wall) cross a box face; [n_wall, n_total) end in a solid cell.
 // Each part is sorted by (group, lattice, direction, cell).
 constexpr uint32_t LINK_DIR_MASK = 31u;
 constexpr uint32_t LINK_GROUP_SHIFT = 5;
 constexpr uint32_t LINK_GROUP_MASK = 511u;
 constexpr uint32_t LINK_DIRICHLET = 1u << 14;
 constexpr uint32_t LINK_D3Q7 = 1u << 15;
+constexpr uint32_t LINK_RULE_SHIFT = 16;
+constexpr uint32_t LINK_AXIS_SHIFT = 18;
+enum LinkRule : uint32_t { RULE_WALL = 0, RULE_SLIP = 1, RULE_VELOCITY = 2, RULE_PRESSURE = 3 };
 
 // Per-cell solid mask (only when the box has solid cells).  On a fluid cell,
 // bit q (1..18) is set when x + c_q is a solid cell reached without crossing
@@ -64,18 +72,31 @@ enum LinkMode : int32_t {
     LINK_AB = 2,             // src A(p, x) post-collision, dst B(opp p, x)
 };
 
-// Bounce-back constants of the in-kernel boundary handling.  Wall faces are
-// numbered 0..5 = x-, x+, y-, y+, z-, z+; walls[f] is set for a no-slip face.
-// A D3Q7 population bouncing off face f becomes gw[f] - g (anti-bounce-back,
-// Dirichlet face) or g (adiabatic); off a solid, solid_gw - g or g.
+// Boundary constants of the in-kernel boundary handling.  Faces are numbered
+// 0..5 = x-, x+, y-, y+, z-, z+; walls[f] is set for every non-periodic face,
+// and slip / vel / pres mark the faces of those kinds (the rest of the
+// non-periodic faces are no-slip walls).  A D3Q7 population bouncing off face
+// f becomes gw[f] - g (anti-bounce-back, Dirichlet face) or g (adiabatic);
+// off a solid, solid_gw - g or g.
 template <typename R>
 struct Bounce {
     R face_gw[6];
     R solid_gw;
-    int32_t walls;            // bit f: face f is a wall
+    int32_t walls;            // bit f: face f is not periodic
     int32_t face_dirichlet;   // bit f: face f has a Dirichlet temperature
     int32_t solid_dirichlet;  // solids have a Dirichlet temperature
     int32_t in_kernel;        // walls and solids are handled inside the step kernel
+    int32_t slip, vel, pres;  // bit f: face f is a SLIP / VELOCITY / PRESSURE face
+    int32_t pad0;
+    R face_rho[6];            // wall density (VELOCITY, PRESSURE faces)
+    R face_u[6][3];           // wall velocity (VELOCITY faces)
+    // PRESSURE faces: the velocity of every cell of the face in its last
+    // step, three planes (ux, uy, uz) of face_area[f] values starting at
+    // face_vel + face_off[f]; a cell's index on an x face is y + ny z, on a y
+    // face x + nx z, on a z face x + nx y.
+    R* face_vel;
+    int64_t face_off[6];
+    int64_t face_area[6];
 };
 
 template <typename R>
@@ -110,6 +131,7 @@ struct LinkArgs {
     double omega;          // (6 + a_T)/21
     int32_t mode;
     int32_t in_kernel;     // bounce-back happened inside the step kernel
+    Bounce<R> bb;          // face rules and the PRESSURE faces' velocities
 };
 
 template <typename R>

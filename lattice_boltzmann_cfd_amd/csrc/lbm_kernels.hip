@@ -52,13 +52,14 @@ __device__ __forceinline__ double w19_rt(int q) { return q == 0 ? 1.0 / 3.0 : (q
 struct Nbr {
     int32_t xm, xp, ym, yp, zm, zp;
     uint32_t faces;  // bit f: the cell touches box face f (x-, x+, y-, y+, z-, z+)
+    int32_t x, y, z;
 
     __device__ __forceinline__ Nbr(const Geometry& G, int32_t cell)
     {
         const uint32_t r = divide((uint32_t)cell, G.div_nx);
-        const int32_t x = cell - (int32_t)r * G.nx;
-        const uint32_t z = divide(r, G.div_ny);
-        const int32_t y = (int32_t)r - (int32_t)z * G.ny;
+        x = cell - (int32_t)r * G.nx;
+        z = (int32_t)divide(r, G.div_ny);
+        y = (int32_t)r - z * G.ny;
         xm = (x == 0) ? G.nx - 1 : -1;
         xp = (x == G.nx - 1) ? 1 - G.nx : 1;
         ym = (y == 0) ? (G.ny - 1) * G.nx : -G.nx;
@@ -146,28 +147,175 @@ __device__ __forceinline__ R bounce7(const Bounce<R>& bb, const Blocked& b, int 
     return bb.solid_dirichlet ? bb.solid_gw - v : v;
 }
 
+// Reflection of D3Q19 direction p across a face of axis a: the a component
+// of c_p reversed.
+__host__ __device__ constexpr int refl19(int a, int p)
+{
+    for (int r = 0; r < Q19; ++r)
+        if (cx19(r) == (a == 0 ? -cx19(p) : cx19(p)) && cy19(r) == (a == 1 ? -cy19(p) : cy19(p)) &&
+            cz19(r) == (a == 2 ? -cz19(p) : cz19(p)))
+            return r;
+    return 0;
+}
+
+// The directions of one cell that leave the box, by the axis of the face
+// that governs them (the first crossed axis in x, y, z order) and by that
+// face's rule.  SLIP keeps only directions that cross a single face: one
+// that crosses two faces bounces back like a wall link.
+struct FaceRules {
+    uint32_t ax, ay, az;
+    uint32_t slip, vel, pres;
+};
+
+template <typename R>
+__device__ __forceinline__ FaceRules face_rules(const Bounce<R>& bb, uint32_t faces)
+{
+    const uint32_t fw = faces & (uint32_t)bb.walls;
+    const uint32_t cx = ((fw & 1u) ? dirs_through(0) : 0u) | ((fw & 2u) ? dirs_through(1) : 0u);
+    const uint32_t cy = ((fw & 4u) ? dirs_through(2) : 0u) | ((fw & 8u) ? dirs_through(3) : 0u);
+    const uint32_t cz = ((fw & 16u) ? dirs_through(4) : 0u) | ((fw & 32u) ? dirs_through(5) : 0u);
+    FaceRules r;
+    r.ax = cx;
+    r.ay = cy & ~cx;
+    r.az = cz & ~(cx | cy);
+    uint32_t sl = 0u, ve = 0u, pr = 0u;
+#pragma unroll
+    for (int f = 0; f < 6; ++f) {
+        const uint32_t gov = (f < 2 ? r.ax : (f < 4 ? r.ay : r.az)) & dirs_through(f);
+        if ((bb.slip >> f) & 1) sl |= gov;
+        if ((bb.vel >> f) & 1) ve |= gov;
+        if ((bb.pres >> f) & 1) pr |= gov;
+    }
+    r.slip = sl & ~((cx & (cy | cz)) | (cy & cz));
+    r.vel = ve;
+    r.pres = pr;
+    return r;
+}
+
+// Axis and face that govern a leaving direction p.
+__device__ __forceinline__ int gov_axis(const FaceRules& r, int p)
+{
+    return ((r.ax >> p) & 1u) ? 0 : (((r.ay >> p) & 1u) ? 1 : 2);
+}
+__device__ __forceinline__ int gov_face(const FaceRules& r, int p)
+{
+    const int a = gov_axis(r, p);
+    const int c = a == 0 ? cx19(p) : (a == 1 ? cy19(p) : cz19(p));
+    return 2 * a + (c > 0 ? 1 : 0);
+}
+
+// VELOCITY link (Ladd's moving wall): the returning population is
+// f_p^+ - 6 w_p rho_w c_p.u_w; this is the subtracted term.
+template <typename R>
+__device__ __forceinline__ R vel_shift(const Bounce<R>& bb, int f, int p)
+{
+    const R cu = (R)cx19(p) * bb.face_u[f][0] + (R)cy19(p) * bb.face_u[f][1] + (R)cz19(p) * bb.face_u[f][2];
+    return (R)(6.0 * w19(p)) * bb.face_rho[f] * cu;
+}
+
+// PRESSURE link (anti-bounce-back at the wall density): the returning
+// population f = -f_p^+ + 2 w_p rho_w [1 + 9/2 (c_p.u)^2 - 3/2 u.u], written
+// for shifted storage (f = h + w_p).
+template <typename R>
+__device__ __forceinline__ R pres_value(const Bounce<R>& bb, int f, int p, R hout, R ux, R uy, R uz)
+{
+    const R cu = (R)cx19(p) * ux + (R)cy19(p) * uy + (R)cz19(p) * uz;
+    const R uu = ux * ux + uy * uy + uz * uz;
+    return (R)(2.0 * w19(p)) * (bb.face_rho[f] * (R(1) + R(4.5) * cu * cu - R(1.5) * uu) - R(1)) - hout;
+}
+
+// A cell's slot in the velocity planes of PRESSURE face f.
+template <typename R>
+__device__ __forceinline__ int64_t face_slot(const Bounce<R>& bb, const Geometry& G, int f, const Nbr& nb)
+{
+    const int32_t i = f < 2 ? nb.y + G.ny * nb.z : (f < 4 ? nb.x + G.nx * nb.z : nb.x + G.nx * nb.y);
+    return bb.face_off[f] + i;
+}
+
+// Keep a cell's velocity for each PRESSURE face it lies on (read by the
+// two-buffer pull and by the force pass).
+template <typename R>
+__device__ __forceinline__ void keep_face_velocity(const Bounce<R>& bb, const Geometry& G, const Nbr& nb, R ux,
+                                                   R uy, R uz)
+{
+    const uint32_t fp = nb.faces & (uint32_t)bb.pres;
+#pragma unroll
+    for (int f = 0; f < 6; ++f)
+        if ((fp >> f) & 1u) {
+            const int64_t i = face_slot(bb, G, f, nb);
+            bb.face_vel[i] = ux;
+            bb.face_vel[i + bb.face_area[f]] = uy;
+            bb.face_vel[i + 2 * bb.face_area[f]] = uz;
+        }
+}
+
+// In place, population q of fluid cell x after an odd step's streaming when
+// the link (x, opp q) is blocked: read where the preceding even step left
+// the returning population.  Wall, solid and PRESSURE links: the cell's own
+// slot (q, x) (an even step stores PRESSURE links already anti-bounced);
+// VELOCITY: the same, less the moving-wall term; SLIP: the population sent
+// from x - c_t along q reflected, at (opposite(q reflected), x - c_t).
+template <typename R, int BND>
+__device__ __forceinline__ R blocked_inflow(const R* f, int64_t S, int32_t cell, const Nbr& nb, const FaceRules& fr,
+                                            const Bounce<R>& bb, int q)
+{
+    const int p = opp19(q);
+    if (BND == 2 && ((fr.slip >> p) & 1u)) {
+        const int a = gov_axis(fr, p);
+        const int src = a == 0 ? refl19(0, q) : (a == 1 ? refl19(1, q) : refl19(2, q));
+        const int32_t y = cell + nb.at(a == 0 ? 0 : -cx19(q), a == 1 ? 0 : -cy19(q), a == 2 ? 0 : -cz19(q));
+        return ld(f + opp19(src) * S, y);
+    }
+    R v = ld(f + q * S, cell);
+    if (BND == 2 && ((fr.vel >> p) & 1u)) v -= vel_shift(bb, gov_face(fr, p), p);
+    return v;
+}
+
+// In place, an odd step's blocked outflow p of fluid cell x, stored where the
+// next (even) step reads the returning population: (opposite(p), x) with the
+// link's rule applied, or for SLIP (p reflected, x + c_t).
+template <typename R, int BND>
+__device__ __forceinline__ void blocked_outflow(R* f, int64_t S, int32_t cell, const Nbr& nb, const FaceRules& fr,
+                                                const Bounce<R>& bb, int p, R h, R ux, R uy, R uz)
+{
+    if (BND == 2 && ((fr.slip >> p) & 1u)) {
+        const int a = gov_axis(fr, p);
+        const int dst = a == 0 ? refl19(0, p) : (a == 1 ? refl19(1, p) : refl19(2, p));
+        st(f + dst * S, cell + nb.at(a == 0 ? 0 : cx19(p), a == 1 ? 0 : cy19(p), a == 2 ? 0 : cz19(p)), h);
+        return;
+    }
+    R v = h;
+    if (BND == 2 && ((fr.vel >> p) & 1u)) v = h - vel_shift(bb, gov_face(fr, p), p);
+    if (BND == 2 && ((fr.pres >> p) & 1u)) v = pres_value(bb, gov_face(fr, p), p, h, ux, uy, uz);
+    st(f + opp19(p) * S, cell, v);
+}
+
 // ------------------------------------------------------------ AA step
 
 
-// One fused time step in place.  With BND the step also applies half-way
-// bounce-back at no-slip walls and solid cells ("Multi-GPU thermal lattice
-// Boltzmann simulations using OpenACC and MPI", Sec. 2); without it the box
-// streams as if periodic and link passes fix the blocked directions.
+// One fused time step in place.  With BND the step also applies the
+// half-way boundary rules at non-periodic faces and solid cells
+// ("Multi-GPU thermal lattice Boltzmann simulations using OpenACC and MPI",
+// Sec. 2); without it the box streams as if periodic and link passes fix
+// the blocked directions.  BND = 1: no-slip walls and solids only; BND = 2:
+// also SLIP, VELOCITY and PRESSURE faces.
 // All bounce-back work happens in the odd step; the even step is the plain
-// kernel for every cell (solid cells compute on NaN in their own slots):
+// kernel for every cell (solid cells compute on NaN in their own slots),
+// except that cells on a PRESSURE face store their leaving populations
+// already anti-bounced (the rule needs the cell's velocity of that step):
 //  * even step: every cell stores f_p^+ at (opp p, x);
 //  * odd step, inflow: a population q whose upstream cell x - c_q is across
-//    a wall or solid is the bounce of f_opp(q)^+(x) from the even step, which
-//    sits in (q, x) of the cell itself -- it is read there;
+//    a face or solid is the returning f_opp(q)^+(x) from the even step, which
+//    sits in (q, x) of the cell itself -- it is read there (blocked_inflow);
 //  * odd step, outflow: f_p^+ for a blocked direction p is stored at
-//    (opp p, x), where the next (even) step reads it.  Its usual slot is
-//    skipped when p leaves through a wall (the addressing wraps onto the cell
-//    across the box, whose slot that is) and kept when p points at a solid
-//    cell (only that solid cell reads it next).
+//    (opp p, x), where the next (even) step reads it (blocked_outflow).  Its
+//    usual slot is skipped when p leaves through a face (the addressing
+//    wraps onto the cell across the box, whose slot that is) and kept when p
+//    points at a solid cell (only that solid cell reads it next).
 // A solid cell skips its odd-step stores into slots a fluid neighbour claims
-// this way (mask bits) and into wrapped slots across a wall.  No slot is
+// this way (mask bits) and into wrapped slots across a face.  No slot is
 // touched by two cells in one step.
-template <typename R, bool TH, bool BND>
+template <typename R, bool TH, int BND>
 __global__ void __launch_bounds__(BLOCK) k_aa_step(StepArgs<R> a)
 {
     const Geometry& G = a.geo;
@@ -185,7 +333,27 @@ __global__ void __launch_bounds__(BLOCK) k_aa_step(StepArgs<R> a)
 #pragma unroll
             for (int k = 0; k < Q7; ++k) g[k] = ld(gg + k * S, cell);
         }
+        uint32_t pdirs = 0u;
+        FaceRules fr{};
+        R ux = R(0), uy = R(0), uz = R(0);
+        if (BND == 2 && a.bb.pres) {
+            const Nbr nb(G, cell);
+            if ((nb.faces & (uint32_t)a.bb.pres) && !(a.mask && (a.mask[cell] & MASK_SOLID))) {
+                fr = face_rules(a.bb, nb.faces);
+                pdirs = fr.pres;
+                const Macro<R> m = macros<R, TH>(h, g, a.col);
+                ux = m.ux;
+                uy = m.uy;
+                uz = m.uz;
+                keep_face_velocity(a.bb, G, nb, ux, uy, uz);
+            }
+        }
         collide<R, TH>(h, g, a.col);
+        if (BND == 2 && pdirs) {
+#pragma unroll
+            for (int p = 1; p < Q19; ++p)
+                if ((pdirs >> p) & 1u) h[p] = pres_value(a.bb, gov_face(fr, p), p, h[p], ux, uy, uz);
+        }
 #pragma unroll
         for (int q = 0; q < Q19; ++q) st(f + opp19(q) * S, cell, h[q]);
         if (TH) {
@@ -197,9 +365,11 @@ __global__ void __launch_bounds__(BLOCK) k_aa_step(StepArgs<R> a)
     const Nbr nb(G, cell);
     Blocked b{0u, 0u, 0u, false};
     if (BND) b = blocked_dirs(a.bb, a.mask, cell, nb.faces);
-    const uint32_t blk = b.wall | b.solid;           // a fluid cell's bounced directions
+    const uint32_t blk = b.wall | b.solid;           // a fluid cell's blocked directions
     const uint32_t skip = b.wall | b.claim;          // usual odd-step stores to leave out
     const bool near = BND && !b.is_solid && blk != 0;
+    FaceRules fr{};
+    if (BND == 2 && near) fr = face_rules(a.bb, nb.faces);
 #pragma unroll
     for (int q = 0; q < Q19; ++q) h[q] = ld(f + opp19(q) * S, cell + nb.at(-cx19(q), -cy19(q), -cz19(q)));
     if (TH) {
@@ -209,12 +379,20 @@ __global__ void __launch_bounds__(BLOCK) k_aa_step(StepArgs<R> a)
     if (near) {
 #pragma unroll
         for (int q = 1; q < Q19; ++q)
-            if ((blk >> opp19(q)) & 1u) h[q] = ld(f + q * S, cell);
+            if ((blk >> opp19(q)) & 1u) h[q] = blocked_inflow<R, BND>(f, S, cell, nb, fr, a.bb, q);
         if (TH) {
 #pragma unroll
             for (int k = 1; k < Q7; ++k)
                 if ((blk >> opp7(k)) & 1u) g[k] = bounce7(a.bb, b, opp7(k), ld(gg + k * S, cell));
         }
+    }
+    R ux = R(0), uy = R(0), uz = R(0);
+    if (BND == 2 && fr.pres) {
+        const Macro<R> m = macros<R, TH>(h, g, a.col);
+        ux = m.ux;
+        uy = m.uy;
+        uz = m.uz;
+        keep_face_velocity(a.bb, G, nb, ux, uy, uz);
     }
     collide<R, TH>(h, g, a.col);
 #pragma unroll
@@ -227,8 +405,8 @@ __global__ void __launch_bounds__(BLOCK) k_aa_step(StepArgs<R> a)
     }
     if (near) {
 #pragma unroll
-        for (int q = 1; q < Q19; ++q)
-            if ((blk >> q) & 1u) st(f + opp19(q) * S, cell, h[q]);
+        for (int p = 1; p < Q19; ++p)
+            if ((blk >> p) & 1u) blocked_outflow<R, BND>(f, S, cell, nb, fr, a.bb, p, h[p], ux, uy, uz);
         if (TH) {
 #pragma unroll
             for (int k = 1; k < Q7; ++k)
@@ -240,8 +418,9 @@ __global__ void __launch_bounds__(BLOCK) k_aa_step(StepArgs<R> a)
 // ------------------------------------------------- two buffers (A-B)
 
 // Collide in place: every population stays in its own slot (solid cells
-// compute on NaN in theirs; no fluid cell pulls from a solid slot).
-template <typename R, bool TH, bool BND>
+// compute on NaN in theirs; no fluid cell pulls from a solid slot).  Cells on
+// a PRESSURE face keep their velocity for the pull's anti-bounce-back.
+template <typename R, bool TH, int BND>
 __global__ void __launch_bounds__(BLOCK) k_ab_collide(StepArgs<R> a)
 {
     const Geometry& G = a.geo;
@@ -256,6 +435,13 @@ __global__ void __launch_bounds__(BLOCK) k_ab_collide(StepArgs<R> a)
 #pragma unroll
         for (int k = 0; k < Q7; ++k) g[k] = ld(a.g + k * S, cell);
     }
+    if (BND == 2 && a.bb.pres) {
+        const Nbr nb(G, cell);
+        if ((nb.faces & (uint32_t)a.bb.pres) && !(a.mask && (a.mask[cell] & MASK_SOLID))) {
+            const Macro<R> m = macros<R, TH>(h, g, a.col);
+            keep_face_velocity(a.bb, G, nb, m.ux, m.uy, m.uz);
+        }
+    }
     collide<R, TH>(h, g, a.col);
 #pragma unroll
     for (int q = 0; q < Q19; ++q) st(a.f + q * S, cell, h[q]);
@@ -266,9 +452,11 @@ __global__ void __launch_bounds__(BLOCK) k_ab_collide(StepArgs<R> a)
 }
 
 // Pull into the other buffer: B(q, x) = A(q, x - c_q).  With BND, when
-// x - c_q is across a wall or a solid cell the population comes back from x
-// itself: B(q, x) = A(opp q, x) (anti-bounce-back for a Dirichlet D3Q7 one).
-template <typename R, bool TH, bool BND>
+// x - c_q is across a face or a solid cell the population returns by the
+// link's rule: from x itself, B(q, x) = A(opp q, x) (bounce-back; less the
+// moving-wall term for VELOCITY; anti-bounce-back for PRESSURE, and for a
+// Dirichlet D3Q7 link), or for SLIP from x - c_t along q reflected.
+template <typename R, bool TH, int BND>
 __global__ void __launch_bounds__(BLOCK) k_ab_pull(StepArgs<R> a)
 {
     const Geometry& G = a.geo;
@@ -279,10 +467,32 @@ __global__ void __launch_bounds__(BLOCK) k_ab_pull(StepArgs<R> a)
     Blocked b{0u, 0u, 0u, false};
     if (BND) b = blocked_dirs(a.bb, a.mask, cell, nb.faces);
     const uint32_t blk = b.is_solid ? 0u : (b.wall | b.solid);
+    FaceRules fr{};
+    if (BND == 2 && blk) fr = face_rules(a.bb, nb.faces);
+    R ux = R(0), uy = R(0), uz = R(0);
+    if (BND == 2 && fr.pres) {
+        const int f = __builtin_ctz(nb.faces & (uint32_t)a.bb.pres);  // any of its PRESSURE faces
+        const int64_t i = face_slot(a.bb, G, f, nb);
+        ux = a.bb.face_vel[i];
+        uy = a.bb.face_vel[i + a.bb.face_area[f]];
+        uz = a.bb.face_vel[i + 2 * a.bb.face_area[f]];
+    }
 #pragma unroll
     for (int q = 0; q < Q19; ++q) {
         R v = ld(a.f + q * S, cell + nb.at(-cx19(q), -cy19(q), -cz19(q)));
-        if (BND && ((blk >> opp19(q)) & 1u)) v = ld(a.f + opp19(q) * S, cell);
+        const int p = opp19(q);
+        if (BND && ((blk >> p) & 1u)) {
+            if (BND == 2 && ((fr.slip >> p) & 1u)) {
+                const int ax = gov_axis(fr, p);
+                const int src = ax == 0 ? refl19(0, q) : (ax == 1 ? refl19(1, q) : refl19(2, q));
+                v = ld(a.f + src * S,
+                       cell + nb.at(ax == 0 ? 0 : -cx19(q), ax == 1 ? 0 : -cy19(q), ax == 2 ? 0 : -cz19(q)));
+            } else {
+                v = ld(a.f + p * S, cell);
+                if (BND == 2 && ((fr.vel >> p) & 1u)) v -= vel_shift(a.bb, gov_face(fr, p), p);
+                if (BND == 2 && ((fr.pres >> p) & 1u)) v = pres_value(a.bb, gov_face(fr, p), p, v, ux, uy, uz);
+            }
+        }
         st(a.f2 + q * S, cell, v);
     }
     if (TH) {
@@ -337,25 +547,65 @@ __device__ __forceinline__ LinkSlots link_slots(int mode, int p, int32_t cell, i
     return s;
 }
 
-// Per-link contribution to the group sums: the wall receives 2 c_p f_p^+
-// (D3Q19; the stored value is f - w), and a Dirichlet D3Q7 link passes
-// w T_w - 2 g_p^+ into the fluid.
+// Per-link contribution to the group sums.  A D3Q19 link hands the boundary
+// the momentum it carries out minus what it brings back, c_p f_out - c_in
+// f_in (stored values are f - w): 2 c_p f_p^+ for a wall or solid,
+// (c_p - c_p reflected) f_p^+ for SLIP, c_p (f_out + f_in) for VELOCITY and
+// PRESSURE.  A Dirichlet D3Q7 link passes w T_w - 2 g_p^+ into the fluid.
+// `returned` says whether v is the returning value (else the leaving one);
+// a PRESSURE link needs only the cell's velocity, from the face planes.
 struct LinkSum {
     double fx, fy, fz, q;
 };
 
+__device__ __forceinline__ int refl_rt(int a, int p)
+{
+    const int c[3] = {dir_comp(CX19, p), dir_comp(CY19, p), dir_comp(CZ19, p)};
+    for (int r = 1; r < Q19; ++r)
+        if (dir_comp(CX19, r) == (a == 0 ? -c[0] : c[0]) && dir_comp(CY19, r) == (a == 1 ? -c[1] : c[1]) &&
+            dir_comp(CZ19, r) == (a == 2 ? -c[2] : c[2]))
+            return r;
+    return 0;
+}
+
 template <typename R>
-__device__ __forceinline__ LinkSum link_sum(const LinkArgs<R>& a, uint32_t meta, int p, int32_t grp, R v)
+__device__ __forceinline__ LinkSum link_sum(const LinkArgs<R>& a, uint32_t meta, int p, int32_t grp, R v,
+                                            bool returned, int64_t l)
 {
     LinkSum c{0.0, 0.0, 0.0, 0.0};
-    if (!(meta & LINK_D3Q7)) {
-        const double fv = 2.0 * ((double)v + w19_rt(p));
-        c.fx = dir_comp(CX19, p) * fv;
-        c.fy = dir_comp(CY19, p) * fv;
-        c.fz = dir_comp(CZ19, p) * fv;
-    } else if (meta & LINK_DIRICHLET) {
-        c.q = a.omega * a.wall_T[grp] - 2.0 * (double)v;
+    if (meta & LINK_D3Q7) {
+        if (meta & LINK_DIRICHLET) c.q = a.omega * a.wall_T[grp] - 2.0 * (double)v;
+        return c;
     }
+    const double cp[3] = {(double)dir_comp(CX19, p), (double)dir_comp(CY19, p), (double)dir_comp(CZ19, p)};
+    const double w = w19_rt(p);
+    const uint32_t rule = (meta >> LINK_RULE_SHIFT) & 3u;
+    double s = 0.0;  // F = s c_p, except SLIP
+    if (rule == RULE_WALL) {
+        s = 2.0 * ((double)v + w);
+    } else if (rule == RULE_SLIP) {
+        const int ax = (int)((meta >> LINK_AXIS_SHIFT) & 3u);
+        const double fv = 2.0 * cp[ax] * ((double)v + w);
+        c.fx = ax == 0 ? fv : 0.0;
+        c.fy = ax == 1 ? fv : 0.0;
+        c.fz = ax == 2 ? fv : 0.0;
+        return c;
+    } else if (rule == RULE_VELOCITY) {
+        const double cu = cp[0] * (double)a.bb.face_u[grp][0] + cp[1] * (double)a.bb.face_u[grp][1] +
+                          cp[2] * (double)a.bb.face_u[grp][2];
+        const double shift = 6.0 * w * (double)a.bb.face_rho[grp] * cu;
+        const double hout = returned ? (double)v + shift : (double)v;
+        s = 2.0 * (hout + w) - shift;
+    } else {
+        const int64_t i = a.bb.face_off[grp] + a.cellw[l];
+        const double ux = (double)a.bb.face_vel[i], uy = (double)a.bb.face_vel[i + a.bb.face_area[grp]],
+                     uz = (double)a.bb.face_vel[i + 2 * a.bb.face_area[grp]];
+        const double cu = cp[0] * ux + cp[1] * uy + cp[2] * uz;
+        s = 2.0 * w * (double)a.bb.face_rho[grp] * (1.0 + 4.5 * cu * cu - 1.5 * (ux * ux + uy * uy + uz * uz));
+    }
+    c.fx = cp[0] * s;
+    c.fy = cp[1] * s;
+    c.fz = cp[2] * s;
     return c;
 }
 
@@ -454,9 +704,14 @@ __global__ void __launch_bounds__(BLOCK) k_link_force(LinkArgs<R> a)
                 idx = sl.dst_idx;
                 transformed = true;
             }
+            if (!g7 && transformed && ((meta >> LINK_RULE_SHIFT) & 3u) == RULE_SLIP) {
+                // the reflected population landed at x + c_t
+                plane = refl_rt((int)((meta >> LINK_AXIS_SHIFT) & 3u), p);
+                idx = a.cellw[l];
+            }
             R v = ld((g7 ? a.g_dst : a.f_dst) + plane * S, idx);
             if (transformed && g7 && (meta & LINK_DIRICHLET)) v = (R)(a.omega * a.wall_T[grp]) - v;
-            c = link_sum(a, meta, p, grp, v);
+            c = link_sum(a, meta, p, grp, v, transformed, l);
         }
         const int32_t lead = __shfl(grp, 0, 64);
         if (__all(grp == lead || grp < 0)) {
@@ -536,15 +791,16 @@ __device__ __forceinline__ bool load_cell(const FieldArgs<R>& a, int32_t cell, R
 #pragma unroll
             for (int k = 0; k < Q7; ++k) g[k] = a.g[opp7(k) * S + (cell + nb.at(-cx7(k), -cy7(k), -cz7(k)))];
         }
-        // with in-kernel bounce-back, an inflow from across a wall or a solid
-        // is the bounce of the cell's own even-step output, kept in (q, x)
+        // with in-kernel boundary rules, an inflow from across a face or a
+        // solid is the returning population the even step left behind
         if (a.bb.in_kernel) {
             const Blocked b = blocked_dirs(a.bb, a.mask, cell, nb.faces);
             const uint32_t blk = b.is_solid ? 0u : (b.wall | b.solid);
             if (blk != 0) {
+                const FaceRules fr = face_rules(a.bb, nb.faces);
 #pragma unroll
                 for (int q = 1; q < Q19; ++q)
-                    if ((blk >> opp19(q)) & 1u) h[q] = a.f[q * S + cell];
+                    if ((blk >> opp19(q)) & 1u) h[q] = blocked_inflow<R, 2>(a.f, S, cell, nb, fr, a.bb, q);
                 if (TH) {
 #pragma unroll
                     for (int k = 1; k < Q7; ++k)
@@ -668,15 +924,21 @@ inline dim3 grid_for(int64_t n) { return dim3((unsigned)((n + BLOCK - 1) / BLOCK
 
 }  // namespace
 
-// Pick the <thermal, in-kernel bounce-back> instance of a cell kernel.
+// Pick the <thermal, boundary rules> instance of a cell kernel: no in-kernel
+// boundary, walls and solids only, or also SLIP / VELOCITY / PRESSURE faces.
 #define LBM_CELL_LAUNCH(KERNEL, a, thermal, s)                                                              \
     do {                                                                                                    \
         const dim3 grid_ = grid_for((a).geo.ncell);                                                         \
-        const bool solid_ = (a).bb.in_kernel != 0;                                                          \
-        if (thermal && solid_) hipLaunchKernelGGL((KERNEL<R, true, true>), grid_, dim3(BLOCK), 0, s, a);    \
-        else if (thermal) hipLaunchKernelGGL((KERNEL<R, true, false>), grid_, dim3(BLOCK), 0, s, a);        \
-        else if (solid_) hipLaunchKernelGGL((KERNEL<R, false, true>), grid_, dim3(BLOCK), 0, s, a);         \
-        else hipLaunchKernelGGL((KERNEL<R, false, false>), grid_, dim3(BLOCK), 0, s, a);                    \
+        const int bnd_ = (a).bb.in_kernel ? (((a).bb.slip | (a).bb.vel | (a).bb.pres) ? 2 : 1) : 0;        \
+        if (thermal) {                                                                                      \
+            if (bnd_ == 2) hipLaunchKernelGGL((KERNEL<R, true, 2>), grid_, dim3(BLOCK), 0, s, a);           \
+            else if (bnd_ == 1) hipLaunchKernelGGL((KERNEL<R, true, 1>), grid_, dim3(BLOCK), 0, s, a);      \
+            else hipLaunchKernelGGL((KERNEL<R, true, 0>), grid_, dim3(BLOCK), 0, s, a);                     \
+        } else {                                                                                            \
+            if (bnd_ == 2) hipLaunchKernelGGL((KERNEL<R, false, 2>), grid_, dim3(BLOCK), 0, s, a);          \
+            else if (bnd_ == 1) hipLaunchKernelGGL((KERNEL<R, false, 1>), grid_, dim3(BLOCK), 0, s, a);     \
+            else hipLaunchKernelGGL((KERNEL<R, false, 0>), grid_, dim3(BLOCK), 0, s, a);                    \
+        }                                                                                                   \
     } while (0)
 
 template <typename R>

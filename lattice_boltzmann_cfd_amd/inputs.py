@@ -23,6 +23,12 @@ Workloads (the pages give no input data; every one is synthetic):
                     (-0.5), seeded random non-overlapping spheres of radius
                     4..12 up to 10 % solid fraction, Ra = 1e8, Pr = 0.71.
   * ``sol256``   -- the ``sol128`` recipe at 256^3 (the throughput point).
+  * ``channel256``-- flow past a sphere in an open channel, 256x128x128: x-
+                    a velocity inlet at U = 0.05, x+ a pressure outlet at
+                    rho_w = 1, y and z free-slip faces, a solid sphere R = 16
+                    at (nx/4, ny/2, nz/2), tau = 0.52, uniform start u = (U,
+                    0, 0) on rho = 1 (exercises the slip, velocity and
+                    pressure face rules).
 
 Relaxation-rate slots follow the moment basis row order used by both sides:
 0 rho, 1 e, 2 eps, 3/5/7 j, 4/6/8 q, 9 3pxx, 10 3pixx, 11 pww, 12 piww,
@@ -304,7 +310,32 @@ def rb512(shape=(512, 512, 512), Ra=1e8, Pr=0.71, H=512, seed=5, rmin=4, rmax=12
     return Workload("rb512", p, rho, u, T, lab, 1000, dict(scales=sc, Ra=Ra, Pr=Pr, H=H, spheres=len(spheres)))
 
 
-WORKLOADS = dict(tg32=tg32, sol128=sol128, sol256=sol256, sphere128=sphere128, cavity256=cavity256, rb512=rb512)
+def channel256(shape=(256, 128, 128), U=0.05, R=16.0, tau=0.52, thermal=False) -> Workload:
+    """Reduced boxes keep the recipe (sphere at a quarter of the length, on
+    the axis).  With thermal=True the inflow carries T = 0.5 into a T = 0
+    channel (Dirichlet inlet, adiabatic elsewhere) and the sphere is held at
+    T = -0.5."""
+    nx, ny, nz = shape
+    rho = np.ones(nx * ny * nz)
+    u = np.zeros((3, rho.size))
+    u[0] = U
+    lab = sphere_labels(nx, ny, nz, R, centre=(nx / 4.0, ny / 2.0, nz / 2.0))
+    fu = np.zeros((6, 3))
+    fu[0] = (U, 0.0, 0.0)
+    kw = {}
+    T = None
+    if thermal:
+        T = np.zeros(rho.size)
+        kw = dict(thermal=True, s7=thermal_rates(0.02), face_thermal=[DIRICHLET, 0, 0, 0, 0, 0],
+                  face_T=[0.5, 0, 0, 0, 0, 0], solid_thermal=DIRICHLET, solid_T=-0.5, gbeta=(0.0, 0.0, 1e-4))
+    p = base_params(nx, ny, nz, mrt_rates(tau),
+                    face_kind=[FACE_VELOCITY, FACE_PRESSURE, FACE_SLIP, FACE_SLIP, FACE_SLIP, FACE_SLIP],
+                    face_u=fu, face_rho=[1.0] * 6, **kw)
+    return Workload("channel256", p, rho, u, T, lab, 2000, dict(U=U, R=R))
+
+
+WORKLOADS = dict(tg32=tg32, sol128=sol128, sol256=sol256, sphere128=sphere128, cavity256=cavity256, rb512=rb512,
+                 channel256=channel256)
 
 
 def make(name: str, shape=None, **kw) -> Workload:

@@ -41,7 +41,9 @@ def test_struct_layout_matches_header():
     assert P.solid_T.offset == 128
     assert P.s19.offset == 136
     assert P.T0.offset == 136 + 8 * (19 + 7 + 1 + 3 + 3)
-    assert binding.ctypes.sizeof(P) == P.T0.offset + 8
+    assert P.face_u.offset == P.T0.offset + 8
+    assert P.face_rho.offset == P.face_u.offset + 8 * 18
+    assert binding.ctypes.sizeof(P) == P.face_rho.offset + 8 * 6
 
 
 def periodic(n=8, **kw):
@@ -67,6 +69,11 @@ def test_required_bytes_sizes(lib):
     lambda p: p.update(a_T=-6.0),
     lambda p: p.update(accel=[float("nan"), 0, 0]),
     lambda p: p.update(face_thermal=[2, 0, 0, 0, 0, 0]),
+    lambda p: p.update(face_kind=[5, 5, 0, 0, 0, 0]),
+    lambda p: p.update(face_kind=[2, 0, 0, 0, 0, 0]),  # one face of x periodic, the other not
+    lambda p: p.update(face_kind=[4, 4, 0, 0, 0, 0], face_rho=[0.0] * 6),
+    lambda p: p.update(face_kind=[3, 1, 0, 0, 0, 0], face_u=[float("inf")] + [0.0] * 17),
+    lambda p: p.update(face_kind=[2, 2, 0, 0, 0, 0], links=binding.LBM_LINKS_PASSES),
 ])
 def test_invalid_params_rejected_without_device_work(lib, mutate):
     p = periodic()
@@ -105,6 +112,31 @@ def test_null_context_calls_are_invalid(lib):
     assert lib.lbm_diagnostics(None, out, binding.LBM_DIAG_COUNT) == binding.LBM_E_INVALID
     assert lib.lbm_time(None) == -1
     assert lib.lbm_num_links(None, 19) == -1
+
+
+def test_solid_on_a_slip_layer_rejected(lib):
+    n = 8
+    p = periodic(n, face_kind=[0, 0, 2, 2, 0, 0])
+    lab = np.zeros(n ** 3, np.uint8)
+    lab[3 + n * 2 + n * n * 4] = 1  # y = 2: allowed
+    assert binding.lbm_required_bytes(p, lab) > 0
+    lab[5 + n * (n - 1) + n * n * 1] = 1  # y = n - 1: on the y+ slip layer
+    assert binding.lbm_required_bytes(p, lab) == 0
+    assert binding.lbm_count_links(p, lab, 19) == -1
+    with pytest.raises(binding.LbmError) as e:
+        binding.lbm_create(p, lab, 256, 1 << 30)
+    assert e.value.status == binding.LBM_E_INVALID
+
+
+@pytest.mark.parametrize("kinds", [[2] * 6, [3, 4, 2, 2, 1, 3], [4] * 6])
+def test_link_counts_do_not_depend_on_face_kind(lib, kinds):
+    """Every non-periodic face blocks the same links whatever its rule."""
+    n = 6
+    walls = inputs.base_params(n, n, n, inputs.mrt_rates(0.6), face_kind=[1] * 6, thermal=True,
+                               s7=[0, 1, 1, 1, 1, 1, 1])
+    other = dict(walls, face_kind=kinds)
+    for lattice in (19, 7):
+        assert binding.lbm_count_links(other, None, lattice) == binding.lbm_count_links(walls, None, lattice)
 
 
 def test_box_too_large_rejected(lib):
