@@ -44,6 +44,8 @@ WORKLOAD_INFO = {
     "rb512": "thermal D3Q19+D3Q7 MRT, 512^3, periodic x/y, z- hot/z+ cold, random spheres R 4..12 (10%), "
              "Ra=1e8, Pr=0.71",
     "tg32": "D3Q19 MRT, 32^3 periodic Taylor-Green, tau=0.6",
+    "channel256": "D3Q19 MRT, 256x128x128 open channel: x- velocity inlet U=0.05, x+ pressure outlet rho=1, "
+                  "free-slip y/z faces, solid sphere R=16 at (64,64,64), tau=0.52",
 }
 
 
@@ -190,6 +192,11 @@ def main(argv=None):
                    "hbm_TBps_algorithmic": round(bpc * w.cells * args.steps / (ms / 1e3) / 1e12, 3)},
         "roofline": roofline,
     }
+    if w.labels is not None:
+        # solid cells are updated too (on NaN); the throughput over fluid cells only
+        fluid = int((w.labels == 0).sum())
+        line["config"]["fluid_cells"] = fluid
+        line["config"]["fluid_MLUPS"] = round(fluid * args.steps / (ms / 1e3) / 1e6, 1)
     solver.close()
     del rho, solver
     torch.cuda.empty_cache()

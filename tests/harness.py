@@ -73,7 +73,7 @@ def window_valid(params, lo, n, steps):
         if n[a] == shape[a]:
             m = np.ones(n[a], bool)
         else:
-            wall = params["face_kind"][2 * a] == 1
+            wall = params["face_kind"][2 * a] != 0  # a non-periodic face bounds the box
             lo_cut = not (wall and lo[a] == 0)
             hi_cut = not (wall and lo[a] + n[a] == shape[a])
             m = np.ones(n[a], bool)

@@ -154,3 +154,15 @@ def test_rb512_windows(rb512):
     wins = random_windows(w.shape, 5, 26, seed=512) + [((300, 17, 0), (26, 26, 26)), ((5, 400, 512 - 26), (26, 26, 26))]
     compare_windows(w, g, 7, wins)
     assert np.isnan(g["rho"][w.labels != 0]).all()
+
+
+def test_channel256_windows():
+    say("CASE channel256 full size (inlet, outlet, slip faces, sphere), 7 steps, windows")
+    w = inputs.make("channel256")
+    g = gpu_run(w, [7], want_forces=False)
+    nx, ny, nz = w.shape
+    n = 26
+    wins = [((0, 0, 0), (n, n, n)), ((nx - n, ny - n, nz - n), (n, n, n)), ((nx // 4 - 16 - 13, ny // 2 - 13, nz // 2 - 13),
+            (n, n, n)), ((0, 50, nz - n), (n, n, n)), ((nx - n, 0, 40), (n, n, n))]
+    compare_windows(w, g, 7, wins)
+    assert np.isnan(g["rho"][w.labels != 0]).all()
