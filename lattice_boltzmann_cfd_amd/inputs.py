@@ -29,11 +29,21 @@ Workloads (the pages give no input data; every one is synthetic):
                     at (nx/4, ny/2, nz/2), tau = 0.52, uniform start u = (U,
                     0, 0) on rho = 1 (exercises the slip, velocity and
                     pressure face rules).
+  * ``cavity2d`` -- thermal D2Q9 + D2Q5 (the thermal-LBM page's 2D model),
+                    8193 x 8193 square cell, x- hot (+0.5), x+ cold (-0.5),
+                    y faces adiabatic, no-slip everywhere, Pr = 0.71,
+                    Ra = 1e8, buoyancy along +y, fp64 (the page runs its 2D
+                    cell in double precision for 12000 steps).
+  * ``tg2d``     -- D2Q9 MRT, 256 x 256 periodic Taylor-Green vortex u0 =
+                    0.05 with +-1e-3 density noise, tau = 0.6.
 
 Relaxation-rate slots follow the moment basis row order used by both sides:
 0 rho, 1 e, 2 eps, 3/5/7 j, 4/6/8 q, 9 3pxx, 10 3pixx, 11 pww, 12 piww,
 13-15 pxy/pyz/pxz, 16-18 m.  D3Q7 rows: 0 T, 1-3 flux, 4 energy-like,
-5-6 second-order anisotropic.
+5-6 second-order anisotropic.  Two-dimensional runs (``lattice = 1``, nz = 1)
+use ``s9`` in the D2Q9 row order 0 rho, 1 e, 2 eps, 3 jx, 4 qx, 5 jy, 6 qy,
+7 pxx, 8 pxy and ``s5`` in the D2Q5 row order 0 T, 1-2 flux, 3 energy-like,
+4 anisotropic.
 """
 from __future__ import annotations
 
@@ -59,6 +69,11 @@ ROWS_M = (16, 17, 18)
 U_FREEFALL = 0.1
 # default D3Q7 constant a_T (rest weight (1 - a_T)/7 = 1/4)
 A_T_DEFAULT = -0.75
+# default D2Q5 constant a_T: rest weight (1 - a_T)/5 = 1/2, moving (4 + a_T)/20
+# = 1/8, the weights the D3Q7 default sums to on a single z layer
+A_T_DEFAULT_2D = -1.5
+ROWS_NU_2D = (7, 8)
+ROWS_Q_2D = (4, 6)
 
 
 def mrt_rates(tau: float, s_e=1.19, s_eps=1.4, s_q=1.2, s_pi=1.4, s_m=1.98) -> list:
@@ -96,6 +111,32 @@ def thermal_rates(alpha: float, a_T: float = A_T_DEFAULT, q_e: float = 1.0, q_nu
     return [0.0, q_k, q_k, q_k, q_e, q_nu, q_nu]
 
 
+def mrt_rates_2d(tau: float, s_e=1.1, s_eps=1.0, s_q=1.2) -> list:
+    """D2Q9 rates: s_nu = 1/tau on the two stress rows, conserved rows 0."""
+    s = [0.0] * 9
+    s[1] = s_e
+    s[2] = s_eps
+    for r in ROWS_Q_2D:
+        s[r] = s_q
+    for r in ROWS_NU_2D:
+        s[r] = 1.0 / tau
+    return s
+
+
+def poiseuille_rates_2d(tau: float) -> list:
+    """D2Q9 rates with s_q = 8(2 - s_nu)/(8 - s_nu) (wall exactly half-way)."""
+    s_nu = 1.0 / tau
+    return mrt_rates_2d(tau, s_q=8.0 * (2.0 - s_nu) / (8.0 - s_nu))
+
+
+def thermal_rates_2d(alpha: float, a_T: float = A_T_DEFAULT_2D, q_e: float = 1.0, q_nu: float = 1.0) -> list:
+    """D2Q5 rates: q_kappa on the flux rows from alpha = cs_T^2 (1/q_kappa - 1/2),
+    cs_T^2 = (4 + a_T)/10."""
+    cs2 = (4.0 + a_T) / 10.0
+    q_k = 1.0 / (alpha / cs2 + 0.5)
+    return [0.0, q_k, q_k, q_e, q_nu]
+
+
 def thermal_scales(H: float, Ra: float, Pr: float, U_f: float = U_FREEFALL) -> dict:
     """Lattice parameters from Ra = g beta dT H^3/(nu alpha), Pr = nu/alpha, dT = 1,
     free-fall velocity U_f = sqrt(g beta dT H)."""
@@ -121,6 +162,29 @@ def base_params(nx, ny, nz, s19, thermal=False, face_kind=None, face_thermal=Non
         solid_thermal=int(solid_thermal), solid_T=float(solid_T),
         face_u=fu, face_rho=list(face_rho or [1.0] * 6),
     )
+
+
+def base_params_2d(nx, ny, s9, thermal=False, face_kind=None, face_thermal=None, face_T=None, s5=None,
+                   a_T=A_T_DEFAULT_2D, accel=(0.0, 0.0), gbeta=(0.0, 0.0), T0=0.0, solid_thermal=ADIABATIC,
+                   solid_T=0.0, face_u=None, face_rho=None) -> dict:
+    """Parameters of a two-dimensional run (D2Q9 + D2Q5, lattice = 1) on one
+    periodic z layer.  face_kind, face_thermal, face_T, face_rho: 4 values
+    (x-, x+, y-, y+); face_u: 4 wall velocities (ux, uy); accel, gbeta: 2
+    components."""
+    def six(v, fill):
+        v = list(v) if v is not None else [fill] * 4
+        return v[:4] + [fill, fill]
+    fu = np.zeros((6, 3))
+    if face_u is not None:
+        fu[:4, :2] = np.asarray(face_u, dtype=float).reshape(4, 2)
+    d = base_params(nx, ny, 1, [0.0] * 19, thermal=thermal, face_kind=six(face_kind, FACE_PERIODIC),
+                    face_thermal=six(face_thermal, ADIABATIC), face_T=six(face_T, 0.0), a_T=a_T,
+                    accel=(accel[0], accel[1], 0.0), gbeta=(gbeta[0], gbeta[1], 0.0), T0=T0,
+                    solid_thermal=solid_thermal, solid_T=solid_T, face_u=fu, face_rho=six(face_rho, 1.0))
+    d["lattice"] = 1
+    d["s9"] = [float(v) for v in s9]
+    d["s5"] = [float(v) for v in (s5 or [0.0] * 5)]
+    return d
 
 
 # ------------------------------------------------------------------ fields
@@ -334,8 +398,32 @@ def channel256(shape=(256, 128, 128), U=0.05, R=16.0, tau=0.52, thermal=False) -
     return Workload("channel256", p, rho, u, T, lab, 2000, dict(U=U, R=R))
 
 
+def cavity2d(shape=(8193, 8193), Ra=1e8, Pr=0.71, H=None) -> Workload:
+    """The thermal-LBM page's 2D convection cell (Sec. 2, Sec. 3 strong
+    scaling grid 8193 x 8193).  Reduced boxes keep the recipe; H defaults to
+    the box width."""
+    nx, ny = shape[0], shape[1]
+    H = nx if H is None else H
+    sc = thermal_scales(H, Ra, Pr)
+    rho, u, T = rest(nx, ny, 1)
+    p = base_params_2d(
+        nx, ny, mrt_rates_2d(sc["tau"]), thermal=True, face_kind=[FACE_WALL] * 4,
+        face_thermal=[DIRICHLET, DIRICHLET, ADIABATIC, ADIABATIC], face_T=[0.5, -0.5, 0.0, 0.0],
+        s5=thermal_rates_2d(sc["alpha"]), gbeta=(0.0, sc["gbeta"]), T0=0.0,
+    )
+    return Workload("cavity2d", p, rho, u, T, None, 12000, dict(scales=sc, Ra=Ra, Pr=Pr, H=H))
+
+
+def tg2d(shape=(256, 256), u0=0.05, seed=1, tau=0.6) -> Workload:
+    nx, ny = shape[0], shape[1]
+    rho, u = taylor_green(nx, ny, 1, u0=u0, seed=seed)
+    u[2] = 0.0
+    p = base_params_2d(nx, ny, mrt_rates_2d(tau))
+    return Workload("tg2d", p, rho, u, None, None, 1000)
+
+
 WORKLOADS = dict(tg32=tg32, sol128=sol128, sol256=sol256, sphere128=sphere128, cavity256=cavity256, rb512=rb512,
-                 channel256=channel256)
+                 channel256=channel256, cavity2d=cavity2d, tg2d=tg2d)
 
 
 def make(name: str, shape=None, **kw) -> Workload:

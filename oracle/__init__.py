@@ -16,6 +16,8 @@ from .oracle import (  # noqa: F401
     equilibrium,
     library_path,
     run,
+    lattice_sizes,
     tables,
+    tables_2d,
     to_params,
 )

@@ -88,6 +88,20 @@
  *      kind; an axis is periodic on both faces or on neither.
  *  R13 No solid cell may lie in the first cell layer of a SLIP face (the
  *      reflected population travels along that layer).
+ *  R14 The two-dimensional variant of [TL] Sec. 2 (D2Q9 for the flow, D2Q5
+ *      for the temperature) runs on a box with nz = 1 and periodic z faces.
+ *      D2Q9 = rest, 4 axis and 4 diagonal vectors of the xy plane with
+ *      weights 4/9, 1/9, 1/36; M = the orthogonal basis of Lallemand and Luo
+ *      (the 2D member of the d'Humieres family); rows, as polynomials of c:
+ *        1, 3c^2-4, (9c^4-21c^2+8)/2, cx, (3c^2-5)cx, cy, (3c^2-5)cy,
+ *        cx^2-cy^2, cx cy;
+ *      S = diag(s9[0..8]); m_eq = M f_eq and F~ as in R3-R4 with the D2Q9
+ *      weights.  [TL] puts the buoyancy along y in 2D; here it is the
+ *      vector gbeta, as in R5.
+ *  R15 D2Q5, directions ordered (0,+x,-x,+y,-y); N rows (1,1,1,1,1), e_x,
+ *      e_y, (-4,1,1,1,1), (0,1,1,-1,-1); n_eq = (T, ux T, uy T, a_T T, 0);
+ *      Q = diag(s5[0..4]).  The anti-bounce-back constant is the one [TL]
+ *      Sec. 2 gives for D2Q5, w = (4 + a_T)/10.
  *
  * Windows: the oracle can run on a window (a sub-box, possibly wrapping
  * through periodic faces) of the full box.  A population that would be
@@ -105,6 +119,8 @@
 
 #define Q19 19
 #define Q7 7
+#define Q9 9
+#define Q5 5
 #define MAXGROUPS 261 /* 6 faces + 255 solid labels */
 
 typedef struct oracle_params {
@@ -124,6 +140,10 @@ typedef struct oracle_params {
     double T0;
     double face_u[18];        /* wall velocity u_w of each face (VELOCITY faces) */
     double face_rho[6];       /* wall density rho_w of each face (VELOCITY, PRESSURE) */
+    int32_t lattice;          /* 0: D3Q19 (+ D3Q7), 1: D2Q9 (+ D2Q5) on nz = 1 (R14) */
+    int32_t pad1;
+    double s9[9];             /* D2Q9 MRT rates in the row order of R14 */
+    double s5[5];             /* D2Q5 rates in the row order of R15 */
 } oracle_params;
 
 enum { PERIODIC = 0, WALL = 1, SLIP = 2, VELOCITY = 3, PRESSURE = 4 };
@@ -139,7 +159,37 @@ static int C7[Q7][3];
 static int OPP7[Q7];
 static double N7[Q7][Q7];
 static double NINV7[Q7][Q7];
+static int C9[Q9][3];
+static double W9[Q9];
+static int OPP9[Q9];
+static double M9[Q9][Q9];
+static double MINV9[Q9][Q9];
+static int C5[Q5][3];
+static int OPP5[Q5];
+static double N5[Q5][Q5];
+static double NINV5[Q5][Q5];
 static int tables_ready = 0;
+
+/* One lattice pair of the double-distribution model: the flow lattice (Q
+   velocities C, weights W, moment matrix M) and the temperature lattice (QT
+   velocities CT, moment matrix N), plus the anti-bounce-back constant
+   w = (wnum + a_T) / wden of [TL] Sec. 2. */
+typedef struct lattice {
+    int Q;
+    const int (*C)[3];
+    const double* W;
+    const int* OPP;
+    const double* M;    /* Q x Q, row k = moment k */
+    const double* MINV;
+    int QT;
+    const int (*CT)[3];
+    const int* OPPT;
+    const double* N;    /* QT x QT */
+    const double* NINV;
+    double wnum, wden;
+} lattice;
+
+static lattice LAT3, LAT2;
 
 /* Gauss-Jordan inversion with partial pivoting; returns 0 on success. */
 static int invert(int n, const double* a, double* inv)
@@ -201,33 +251,64 @@ static void moment_row_values(const int* c, double* row)
     row[18] = (cx * cx - cy * cy) * cz;
 }
 
-static int build_tables(void)
+/* Moment polynomials of R14 (D2Q9), evaluated at one velocity vector. */
+static void moment_row_values_2d(const int* c, double* row)
 {
-    if (tables_ready) return 0;
-    /* R1: every c in {-1,0,1}^3 with |c|^2 <= 2, rest first, then by |c|^2,
-       each vector followed by its opposite. */
+    double cx = c[0], cy = c[1];
+    double c2 = cx * cx + cy * cy;
+    row[0] = 1.0;
+    row[1] = 3.0 * c2 - 4.0;
+    row[2] = (9.0 * c2 * c2 - 21.0 * c2 + 8.0) / 2.0;
+    row[3] = cx;
+    row[4] = (3.0 * c2 - 5.0) * cx;
+    row[5] = cy;
+    row[6] = (3.0 * c2 - 5.0) * cy;
+    row[7] = cx * cx - cy * cy;
+    row[8] = cx * cy;
+}
+
+/* Every c in {-1,0,1}^dims (z = 0 when dims = 2) with |c|^2 <= 2, rest
+   first, then by |c|^2, each vector followed by its opposite; returns the
+   count. */
+static int velocity_set(int dims, int (*C)[3])
+{
     int n = 0;
+    int zr = dims == 3 ? 1 : 0;
     for (int len2 = 0; len2 <= 2; ++len2)
-        for (int z = -1; z <= 1; ++z)
+        for (int z = -zr; z <= zr; ++z)
             for (int y = -1; y <= 1; ++y)
                 for (int x = -1; x <= 1; ++x) {
                     if (x * x + y * y + z * z != len2) continue;
                     /* keep only the "positive" member of each pair here */
                     int first = x != 0 ? x : (y != 0 ? y : z);
                     if (len2 > 0 && first < 0) continue;
-                    C19[n][0] = x; C19[n][1] = y; C19[n][2] = z; ++n;
-                    if (len2 > 0) { C19[n][0] = -x; C19[n][1] = -y; C19[n][2] = -z; ++n; }
+                    C[n][0] = x; C[n][1] = y; C[n][2] = z; ++n;
+                    if (len2 > 0) { C[n][0] = -x; C[n][1] = -y; C[n][2] = -z; ++n; }
                 }
-    if (n != Q19) return -1;
+    return n;
+}
+
+static int opposites(int Q, const int (*C)[3], int* opp)
+{
+    for (int q = 0; q < Q; ++q) {
+        opp[q] = -1;
+        for (int p = 0; p < Q; ++p)
+            if (C[p][0] == -C[q][0] && C[p][1] == -C[q][1] && C[p][2] == -C[q][2]) opp[q] = p;
+        if (opp[q] < 0) return -1;
+    }
+    return 0;
+}
+
+static int build_tables(void)
+{
+    if (tables_ready) return 0;
+    /* R1 */
+    if (velocity_set(3, C19) != Q19) return -1;
     for (int q = 0; q < Q19; ++q) {
         int l2 = C19[q][0] * C19[q][0] + C19[q][1] * C19[q][1] + C19[q][2] * C19[q][2];
         W19[q] = l2 == 0 ? 1.0 / 3.0 : (l2 == 1 ? 1.0 / 18.0 : 1.0 / 36.0);
-        OPP19[q] = -1;
-        for (int p = 0; p < Q19; ++p)
-            if (C19[p][0] == -C19[q][0] && C19[p][1] == -C19[q][1] && C19[p][2] == -C19[q][2])
-                OPP19[q] = p;
-        if (OPP19[q] < 0) return -1;
     }
+    if (opposites(Q19, (const int (*)[3])C19, OPP19)) return -1;
     double mrow[Q19];
     for (int q = 0; q < Q19; ++q) {
         moment_row_values(C19[q], mrow);
@@ -250,15 +331,51 @@ static int build_tables(void)
         for (int a = 0; a < 3; ++a) C7[k][a] = c7[k][a];
         for (int j = 0; j < Q7; ++j) N7[k][j] = n7[k][j];
     }
-    for (int k = 0; k < Q7; ++k) {
-        OPP7[k] = -1;
-        for (int p = 0; p < Q7; ++p)
-            if (C7[p][0] == -C7[k][0] && C7[p][1] == -C7[k][1] && C7[p][2] == -C7[k][2]) OPP7[k] = p;
-    }
+    if (opposites(Q7, (const int (*)[3])C7, OPP7)) return -1;
     if (invert(Q7, &N7[0][0], &NINV7[0][0])) return -1;
+
+    /* R14: D2Q9 */
+    if (velocity_set(2, C9) != Q9) return -1;
+    for (int q = 0; q < Q9; ++q) {
+        int l2 = C9[q][0] * C9[q][0] + C9[q][1] * C9[q][1];
+        W9[q] = l2 == 0 ? 4.0 / 9.0 : (l2 == 1 ? 1.0 / 9.0 : 1.0 / 36.0);
+    }
+    if (opposites(Q9, (const int (*)[3])C9, OPP9)) return -1;
+    double mrow9[Q9];
+    for (int q = 0; q < Q9; ++q) {
+        moment_row_values_2d(C9[q], mrow9);
+        for (int k = 0; k < Q9; ++k) M9[k][q] = mrow9[k];
+    }
+    if (invert(Q9, &M9[0][0], &MINV9[0][0])) return -1;
+
+    /* R15: D2Q5 */
+    static const int c5[Q5][3] = {{0, 0, 0}, {1, 0, 0}, {-1, 0, 0}, {0, 1, 0}, {0, -1, 0}};
+    static const double n5[Q5][Q5] = {
+        {1, 1, 1, 1, 1},
+        {0, 1, -1, 0, 0},
+        {0, 0, 0, 1, -1},
+        {-4, 1, 1, 1, 1},
+        {0, 1, 1, -1, -1}};
+    for (int k = 0; k < Q5; ++k) {
+        for (int a = 0; a < 3; ++a) C5[k][a] = c5[k][a];
+        for (int j = 0; j < Q5; ++j) N5[k][j] = n5[k][j];
+    }
+    if (opposites(Q5, (const int (*)[3])C5, OPP5)) return -1;
+    if (invert(Q5, &N5[0][0], &NINV5[0][0])) return -1;
+
+    LAT3 = (lattice){Q19, (const int (*)[3])C19, W19, OPP19, &M19[0][0], &MINV19[0][0],
+                     Q7, (const int (*)[3])C7, OPP7, &N7[0][0], &NINV7[0][0], 6.0, 21.0};
+    LAT2 = (lattice){Q9, (const int (*)[3])C9, W9, OPP9, &M9[0][0], &MINV9[0][0],
+                     Q5, (const int (*)[3])C5, OPP5, &N5[0][0], &NINV5[0][0], 4.0, 10.0};
     tables_ready = 1;
     return 0;
 }
+
+static const lattice* lattice_of(const oracle_params* p) { return p->lattice == 1 ? &LAT2 : &LAT3; }
+
+/* The flow and temperature rates of the lattice in use. */
+static const double* flow_rates(const oracle_params* p) { return p->lattice == 1 ? p->s9 : p->s19; }
+static const double* temp_rates(const oracle_params* p) { return p->lattice == 1 ? p->s5 : p->s7; }
 
 /* Export the tables so that tests can pin them against closed forms. */
 int oracle_tables(int32_t* c19, double* w19, int32_t* opp19, double* m19, double* minv19,
@@ -285,6 +402,31 @@ int oracle_tables(int32_t* c19, double* w19, int32_t* opp19, double* m19, double
     return 0;
 }
 
+/* The same for the two-dimensional pair (D2Q9, D2Q5). */
+int oracle_tables_2d(int32_t* c9, double* w9, int32_t* opp9, double* m9, double* minv9,
+                     int32_t* c5, int32_t* opp5, double* n5, double* ninv5)
+{
+    if (build_tables()) return -1;
+    for (int q = 0; q < Q9; ++q) {
+        for (int a = 0; a < 3; ++a) c9[q * 3 + a] = C9[q][a];
+        w9[q] = W9[q];
+        opp9[q] = OPP9[q];
+        for (int k = 0; k < Q9; ++k) {
+            m9[q * Q9 + k] = M9[q][k];
+            minv9[q * Q9 + k] = MINV9[q][k];
+        }
+    }
+    for (int k = 0; k < Q5; ++k) {
+        for (int a = 0; a < 3; ++a) c5[k * 3 + a] = C5[k][a];
+        opp5[k] = OPP5[k];
+        for (int j = 0; j < Q5; ++j) {
+            n5[k * Q5 + j] = N5[k][j];
+            ninv5[k * Q5 + j] = NINV5[k][j];
+        }
+    }
+    return 0;
+}
+
 /* ---------------------------------------------------------------- one cell */
 
 /* Macroscopic values of the pre-collision state ([TL] Sec. 2):
@@ -293,14 +435,15 @@ int oracle_tables(int32_t* c19, double* w19, int32_t* opp19, double* m19, double
 static void macros(const oracle_params* p, const double* f, const double* g,
                    double* rho_out, double* u, double* T_out, double* F)
 {
+    const lattice* L = lattice_of(p);
     double rho = 0.0, j[3] = {0.0, 0.0, 0.0};
-    for (int q = 0; q < Q19; ++q) {
+    for (int q = 0; q < L->Q; ++q) {
         rho += f[q];
-        for (int a = 0; a < 3; ++a) j[a] += C19[q][a] * f[q];
+        for (int a = 0; a < 3; ++a) j[a] += L->C[q][a] * f[q];
     }
     double T = 0.0;
     if (p->thermal)
-        for (int k = 0; k < Q7; ++k) T += g[k];
+        for (int k = 0; k < L->QT; ++k) T += g[k];
     for (int a = 0; a < 3; ++a) {
         F[a] = rho * p->accel[a];
         if (p->thermal) F[a] += rho * p->gbeta[a] * (T - p->T0);
@@ -310,69 +453,79 @@ static void macros(const oracle_params* p, const double* f, const double* g,
     *T_out = T;
 }
 
-static void f_equilibrium(double rho, const double* u, double* feq)
+static void f_equilibrium(const lattice* L, double rho, const double* u, double* feq)
 {
     double uu = u[0] * u[0] + u[1] * u[1] + u[2] * u[2];
-    for (int q = 0; q < Q19; ++q) {
-        double cu = C19[q][0] * u[0] + C19[q][1] * u[1] + C19[q][2] * u[2];
-        feq[q] = W19[q] * rho * (1.0 + 3.0 * cu + 4.5 * cu * cu - 1.5 * uu);
+    for (int q = 0; q < L->Q; ++q) {
+        double cu = L->C[q][0] * u[0] + L->C[q][1] * u[1] + L->C[q][2] * u[2];
+        feq[q] = L->W[q] * rho * (1.0 + 3.0 * cu + 4.5 * cu * cu - 1.5 * uu);
     }
 }
 
+/* R6 (D3Q7) and R15 (D2Q5): (T, u T, a_T T, 0, ...) */
 static void g_equilibrium_moments(const oracle_params* p, double T, const double* u, double* neq)
 {
+    const lattice* L = lattice_of(p);
+    int dims = L->QT == Q7 ? 3 : 2;
+    for (int k = 0; k < L->QT; ++k) neq[k] = 0.0;
     neq[0] = T;
-    neq[1] = u[0] * T;
-    neq[2] = u[1] * T;
-    neq[3] = u[2] * T;
-    neq[4] = p->a_T * T;
-    neq[5] = 0.0;
-    neq[6] = 0.0;
+    for (int a = 0; a < dims; ++a) neq[1 + a] = u[a] * T;
+    neq[1 + dims] = p->a_T * T;
 }
 
-/* One cell's collision ([TL] Eq. 5-7 with the readings R2-R6). */
+static void g_from_moments(const lattice* L, const double* n, double* g)
+{
+    for (int k = 0; k < L->QT; ++k) {
+        g[k] = 0.0;
+        for (int j = 0; j < L->QT; ++j) g[k] += L->NINV[k * L->QT + j] * n[j];
+    }
+}
+
+/* One cell's collision ([TL] Eq. 5-7 with the readings R2-R6, R14-R15). */
 static void collide_cell(const oracle_params* p, const double* f, const double* g,
                          double* fpost, double* gpost, double* mac)
 {
+    const lattice* L = lattice_of(p);
+    const int Q = L->Q;
+    const double* s = flow_rates(p);
     double rho, u[3], T, F[3];
     macros(p, f, g, &rho, u, &T, F);
 
     double feq[Q19], Ft[Q19];
-    f_equilibrium(rho, u, feq);
-    for (int q = 0; q < Q19; ++q) {
-        double cu = C19[q][0] * u[0] + C19[q][1] * u[1] + C19[q][2] * u[2];
-        double s = 0.0;
-        for (int a = 0; a < 3; ++a) s += (3.0 * (C19[q][a] - u[a]) + 9.0 * cu * C19[q][a]) * F[a];
-        Ft[q] = W19[q] * s;
+    f_equilibrium(L, rho, u, feq);
+    for (int q = 0; q < Q; ++q) {
+        double cu = L->C[q][0] * u[0] + L->C[q][1] * u[1] + L->C[q][2] * u[2];
+        double sum = 0.0;
+        for (int a = 0; a < 3; ++a) sum += (3.0 * (L->C[q][a] - u[a]) + 9.0 * cu * L->C[q][a]) * F[a];
+        Ft[q] = L->W[q] * sum;
     }
     double m[Q19], meq[Q19], mF[Q19], mstar[Q19];
-    for (int k = 0; k < Q19; ++k) {
+    for (int k = 0; k < Q; ++k) {
         m[k] = meq[k] = mF[k] = 0.0;
-        for (int q = 0; q < Q19; ++q) {
-            m[k] += M19[k][q] * f[q];
-            meq[k] += M19[k][q] * feq[q];
-            mF[k] += M19[k][q] * Ft[q];
+        for (int q = 0; q < Q; ++q) {
+            m[k] += L->M[k * Q + q] * f[q];
+            meq[k] += L->M[k * Q + q] * feq[q];
+            mF[k] += L->M[k * Q + q] * Ft[q];
         }
     }
-    for (int k = 0; k < Q19; ++k)
-        mstar[k] = m[k] - p->s19[k] * (m[k] - meq[k]) + (1.0 - 0.5 * p->s19[k]) * mF[k];
-    for (int q = 0; q < Q19; ++q) {
+    for (int k = 0; k < Q; ++k)
+        mstar[k] = m[k] - s[k] * (m[k] - meq[k]) + (1.0 - 0.5 * s[k]) * mF[k];
+    for (int q = 0; q < Q; ++q) {
         fpost[q] = 0.0;
-        for (int k = 0; k < Q19; ++k) fpost[q] += MINV19[q][k] * mstar[k];
+        for (int k = 0; k < Q; ++k) fpost[q] += L->MINV[q * Q + k] * mstar[k];
     }
 
     if (p->thermal) {
+        const int QT = L->QT;
+        const double* sT = temp_rates(p);
         double n[Q7], neq[Q7], nstar[Q7];
         g_equilibrium_moments(p, T, u, neq);
-        for (int k = 0; k < Q7; ++k) {
+        for (int k = 0; k < QT; ++k) {
             n[k] = 0.0;
-            for (int j = 0; j < Q7; ++j) n[k] += N7[k][j] * g[j];
+            for (int j = 0; j < QT; ++j) n[k] += L->N[k * QT + j] * g[j];
         }
-        for (int k = 0; k < Q7; ++k) nstar[k] = n[k] - p->s7[k] * (n[k] - neq[k]);
-        for (int k = 0; k < Q7; ++k) {
-            gpost[k] = 0.0;
-            for (int j = 0; j < Q7; ++j) gpost[k] += NINV7[k][j] * nstar[j];
-        }
+        for (int k = 0; k < QT; ++k) nstar[k] = n[k] - sT[k] * (n[k] - neq[k]);
+        g_from_moments(L, nstar, gpost);
     }
     if (mac) {
         mac[0] = rho;
@@ -383,34 +536,34 @@ static void collide_cell(const oracle_params* p, const double* f, const double* 
     }
 }
 
-/* Collide a batch of cells given as cell-major arrays f[n][19], g[n][7].
-   mac[n][5] = (rho, ux, uy, uz, T) of the pre-collision state. */
+/* Collide a batch of cells given as cell-major arrays f[n][Q], g[n][QT]
+   (Q, QT those of the lattice in use).  mac[n][5] = (rho, ux, uy, uz, T) of
+   the pre-collision state. */
 int oracle_collide(const oracle_params* p, int64_t ncells, const double* f, const double* g,
                    double* fpost, double* gpost, double* mac)
 {
     if (build_tables() || !p || ncells < 0) return -1;
     if (p->thermal && (!g || !gpost)) return -1;
+    const lattice* L = lattice_of(p);
     for (int64_t i = 0; i < ncells; ++i)
-        collide_cell(p, f + i * Q19, p->thermal ? g + i * Q7 : NULL, fpost + i * Q19,
-                     p->thermal ? gpost + i * Q7 : NULL, mac ? mac + i * 5 : NULL);
+        collide_cell(p, f + i * L->Q, p->thermal ? g + i * L->QT : NULL, fpost + i * L->Q,
+                     p->thermal ? gpost + i * L->QT : NULL, mac ? mac + i * 5 : NULL);
     return 0;
 }
 
-/* Equilibria for a batch of (rho, u, T): feq[n][19], geq[n][7] (R7). */
+/* Equilibria for a batch of (rho, u, T): feq[n][Q], geq[n][QT] (R7). */
 int oracle_equilibrium(const oracle_params* p, int64_t ncells, const double* rho, const double* u,
                        const double* T, double* feq, double* geq)
 {
     if (build_tables() || !p) return -1;
+    const lattice* L = lattice_of(p);
     for (int64_t i = 0; i < ncells; ++i) {
         double uu[3] = {u[i * 3], u[i * 3 + 1], u[i * 3 + 2]};
-        f_equilibrium(rho[i], uu, feq + i * Q19);
+        f_equilibrium(L, rho[i], uu, feq + i * L->Q);
         if (geq) {
             double neq[Q7];
             g_equilibrium_moments(p, T ? T[i] : 0.0, uu, neq);
-            for (int k = 0; k < Q7; ++k) {
-                geq[i * Q7 + k] = 0.0;
-                for (int j = 0; j < Q7; ++j) geq[i * Q7 + k] += NINV7[k][j] * neq[j];
-            }
+            g_from_moments(L, neq, geq + i * L->QT);
         }
     }
     return 0;
@@ -540,6 +693,11 @@ int oracle_run(const oracle_params* p, const uint8_t* labels, const int32_t* win
     }
     if (nsteps < 0) return -1;
     if (diag && ngroups < 6) return -1;
+    /* R14: the two-dimensional lattices live on one periodic z layer */
+    if (p->lattice != 0 && p->lattice != 1) return -1;
+    if (p->lattice == 1 && (w.N[2] != 1 || p->face_kind[4] != PERIODIC || p->face_kind[5] != PERIODIC)) return -1;
+    const lattice* L = lattice_of(p);
+    const int Q = L->Q, QT = L->QT;
     /* R13: the first layer of a slip face holds no solid */
     if (labels) {
         for (int f = 0; f < 6; ++f) {
@@ -563,10 +721,10 @@ int oracle_run(const oracle_params* p, const uint8_t* labels, const int32_t* win
     (void)nthreads;
 #endif
 
-    double* f = (double*)malloc(sizeof(double) * Q19 * n);
-    double* fp = (double*)malloc(sizeof(double) * Q19 * n);
-    double* g = th ? (double*)malloc(sizeof(double) * Q7 * n) : NULL;
-    double* gp = th ? (double*)malloc(sizeof(double) * Q7 * n) : NULL;
+    double* f = (double*)malloc(sizeof(double) * Q * n);
+    double* fp = (double*)malloc(sizeof(double) * Q * n);
+    double* g = th ? (double*)malloc(sizeof(double) * QT * n) : NULL;
+    double* gp = th ? (double*)malloc(sizeof(double) * QT * n) : NULL;
     uint8_t* solid = (uint8_t*)malloc(n);
     double* uc = (double*)malloc(sizeof(double) * 3 * n); /* each cell's velocity in its last collision */
     if (!f || !fp || (th && (!g || !gp)) || !solid || !uc) {
@@ -581,26 +739,23 @@ int oracle_run(const oracle_params* p, const uint8_t* labels, const int32_t* win
         local_to_global(&w, l, gc);
         solid[l] = (uint8_t)is_solid(labels, w.N, gc);
         if (solid[l]) {
-            for (int q = 0; q < Q19; ++q) f[q * n + l] = nan;
-            if (th) for (int k = 0; k < Q7; ++k) g[k * n + l] = nan;
+            for (int q = 0; q < Q; ++q) f[q * n + l] = nan;
+            if (th) for (int k = 0; k < QT; ++k) g[k * n + l] = nan;
             continue;
         }
         if (f0) {
-            for (int q = 0; q < Q19; ++q) f[q * n + l] = f0[q * n + l];
-            if (th) for (int k = 0; k < Q7; ++k) g[k * n + l] = g0[k * n + l];
+            for (int q = 0; q < Q; ++q) f[q * n + l] = f0[q * n + l];
+            if (th) for (int k = 0; k < QT; ++k) g[k * n + l] = g0[k * n + l];
         } else {
             double uu[3] = {u0[l], u0[n + l], u0[2 * n + l]};
             double feq[Q19];
-            f_equilibrium(rho0[l], uu, feq);
-            for (int q = 0; q < Q19; ++q) f[q * n + l] = feq[q];
+            f_equilibrium(L, rho0[l], uu, feq);
+            for (int q = 0; q < Q; ++q) f[q * n + l] = feq[q];
             if (th) {
-                double neq[Q7];
+                double neq[Q7], geq[Q7];
                 g_equilibrium_moments(p, T0[l], uu, neq);
-                for (int k = 0; k < Q7; ++k) {
-                    double s = 0.0;
-                    for (int j = 0; j < Q7; ++j) s += NINV7[k][j] * neq[j];
-                    g[k * n + l] = s;
-                }
+                g_from_moments(L, neq, geq);
+                for (int k = 0; k < QT; ++k) g[k * n + l] = geq[k];
             }
         }
     }
@@ -619,17 +774,17 @@ int oracle_run(const oracle_params* p, const uint8_t* labels, const int32_t* win
         for (int64_t l = 0; l < n; ++l) {
             double fl[Q19], gl[Q7], fo[Q19], go[Q7];
             if (solid[l]) {
-                for (int q = 0; q < Q19; ++q) fp[q * n + l] = nan;
-                if (th) for (int k = 0; k < Q7; ++k) gp[k * n + l] = nan;
+                for (int q = 0; q < Q; ++q) fp[q * n + l] = nan;
+                if (th) for (int k = 0; k < QT; ++k) gp[k * n + l] = nan;
                 continue;
             }
-            for (int q = 0; q < Q19; ++q) fl[q] = f[q * n + l];
-            if (th) for (int k = 0; k < Q7; ++k) gl[k] = g[k * n + l];
+            for (int q = 0; q < Q; ++q) fl[q] = f[q * n + l];
+            if (th) for (int k = 0; k < QT; ++k) gl[k] = g[k * n + l];
             double mac[5];
             collide_cell(p, fl, th ? gl : NULL, fo, th ? go : NULL, mac);
             for (int a = 0; a < 3; ++a) uc[a * n + l] = mac[1 + a];
-            for (int q = 0; q < Q19; ++q) fp[q * n + l] = fo[q];
-            if (th) for (int k = 0; k < Q7; ++k) gp[k * n + l] = go[k];
+            for (int q = 0; q < Q; ++q) fp[q * n + l] = fo[q];
+            if (th) for (int k = 0; k < QT; ++k) gp[k * n + l] = go[k];
         }
         if (part) memset(part, 0, sizeof(double) * (size_t)w.n[2] * ngroups * 4);
 
@@ -641,19 +796,19 @@ int oracle_run(const oracle_params* p, const uint8_t* labels, const int32_t* win
                 if (solid[l]) continue;
                 int64_t gc[3];
                 local_to_global(&w, l, gc);
-                for (int q = 0; q < Q19; ++q) {
-                    int o = OPP19[q];
+                for (int q = 0; q < Q; ++q) {
+                    int o = L->OPP[q];
                     int rule = WALL, axis = 0;
-                    int grp = face_rule(p, w.N, gc, C19[o], &rule, &axis);
-                    if (grp < 0) grp = blocked_group(p, labels, w.N, gc, C19[o]); /* a solid: WALL */
+                    int grp = face_rule(p, w.N, gc, L->C[o], &rule, &axis);
+                    if (grp < 0) grp = blocked_group(p, labels, w.N, gc, L->C[o]); /* a solid: WALL */
                     if (grp >= 0 && rule == SLIP) {
                         /* R10 SLIP: q arrives from y = x - c_t, sent along q with its normal
                            component reversed (the tangential part c_t of c_q is kept) */
                         int pr = -1, ct[3];
-                        for (int a = 0; a < 3; ++a) ct[a] = a == axis ? 0 : C19[q][a];
-                        for (int r = 0; r < Q19; ++r)
-                            if (C19[r][axis] == -C19[q][axis] && C19[r][(axis + 1) % 3] == C19[q][(axis + 1) % 3] &&
-                                C19[r][(axis + 2) % 3] == C19[q][(axis + 2) % 3])
+                        for (int a = 0; a < 3; ++a) ct[a] = a == axis ? 0 : L->C[q][a];
+                        for (int r = 0; r < Q; ++r)
+                            if (L->C[r][axis] == -L->C[q][axis] && L->C[r][(axis + 1) % 3] == L->C[q][(axis + 1) % 3] &&
+                                L->C[r][(axis + 2) % 3] == L->C[q][(axis + 2) % 3])
                                 pr = r;
                         int64_t src[3];
                         for (int a = 0; a < 3; ++a) src[a] = wrap_coord(gc[a] - ct[a], w.N[a]);
@@ -661,42 +816,42 @@ int oracle_run(const oracle_params* p, const uint8_t* labels, const int32_t* win
                         double v = ls >= 0 ? fp[pr * n + ls] : nan;
                         f[q * n + l] = v;
                         if (pd && grp < ngroups)
-                            for (int a = 0; a < 3; ++a) pd[grp * 4 + a] += (C19[pr][a] - C19[q][a]) * v;
+                            for (int a = 0; a < 3; ++a) pd[grp * 4 + a] += (L->C[pr][a] - L->C[q][a]) * v;
                     } else if (grp >= 0) {
                         /* the population x sent along c_o comes back along c_q (R10) */
                         double v = fp[o * n + l], vin = v;
                         if (rule == VELOCITY) {
                             double cu = 0.0;
-                            for (int a = 0; a < 3; ++a) cu += C19[o][a] * p->face_u[3 * grp + a];
-                            vin = v - 6.0 * W19[o] * p->face_rho[grp] * cu;
+                            for (int a = 0; a < 3; ++a) cu += L->C[o][a] * p->face_u[3 * grp + a];
+                            vin = v - 6.0 * L->W[o] * p->face_rho[grp] * cu;
                         } else if (rule == PRESSURE) {
                             double cu = 0.0, uu = 0.0;
                             for (int a = 0; a < 3; ++a) {
                                 double ua = uc[a * n + l];
-                                cu += C19[o][a] * ua;
+                                cu += L->C[o][a] * ua;
                                 uu += ua * ua;
                             }
-                            vin = -v + 2.0 * W19[o] * p->face_rho[grp] * (1.0 + 4.5 * cu * cu - 1.5 * uu);
+                            vin = -v + 2.0 * L->W[o] * p->face_rho[grp] * (1.0 + 4.5 * cu * cu - 1.5 * uu);
                         }
                         f[q * n + l] = vin;
                         /* R9: momentum out along c_o minus momentum back along c_q = -c_o */
                         if (pd && grp < ngroups)
-                            for (int a = 0; a < 3; ++a) pd[grp * 4 + a] += C19[o][a] * (v + vin);
+                            for (int a = 0; a < 3; ++a) pd[grp * 4 + a] += L->C[o][a] * (v + vin);
                     } else {
                         int64_t src[3];
-                        for (int a = 0; a < 3; ++a) src[a] = wrap_coord(gc[a] - C19[q][a], w.N[a]);
+                        for (int a = 0; a < 3; ++a) src[a] = wrap_coord(gc[a] - L->C[q][a], w.N[a]);
                         int64_t ls = global_to_local(&w, src);
                         f[q * n + l] = ls >= 0 ? fp[q * n + ls] : nan;
                     }
                 }
                 if (th) {
-                    for (int k = 0; k < Q7; ++k) {
-                        int o = OPP7[k];
-                        int grp = blocked_group(p, labels, w.N, gc, C7[o]);
+                    for (int k = 0; k < QT; ++k) {
+                        int o = L->OPPT[k];
+                        int grp = blocked_group(p, labels, w.N, gc, L->CT[o]);
                         if (grp >= 0) {
                             double v = gp[o * n + l];
                             if (wall_is_dirichlet(p, grp)) {
-                                double omega = (6.0 + p->a_T) / 21.0;
+                                double omega = (L->wnum + p->a_T) / L->wden;
                                 double tw = wall_temperature(p, grp);
                                 g[k * n + l] = -v + omega * tw;
                                 if (pd && grp < ngroups) pd[grp * 4 + 3] += omega * tw - 2.0 * v;
@@ -705,7 +860,7 @@ int oracle_run(const oracle_params* p, const uint8_t* labels, const int32_t* win
                             }
                         } else {
                             int64_t src[3];
-                            for (int a = 0; a < 3; ++a) src[a] = wrap_coord(gc[a] - C7[k][a], w.N[a]);
+                            for (int a = 0; a < 3; ++a) src[a] = wrap_coord(gc[a] - L->CT[k][a], w.N[a]);
                             int64_t ls = global_to_local(&w, src);
                             g[k * n + l] = ls >= 0 ? gp[k * n + ls] : nan;
                         }
@@ -726,8 +881,8 @@ int oracle_run(const oracle_params* p, const uint8_t* labels, const int32_t* win
         double r = nan, uu[3] = {nan, nan, nan}, t = nan, F[3];
         if (!solid[l]) {
             double fl[Q19], gl[Q7];
-            for (int q = 0; q < Q19; ++q) fl[q] = f[q * n + l];
-            if (th) for (int k = 0; k < Q7; ++k) gl[k] = g[k * n + l];
+            for (int q = 0; q < Q; ++q) fl[q] = f[q * n + l];
+            if (th) for (int k = 0; k < QT; ++k) gl[k] = g[k * n + l];
             macros(p, fl, th ? gl : NULL, &r, uu, &t, F);
             if (!th) t = 0.0;
         }
@@ -735,8 +890,8 @@ int oracle_run(const oracle_params* p, const uint8_t* labels, const int32_t* win
         if (u) { u[l] = uu[0]; u[n + l] = uu[1]; u[2 * n + l] = uu[2]; }
         if (T) T[l] = t;
     }
-    if (f_out) memcpy(f_out, f, sizeof(double) * Q19 * n);
-    if (g_out && th) memcpy(g_out, g, sizeof(double) * Q7 * n);
+    if (f_out) memcpy(f_out, f, sizeof(double) * Q * n);
+    if (g_out && th) memcpy(g_out, g, sizeof(double) * QT * n);
 
     free(part);
     free(f); free(fp); free(g); free(gp); free(solid); free(uc);
@@ -746,4 +901,6 @@ int oracle_run(const oracle_params* p, const uint8_t* labels, const int32_t* win
 /* Velocity-set sizes, for the ctypes wrapper's sanity checks. */
 int oracle_q19(void) { return Q19; }
 int oracle_q7(void) { return Q7; }
+int oracle_q9(void) { return Q9; }
+int oracle_q5(void) { return Q5; }
 int oracle_max_groups(void) { return MAXGROUPS; }

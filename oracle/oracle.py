@@ -19,6 +19,8 @@ _SO = os.path.join(_HERE, "liboracle.so")
 
 Q19 = 19
 Q7 = 7
+Q9 = 9
+Q5 = 5
 MAX_GROUPS = 261  # 6 faces + 255 solid labels
 
 
@@ -44,6 +46,10 @@ class OracleParams(ctypes.Structure):
         ("T0", ctypes.c_double),
         ("face_u", ctypes.c_double * 18),
         ("face_rho", ctypes.c_double * 6),
+        ("lattice", ctypes.c_int32),
+        ("pad1", ctypes.c_int32),
+        ("s9", ctypes.c_double * 9),
+        ("s5", ctypes.c_double * 5),
     ]
 
 
@@ -76,6 +82,8 @@ def _lib():
         ip = ctypes.POINTER(ctypes.c_int32)
         lib.oracle_tables.argtypes = [ip, dp, ip, dp, dp, ip, ip, dp, dp]
         lib.oracle_tables.restype = ctypes.c_int
+        lib.oracle_tables_2d.argtypes = [ip, dp, ip, dp, dp, ip, ip, dp, dp]
+        lib.oracle_tables_2d.restype = ctypes.c_int
         lib.oracle_collide.argtypes = [ctypes.POINTER(OracleParams), ctypes.c_int64, dp, dp, dp, dp, dp]
         lib.oracle_collide.restype = ctypes.c_int
         lib.oracle_equilibrium.argtypes = [ctypes.POINTER(OracleParams), ctypes.c_int64, dp, dp, dp, dp, dp]
@@ -111,10 +119,6 @@ def to_params(d: dict) -> OracleParams:
         p.face_T[i] = float(d.get("face_T", [0.0] * 6)[i])
     p.solid_thermal = int(d.get("solid_thermal", 0))
     p.solid_T = float(d.get("solid_T", 0.0))
-    for i in range(19):
-        p.s19[i] = float(d["s19"][i])
-    for i in range(7):
-        p.s7[i] = float(d.get("s7", [0.0] * 7)[i])
     p.a_T = float(d.get("a_T", 0.0))
     for i in range(3):
         p.accel[i] = float(d.get("accel", [0.0] * 3)[i])
@@ -126,7 +130,23 @@ def to_params(d: dict) -> OracleParams:
         p.face_u[i] = float(fu[i])
     for i in range(6):
         p.face_rho[i] = float(fr[i])
+    p.lattice = int(d.get("lattice", 0))
+    if p.lattice == 0:
+        for i in range(19):
+            p.s19[i] = float(d["s19"][i])
+        for i in range(7):
+            p.s7[i] = float(d.get("s7", [0.0] * 7)[i])
+    else:
+        for i in range(9):
+            p.s9[i] = float(d["s9"][i])
+        for i in range(5):
+            p.s5[i] = float(d.get("s5", [0.0] * 5)[i])
     return p
+
+
+def lattice_sizes(params: dict) -> tuple:
+    """(Q, QT): velocities of the flow and temperature lattices in use."""
+    return (Q9, Q5) if int(params.get("lattice", 0)) == 1 else (Q19, Q7)
 
 
 def tables() -> dict:
@@ -149,8 +169,30 @@ def tables() -> dict:
     return dict(c19=c19, w19=w19, opp19=opp19, M=m19, Minv=minv19, c7=c7, opp7=opp7, N=n7, Ninv=ninv7)
 
 
+def tables_2d() -> dict:
+    """The two-dimensional pair (D2Q9, D2Q5) as the oracle built it."""
+    lib = _lib()
+    c9 = np.zeros((Q9, 3), np.int32)
+    w9 = np.zeros(Q9)
+    opp9 = np.zeros(Q9, np.int32)
+    m9 = np.zeros((Q9, Q9))
+    minv9 = np.zeros((Q9, Q9))
+    c5 = np.zeros((Q5, 3), np.int32)
+    opp5 = np.zeros(Q5, np.int32)
+    n5 = np.zeros((Q5, Q5))
+    ninv5 = np.zeros((Q5, Q5))
+    ip = ctypes.POINTER(ctypes.c_int32)
+    rc = lib.oracle_tables_2d(c9.ctypes.data_as(ip), _dp(w9), opp9.ctypes.data_as(ip), _dp(m9),
+                              _dp(minv9), c5.ctypes.data_as(ip), opp5.ctypes.data_as(ip), _dp(n5), _dp(ninv5))
+    if rc:
+        raise RuntimeError("oracle_tables_2d failed")
+    return dict(c9=c9, w9=w9, opp9=opp9, M=m9, Minv=minv9, c5=c5, opp5=opp5, N=n5, Ninv=ninv5)
+
+
 def collide(params: dict, f, g=None):
-    """Collide cells given cell-major: f[n,19], g[n,7].  Returns (fpost, gpost, mac[n,5])."""
+    """Collide cells given cell-major: f[n,Q], g[n,QT] (19 and 7, or 9 and 5).
+
+    Returns (fpost, gpost, mac[n,5])."""
     p = to_params(params)
     f = _f64(np.atleast_2d(f))
     n = f.shape[0]
@@ -167,13 +209,14 @@ def collide(params: dict, f, g=None):
 
 
 def equilibrium(params: dict, rho, u, T=None):
-    """f_eq[n,19] (and g_eq[n,7]) for cell-major rho[n], u[n,3], T[n]."""
+    """f_eq[n,Q] (and g_eq[n,QT]) for cell-major rho[n], u[n,3], T[n]."""
     p = to_params(params)
+    Q, QT = lattice_sizes(params)
     rho = _f64(np.atleast_1d(rho))
     u = _f64(np.atleast_2d(u))
     n = rho.shape[0]
-    feq = np.zeros((n, Q19))
-    geq = np.zeros((n, Q7)) if T is not None else None
+    feq = np.zeros((n, Q))
+    geq = np.zeros((n, QT)) if T is not None else None
     T = _f64(np.atleast_1d(T)) if T is not None else None
     rc = _lib().oracle_equilibrium(ctypes.byref(p), n, _dp(rho), _dp(u), _dp(T), _dp(feq), _dp(geq))
     if rc:
@@ -189,9 +232,10 @@ def run(params: dict, nsteps: int, rho0=None, u0=None, T0=None, labels=None, win
     window: ((lo_x, lo_y, lo_z), (n_x, n_y, n_z)) or None for the whole box.
     rho0/u0/T0 are window-local fields (u0 shaped [3, cells]); labels is the
     full box (uint8, 0 = fluid).  Returns a dict with rho, u[3,cells], T and
-    optionally f[19,cells], g[7,cells], diag[nsteps, ngroups, 4].
+    optionally f[Q,cells], g[QT,cells], diag[nsteps, ngroups, 4].
     """
     p = to_params(params)
+    Q, QT = lattice_sizes(params)
     N = (p.nx, p.ny, p.nz)
     if window is None:
         lo, wn = (0, 0, 0), N
@@ -215,14 +259,14 @@ def run(params: dict, nsteps: int, rho0=None, u0=None, T0=None, labels=None, win
         if p.thermal:
             assert T0 is not None and T0.size == cells
     else:
-        assert f0.size == Q19 * cells
+        assert f0.size == Q * cells
         if p.thermal:
-            assert g0 is not None and g0.size == Q7 * cells
+            assert g0 is not None and g0.size == QT * cells
     rho = np.zeros(cells)
     u = np.zeros((3, cells))
     T = np.zeros(cells)
-    fo = np.zeros((Q19, cells)) if want_populations else None
-    go = np.zeros((Q7, cells)) if (want_populations and p.thermal) else None
+    fo = np.zeros((Q, cells)) if want_populations else None
+    go = np.zeros((QT, cells)) if (want_populations and p.thermal) else None
     diag = np.zeros((max(nsteps, 0), ngroups, 4)) if want_diag else None
     rc = _lib().oracle_run(ctypes.byref(p), lab_ptr, lo_a, wn_a, _dp(rho0), _dp(u0), _dp(T0), _dp(f0),
                            _dp(g0), int(nsteps), _dp(rho), _dp(u), _dp(T), _dp(fo), _dp(go), _dp(diag),
