@@ -29,8 +29,8 @@ METRIC = "MLUPS and achieved HBM TB/s, D3Q19(+D3Q7) fp32 AA step, 128³–512³,
 HBM_PEAK_GBPS = 8000.0
 
 # algorithmic bytes per cell update: every population read once and written once
-def bytes_per_cell(thermal: bool, dtype: int, streaming: int) -> int:
-    q = 19 + (7 if thermal else 0)
+def bytes_per_cell(thermal: bool, dtype: int, streaming: int, two_d: bool = False) -> int:
+    q = (9 + (5 if thermal else 0)) if two_d else (19 + (7 if thermal else 0))
     passes = 2 if streaming == 2 else 1  # two-buffer: collide in place, then pull
     return 2 * q * dtype * passes
 
@@ -46,6 +46,9 @@ WORKLOAD_INFO = {
     "tg32": "D3Q19 MRT, 32^3 periodic Taylor-Green, tau=0.6",
     "channel256": "D3Q19 MRT, 256x128x128 open channel: x- velocity inlet U=0.05, x+ pressure outlet rho=1, "
                   "free-slip y/z faces, solid sphere R=16 at (64,64,64), tau=0.52",
+    "cavity2d": "thermal D2Q9+D2Q5 MRT, 8193x8193 square cell, x- hot/x+ cold, adiabatic y faces, no-slip, "
+                "Ra=1e8, Pr=0.71, buoyancy +y (the thermal-LBM page's 2D case; it runs fp64)",
+    "tg2d": "D2Q9 MRT, 256x256 periodic Taylor-Green, tau=0.6",
 }
 
 
@@ -169,8 +172,10 @@ def main(argv=None):
     ms_per_step = ms / args.steps
     mlups = w.cells * args.steps / (ms / 1e3) / 1e6
 
-    bpc = bytes_per_cell(thermal, args.dtype, args.streaming)
-    has_links = (solver.num_links(19) + solver.num_links(7)) > 0
+    two_d = int(w.params.get("lattice", 0)) == 1
+    bpc = bytes_per_cell(thermal, args.dtype, args.streaming, two_d)
+    flow, temp = (9, 5) if two_d else (19, 7)
+    has_links = (solver.num_links(flow) + solver.num_links(temp)) > 0
     launches = 1 if args.streaming == 1 else 2
     per_launch_bytes = bpc * w.cells / launches
     # periodic boxes run exactly `launches` bulk kernels per step and nothing else

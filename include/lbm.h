@@ -107,6 +107,27 @@ enum { LBM_MAX_GROUPS = 261 }; /* 6 faces + 255 solid labels */
  * same populations bit for bit; IN_KERNEL moves fewer bytes. */
 enum { LBM_LINKS_IN_KERNEL = 0, LBM_LINKS_PASSES = 1 };
 
+/* Lattice pairs of the double-distribution model ("Multi-GPU thermal
+ * lattice Boltzmann simulations using OpenACC and MPI", Sec. 2: D3Q19 + D3Q7
+ * in three dimensions, D2Q9 + D2Q5 in two, MRT collision on both).
+ *   LBM_LATTICE_3D  D3Q19 flow + D3Q7 temperature; rates s19, s7.
+ *   LBM_LATTICE_2D  D2Q9 flow + D2Q5 temperature on a box with nz = 1 and
+ *                   periodic z faces; rates s9, s5; accel[2], gbeta[2] and
+ *                   the z components of face_u must be 0.  D2Q9 = rest, 4
+ *                   axis and 4 diagonal velocities, weights 4/9, 1/9, 1/36;
+ *                   moment basis of Lallemand and Luo, rows (order of s9):
+ *                     0 rho: 1   1 e: 3c^2-4   2 eps: (9c^4-21c^2+8)/2
+ *                     3 jx: cx   4 qx: (3c^2-5)cx   5 jy   6 qy
+ *                     7 pxx: cx^2-cy^2   8 pxy: cx cy
+ *                   D2Q5 directions (0, +x, -x, +y, -y), rows of N (order of
+ *                   s5): 1, e_x, e_y, (-4,1,1,1,1), (0,1,1,-1,-1);
+ *                   n_eq = (T, ux T, uy T, a_T T, 0); a_T in (-4, 1]; the
+ *                   anti-bounce-back constant is w = (4 + a_T)/10 (Sec. 2).
+ * Forces, heat and diagnostics keep their three components (z = 0 in 2D);
+ * fields keep three velocity planes (uz = 0 in 2D; ignored by
+ * lbm_init_fields). */
+enum { LBM_LATTICE_3D = 0, LBM_LATTICE_2D = 1 };
+
 /* Faces are numbered 0..5 = x-, x+, y-, y+, z-, z+.  Force/heat group g is
  * face g for g < 6 and solid label g - 5 for g >= 6. */
 typedef struct lbm_params {
@@ -128,6 +149,10 @@ typedef struct lbm_params {
     double T0;               /* reference temperature of the buoyancy term */
     double face_u[6][3];     /* wall velocity u_w of each VELOCITY face */
     double face_rho[6];      /* wall density rho_w of each VELOCITY and PRESSURE face, > 0 */
+    int32_t lattice;         /* LBM_LATTICE_3D (0) or LBM_LATTICE_2D (1), see below */
+    int32_t pad1;
+    double s9[9];            /* D2Q9 relaxation rates (LBM_LATTICE_2D), row order below, each in [0, 2) */
+    double s5[5];            /* D2Q5 relaxation rates (LBM_LATTICE_2D), row order below, each in [0, 2) */
 } lbm_params;
 
 typedef struct lbm_ctx lbm_ctx;
@@ -148,7 +173,9 @@ size_t lbm_required_bytes(const lbm_params* p, const uint8_t* solid_labels);
  * hip_stream: a hipStream_t (NULL = the null stream), BORROWED.
  * Host arrays are copied before the call returns.  On failure nothing is kept
  * and *out is NULL.  Errors: LBM_E_INVALID (bad sizes, a rate outside [0, 2),
- * a_T outside (-6, 1], one face of an axis periodic and the other not,
+ * a_T outside (-6, 1] (3D) or (-4, 1] (2D), one face of an axis periodic
+ * and the other not, a 2D box with nz != 1 or non-periodic z faces or a
+ * z component of accel, gbeta or face_u,
  * dtype not 4 or 8, a SLIP, VELOCITY or PRESSURE face with links =
  * LBM_LINKS_PASSES, a solid cell in the first layer of a SLIP face),
  * LBM_E_NOMEM (device_bytes too small), LBM_E_DEVICE. */
@@ -224,13 +251,16 @@ lbm_status lbm_diagnostics(lbm_ctx* ctx, double* out, int32_t n);
 /* Current time step count (number of steps since lbm_init_fields). */
 int64_t lbm_time(const lbm_ctx* ctx);
 
-/* Number of links of the D3Q19 (lattice = 19) or D3Q7 (lattice = 7) list. */
+/* Number of links of the flow lattice's list (lattice = 19 for D3Q19 or 9
+ * for D2Q9) or of the temperature lattice's (7 for D3Q7, 5 for D2Q5); -1
+ * when the number does not name a lattice of this context. */
 int64_t lbm_num_links(const lbm_ctx* ctx, int32_t lattice);
 
 /* Host only (no device work): the number of links lbm_create() would build
- * for these parameters and labels on the D3Q19 (19) or D3Q7 (7) lattice; a
- * link is a fluid cell x and direction p with x + c_p a wall face or a solid
- * cell.  Returns -1 for invalid parameters or lattice. */
+ * for these parameters and labels on the flow lattice (19 or 9) or the
+ * temperature lattice (7 or 5) of p->lattice; a link is a fluid cell x and
+ * direction p with x + c_p a wall face or a solid cell.  Returns -1 for
+ * invalid parameters or lattice. */
 int64_t lbm_count_links(const lbm_params* p, const uint8_t* solid_labels, int32_t lattice);
 
 /* Last error text of this context (or of the last failed lbm_create when ctx

@@ -22,6 +22,7 @@ LBM_OK, LBM_E_INVALID, LBM_E_NOMEM, LBM_E_DEVICE, LBM_E_UNSTABLE = 0, 1, 2, 3, 4
 STATUS_NAMES = {0: "LBM_OK", 1: "LBM_E_INVALID", 2: "LBM_E_NOMEM", 3: "LBM_E_DEVICE", 4: "LBM_E_UNSTABLE"}
 LBM_STREAM_AUTO, LBM_STREAM_AA, LBM_STREAM_AB = 0, 1, 2
 LBM_LINKS_IN_KERNEL, LBM_LINKS_PASSES = 0, 1
+LBM_LATTICE_3D, LBM_LATTICE_2D = 0, 1
 LBM_FACE_PERIODIC, LBM_FACE_WALL, LBM_FACE_SLIP, LBM_FACE_VELOCITY, LBM_FACE_PRESSURE = 0, 1, 2, 3, 4
 MAX_GROUPS = 261
 (LBM_DIAG_FLUID_CELLS, LBM_DIAG_MASS, LBM_DIAG_MOM_X, LBM_DIAG_MOM_Y, LBM_DIAG_MOM_Z, LBM_DIAG_KINETIC,
@@ -48,6 +49,8 @@ class LbmParams(ctypes.Structure):
         ("a_T", ctypes.c_double), ("accel", ctypes.c_double * 3), ("gbeta", ctypes.c_double * 3),
         ("T0", ctypes.c_double),
         ("face_u", ctypes.c_double * 18), ("face_rho", ctypes.c_double * 6),
+        ("lattice", ctypes.c_int32), ("pad1", ctypes.c_int32),
+        ("s9", ctypes.c_double * 9), ("s5", ctypes.c_double * 5),
     ]
 
 
@@ -113,9 +116,14 @@ def to_params(d: dict, dtype: int = 4, streaming: int = LBM_STREAM_AUTO) -> LbmP
     p.links = int(d.get("links", LBM_LINKS_IN_KERNEL))
     p.solid_T = float(d.get("solid_T", 0.0))
     for i in range(19):
-        p.s19[i] = float(d["s19"][i])
+        p.s19[i] = float(d.get("s19", [0.0] * 19)[i])
     for i in range(7):
         p.s7[i] = float(d.get("s7", [0.0] * 7)[i])
+    p.lattice = int(d.get("lattice", LBM_LATTICE_3D))
+    for i in range(9):
+        p.s9[i] = float(d.get("s9", [0.0] * 9)[i])
+    for i in range(5):
+        p.s5[i] = float(d.get("s5", [0.0] * 5)[i])
     p.a_T = float(d.get("a_T", 0.0))
     for i in range(3):
         p.accel[i] = float(d.get("accel", [0.0] * 3)[i])

@@ -22,6 +22,7 @@ struct lbm_ctx {
     int es = 4;
     bool thermal = false;
     bool ab = false;
+    bool two_d = false;  // D2Q9 + D2Q5 on one z layer
     hipStream_t stream = nullptr;
     Geometry geo{};
     char* f = nullptr;
@@ -159,11 +160,26 @@ std::string validate(const lbm_params* p)
         return "SLIP, VELOCITY and PRESSURE faces need links = LBM_LINKS_IN_KERNEL";
     if (p->solid_thermal != LBM_ADIABATIC && p->solid_thermal != LBM_DIRICHLET) return "bad solid_thermal";
     if (!finite(p->solid_T)) return "solid_T must be finite";
-    for (int k = 0; k < 19; ++k)
-        if (!(p->s19[k] >= 0.0 && p->s19[k] < 2.0)) return "s19 rates must lie in [0, 2)";
-    for (int k = 0; k < 7; ++k)
-        if (!(p->s7[k] >= 0.0 && p->s7[k] < 2.0)) return "s7 rates must lie in [0, 2)";
-    if (!(p->a_T > -6.0 && p->a_T <= 1.0)) return "a_T must lie in (-6, 1]";
+    if (p->lattice != LBM_LATTICE_3D && p->lattice != LBM_LATTICE_2D) return "lattice must be 0 (3D) or 1 (2D)";
+    if (p->lattice == LBM_LATTICE_3D) {
+        for (int k = 0; k < 19; ++k)
+            if (!(p->s19[k] >= 0.0 && p->s19[k] < 2.0)) return "s19 rates must lie in [0, 2)";
+        for (int k = 0; k < 7; ++k)
+            if (!(p->s7[k] >= 0.0 && p->s7[k] < 2.0)) return "s7 rates must lie in [0, 2)";
+        if (!(p->a_T > -6.0 && p->a_T <= 1.0)) return "a_T must lie in (-6, 1]";
+    } else {
+        if (p->nz != 1) return "a 2D box (D2Q9 + D2Q5) needs nz = 1";
+        if (p->face_kind[4] != LBM_FACE_PERIODIC || p->face_kind[5] != LBM_FACE_PERIODIC)
+            return "a 2D box needs periodic z faces";
+        for (int k = 0; k < 9; ++k)
+            if (!(p->s9[k] >= 0.0 && p->s9[k] < 2.0)) return "s9 rates must lie in [0, 2)";
+        for (int k = 0; k < 5; ++k)
+            if (!(p->s5[k] >= 0.0 && p->s5[k] < 2.0)) return "s5 rates must lie in [0, 2)";
+        if (!(p->a_T > -4.0 && p->a_T <= 1.0)) return "a_T must lie in (-4, 1] for D2Q5";
+        if (p->accel[2] != 0.0 || p->gbeta[2] != 0.0) return "accel[2] and gbeta[2] must be 0 in 2D";
+        for (int f = 0; f < 6; ++f)
+            if (p->face_u[f][2] != 0.0) return "face_u z components must be 0 in 2D";
+    }
     for (int a = 0; a < 3; ++a)
         if (!finite(p->accel[a]) || !finite(p->gbeta[a])) return "accel and gbeta must be finite";
     if (!finite(p->T0)) return "T0 must be finite";
@@ -202,7 +218,44 @@ Collision<R> make_collision(const lbm_params* p)
     }
     c.T0 = (R)p->T0;
     c.a_T = (R)p->a_T;
+    const double* s2 = p->s9;
+    c.s2_e = (R)s2[1];
+    c.s2_eps = (R)s2[2];
+    c.s2_qx = (R)s2[4];
+    c.s2_qy = (R)s2[6];
+    c.s2_pxx = (R)s2[7];
+    c.s2_pxy = (R)s2[8];
+    c.q2_jx = (R)p->s5[1];
+    c.q2_jy = (R)p->s5[2];
+    c.q2_e = (R)p->s5[3];
+    c.q2_4 = (R)p->s5[4];
     return c;
+}
+
+// Anti-bounce-back constant of the temperature lattice ("Multi-GPU thermal
+// lattice Boltzmann simulations using OpenACC and MPI", Sec. 2):
+// (6 + a_T)/21 for D3Q7, (4 + a_T)/10 for D2Q5.
+double abb_omega(const lbm_params* p)
+{
+    return p->lattice == LBM_LATTICE_2D ? (4.0 + p->a_T) / 10.0 : (6.0 + p->a_T) / 21.0;
+}
+
+// Velocities of the flow (temp = false) or temperature lattice, rest excluded.
+int lattice_dirs(const lbm_params* p, bool temp, int (*c)[3])
+{
+    int n = 0;
+    if (p->lattice == LBM_LATTICE_2D) {
+        if (!temp)
+            for (int q = 1; q < Q9; ++q) c[n][0] = cx9(q), c[n][1] = cy9(q), c[n][2] = 0, ++n;
+        else
+            for (int k = 1; k < Q5; ++k) c[n][0] = cx7(k), c[n][1] = cy7(k), c[n][2] = 0, ++n;
+    } else {
+        if (!temp)
+            for (int q = 1; q < Q19; ++q) c[n][0] = cx19(q), c[n][1] = cy19(q), c[n][2] = cz19(q), ++n;
+        else
+            for (int k = 1; k < Q7; ++k) c[n][0] = cx7(k), c[n][1] = cy7(k), c[n][2] = cz7(k), ++n;
+    }
+    return n;
 }
 
 // Cells of face f (x faces: ny*nz, y faces: nx*nz, z faces: nx*ny).
@@ -230,7 +283,7 @@ template <typename R>
 Bounce<R> make_bounce(const lbm_params* p, bool in_kernel, void* face_vel)
 {
     Bounce<R> b{};
-    const double omega = (6.0 + p->a_T) / 21.0;
+    const double omega = abb_omega(p);
     for (int f = 0; f < 6; ++f) {
         b.face_gw[f] = (R)(omega * p->face_T[f]);
         if (nonperiodic(p, f)) b.walls |= 1 << f;
@@ -301,14 +354,12 @@ inline int blocked_group(const lbm_params* p, const uint8_t* labels, int x, int 
 // index order by several host threads; the result is then ordered by group
 // with a stable counting sort so that wavefronts of the gather pass mostly
 // see a single group.
-int64_t build_links(const lbm_params* p, const uint8_t* labels, bool d3q7, LinkList* out)
+int64_t build_links(const lbm_params* p, const uint8_t* labels, bool temp, LinkList* out)
 {
     std::vector<Dir> dirs;
-    if (!d3q7) {
-        for (int q = 1; q < Q19; ++q) dirs.push_back({{cx19(q), cy19(q), cz19(q)}});
-    } else {
-        for (int k = 1; k < Q7; ++k) dirs.push_back({{cx7(k), cy7(k), cz7(k)}});
-    }
+    int c[Q19][3];
+    const int nd = lattice_dirs(p, temp, c);
+    for (int i = 0; i < nd; ++i) dirs.push_back({{c[i][0], c[i][1], c[i][2]}});
     const int nz = p->nz;
     unsigned nthreads = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
     nthreads = std::min<unsigned>(nthreads, (unsigned)nz);
@@ -340,8 +391,8 @@ int64_t build_links(const lbm_params* p, const uint8_t* labels, bool d3q7, LinkL
                         ++cnt;
                         if (!out) continue;
                         uint32_t meta = (uint32_t)(i + 1) | ((uint32_t)grp << LINK_GROUP_SHIFT);
-                        if (d3q7) {
-                            meta |= LINK_D3Q7;
+                        if (temp) {
+                            meta |= LINK_TEMP;
                             const int dir = grp < 6 ? p->face_thermal[grp] : p->solid_thermal;
                             if (dir == LBM_DIRICHLET) meta |= LINK_DIRICHLET;
                         } else {
@@ -395,7 +446,7 @@ int64_t order_links(const LinkList& f, const LinkList& g, LinkList* out)
     constexpr int NB = LBM_MAX_GROUPS * 2 * 32;
     auto bucket_of = [](uint32_t m) {
         const uint32_t grp = (m >> LINK_GROUP_SHIFT) & LINK_GROUP_MASK;
-        return (int)((grp * 2 + ((m & LINK_D3Q7) ? 1 : 0)) * 32 + (m & LINK_DIR_MASK));
+        return (int)((grp * 2 + ((m & LINK_TEMP) ? 1 : 0)) * 32 + (m & LINK_DIR_MASK));
     };
     std::vector<int64_t> start(NB + 1, 0);
     for (const LinkList* L : {&f, &g})
@@ -426,7 +477,7 @@ bool any_solid(const lbm_params* p, const uint8_t* labels)
     return false;
 }
 
-// Per-cell solid mask.  Fluid cell: bit q (kernel direction 1..18) when the
+// Per-cell solid mask.  Fluid cell: bit q (flow direction 1..18 or 1..8) when the
 // link (x, q) ends in a solid cell without crossing a wall face.  Solid cell:
 // MASK_SOLID, and bit q when (s + c_q, opp q) is such a link of a fluid cell.
 std::vector<uint32_t> build_mask(const lbm_params* p, const uint8_t* labels)
@@ -434,6 +485,8 @@ std::vector<uint32_t> build_mask(const lbm_params* p, const uint8_t* labels)
     const int64_t n = (int64_t)p->nx * p->ny * p->nz;
     std::vector<uint32_t> mask((size_t)n, 0u);
     const int nz = p->nz;
+    int dirs[Q19][3];
+    const int nd = lattice_dirs(p, false, dirs);
     unsigned nthreads = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
     nthreads = std::min<unsigned>(nthreads, (unsigned)nz);
     auto work = [&](unsigned tid) {
@@ -443,8 +496,8 @@ std::vector<uint32_t> build_mask(const lbm_params* p, const uint8_t* labels)
                 for (int x = 0; x < p->nx; ++x) {
                     const int32_t cell = x + p->nx * (y + p->ny * z);
                     uint32_t m = 0;
-                    for (int q = 1; q < Q19; ++q) {
-                        const int c[3] = {cx19(q), cy19(q), cz19(q)};
+                    for (int q = 1; q <= nd; ++q) {
+                        const int c[3] = {dirs[q - 1][0], dirs[q - 1][1], dirs[q - 1][2]};
                         int32_t image;
                         if (!labels[cell]) {
                             if (blocked_group(p, labels, x, y, z, c, &image) >= 6) m |= 1u << q;
@@ -482,8 +535,9 @@ Layout make_layout(const lbm_params* p, bool solids, int64_t n_links)
     const int64_t n = (int64_t)p->nx * p->ny * p->nz;
     L.stride = plane_stride(n);
     const size_t es = (size_t)p->dtype;
-    const size_t fb = align_up(19 * (size_t)L.stride * es);
-    const size_t gb = p->thermal ? align_up(7 * (size_t)L.stride * es) : 0;
+    const bool two_d = p->lattice == LBM_LATTICE_2D;
+    const size_t fb = align_up((two_d ? Q9 : Q19) * (size_t)L.stride * es);
+    const size_t gb = p->thermal ? align_up((two_d ? Q5 : Q7) * (size_t)L.stride * es) : 0;
     const bool ab = p->streaming == LBM_STREAM_AB;
     size_t off = 0;
     L.f = off; off += fb;
@@ -534,7 +588,7 @@ LinkArgs<R> link_args(lbm_ctx* c, int mode, char* fsrc, char* fdst, char* gsrc, 
     a.g_dst = (R*)gdst;
     a.begin = 0;
     a.end = c->n_f + c->n_g;
-    a.omega = (6.0 + c->p.a_T) / 21.0;
+    a.omega = abb_omega(&c->p);
     a.mode = mode;
     a.in_kernel = c->in_kernel ? 1 : 0;
     a.bb = make_bounce<R>(&c->p, c->in_kernel, c->face_vel);
@@ -550,7 +604,7 @@ const Collision<double>& collision<double>(const lbm_ctx* c) { return c->cold; }
 
 // Enqueue one time step (parity from c->t) on `stream` and advance c->t;
 // `last` adds the force/heat pass of a submission's last step.
-template <typename R>
+template <class L, typename R>
 lbm_status enqueue_step(lbm_ctx* c, hipStream_t stream, bool last)
 {
     const int64_t n_links = c->n_f + c->n_g;
@@ -567,7 +621,7 @@ lbm_status enqueue_step(lbm_ctx* c, hipStream_t stream, bool last)
         s.f = (R*)c->f;
         s.g = (R*)c->g;
         s.parity = parity;
-        LBM_HIP(c, launch_aa_step<R>(s, c->thermal, stream), "AA step kernel");
+        LBM_HIP(c, (launch_aa_step<L, R>(s, c->thermal, stream)), "AA step kernel");
         la = link_args<R>(c, parity == 0 ? LINK_AA_AFTER_EVEN : LINK_AA_AFTER_ODD, c->f, c->f, c->g, c->g);
         if (passes) {
             // link passes: gather every source, then scatter
@@ -585,8 +639,8 @@ lbm_status enqueue_step(lbm_ctx* c, hipStream_t stream, bool last)
         s.g = (R*)ga;
         s.f2 = (R*)fb;
         s.g2 = (R*)gb;
-        LBM_HIP(c, launch_ab_collide<R>(s, c->thermal, stream), "A-B collide kernel");
-        LBM_HIP(c, launch_ab_pull<R>(s, c->thermal, stream), "A-B pull kernel");
+        LBM_HIP(c, (launch_ab_collide<L, R>(s, c->thermal, stream)), "A-B collide kernel");
+        LBM_HIP(c, (launch_ab_pull<L, R>(s, c->thermal, stream)), "A-B pull kernel");
         la = link_args<R>(c, LINK_AB, fa, fb, ga, gb);
         if (passes) {
             // sources in one buffer, destinations in the other: one pass
@@ -601,7 +655,7 @@ lbm_status enqueue_step(lbm_ctx* c, hipStream_t stream, bool last)
         LBM_HIP(c, launch_zero_f64(c->accum, 4 * LBM_MAX_GROUPS, stream), "zero accumulators");
         la.begin = 0;
         la.end = n_links;
-        LBM_HIP(c, launch_link_force<R>(la, stream), "force kernel");
+        LBM_HIP(c, (launch_link_force<L, R>(la, stream)), "force kernel");
     }
     c->t += 1;
     return LBM_OK;
@@ -611,7 +665,7 @@ lbm_status enqueue_step(lbm_ctx* c, hipStream_t stream, bool last)
 // per context: 8 pairs for boxes up to 2^21 cells, where launch overhead is
 // comparable to a step, else 1.  Any failure leaves the context on per-step
 // launches.
-template <typename R>
+template <class L, typename R>
 void capture_pair(lbm_ctx* c)
 {
     if (c->pair || c->pair_failed) return;
@@ -628,7 +682,7 @@ void capture_pair(lbm_ctx* c)
     bool ok = hipStreamBeginCapture(c->capture_stream, hipStreamCaptureModeThreadLocal) == hipSuccess;
     if (ok) {
         bool launched = true;
-        for (int i = 0; i < steps && launched; ++i) launched = enqueue_step<R>(c, c->capture_stream, false) == LBM_OK;
+        for (int i = 0; i < steps && launched; ++i) launched = enqueue_step<L, R>(c, c->capture_stream, false) == LBM_OK;
         ok = hipStreamEndCapture(c->capture_stream, &graph) == hipSuccess && launched && graph;
     }
     c->t = t_saved;
@@ -646,14 +700,14 @@ void capture_pair(lbm_ctx* c)
 // n steps: an odd first step alone, then replays of the step-pair graph,
 // then the remaining steps (the very last with the force pass) launched
 // directly.  Short submissions launch every step directly.
-template <typename R>
+template <class L, typename R>
 lbm_status step_impl(lbm_ctx* c, int64_t n)
 {
     int64_t left = n;
-    if (left >= 6) capture_pair<R>(c);
+    if (left >= 6) capture_pair<L, R>(c);
     if (c->pair && left > c->pair_steps + 1) {
         if (c->t & 1) {
-            if (lbm_status st = enqueue_step<R>(c, c->stream, false)) return st;
+            if (lbm_status st = enqueue_step<L, R>(c, c->stream, false)) return st;
             --left;
         }
         while (left > c->pair_steps) {
@@ -663,7 +717,7 @@ lbm_status step_impl(lbm_ctx* c, int64_t n)
         }
     }
     while (left > 0) {
-        if (lbm_status st = enqueue_step<R>(c, c->stream, left == 1)) return st;
+        if (lbm_status st = enqueue_step<L, R>(c, c->stream, left == 1)) return st;
         --left;
     }
     return LBM_OK;
@@ -733,6 +787,7 @@ lbm_status lbm_create(const lbm_params* p, const uint8_t* solid_labels, void* de
         c->es = p->dtype;
         c->thermal = p->thermal != 0;
         c->ab = p->streaming == LBM_STREAM_AB;
+        c->two_d = p->lattice == LBM_LATTICE_2D;
         c->stream = (hipStream_t)hip_stream;
         const bool solids = any_solid(p, solid_labels);
         const uint8_t* lab = solids ? solid_labels : nullptr;
@@ -844,13 +899,15 @@ lbm_status lbm_init_fields(lbm_ctx* c, const void* rho, const void* u, const voi
         a.rho = (const float*)rho;
         a.u = (const float*)u;
         a.T = (const float*)T;
-        e = launch_init<float>(a, c->thermal, c->stream);
+        e = c->two_d ? launch_init<Lat2D, float>(a, c->thermal, c->stream)
+                     : launch_init<Lat3D, float>(a, c->thermal, c->stream);
     } else {
         FieldArgs<double> a = field_args<double>(c);
         a.rho = (const double*)rho;
         a.u = (const double*)u;
         a.T = (const double*)T;
-        e = launch_init<double>(a, c->thermal, c->stream);
+        e = c->two_d ? launch_init<Lat2D, double>(a, c->thermal, c->stream)
+                     : launch_init<Lat3D, double>(a, c->thermal, c->stream);
     }
     if (e != hipSuccess) return device_error(c, e, "init kernel");
     c->initialised = true;
@@ -869,7 +926,8 @@ lbm_status lbm_step(lbm_ctx* c, int64_t n)
         return LBM_E_INVALID;
     }
     if (n == 0) return LBM_OK;
-    return c->es == 4 ? step_impl<float>(c, n) : step_impl<double>(c, n);
+    if (c->two_d) return c->es == 4 ? step_impl<Lat2D, float>(c, n) : step_impl<Lat2D, double>(c, n);
+    return c->es == 4 ? step_impl<Lat3D, float>(c, n) : step_impl<Lat3D, double>(c, n);
 }
 
 lbm_status lbm_read_macros(lbm_ctx* c, void* rho, void* u, void* T)
@@ -885,13 +943,15 @@ lbm_status lbm_read_macros(lbm_ctx* c, void* rho, void* u, void* T)
         a.rho_out = (float*)rho;
         a.u_out = (float*)u;
         a.T_out = (float*)T;
-        e = launch_read<float>(a, c->thermal, c->stream);
+        e = c->two_d ? launch_read<Lat2D, float>(a, c->thermal, c->stream)
+                     : launch_read<Lat3D, float>(a, c->thermal, c->stream);
     } else {
         FieldArgs<double> a = field_args<double>(c);
         a.rho_out = (double*)rho;
         a.u_out = (double*)u;
         a.T_out = (double*)T;
-        e = launch_read<double>(a, c->thermal, c->stream);
+        e = c->two_d ? launch_read<Lat2D, double>(a, c->thermal, c->stream)
+                     : launch_read<Lat3D, double>(a, c->thermal, c->stream);
     }
     if (e != hipSuccess) return device_error(c, e, "read kernel");
     return LBM_OK;
@@ -932,8 +992,13 @@ lbm_status lbm_diagnostics(lbm_ctx* c, double* out, int32_t n)
         return LBM_E_INVALID;
     }
     LBM_HIP(c, launch_zero_f64(c->diag, LBM_DIAG_COUNT, c->stream), "clear diagnostics");
-    hipError_t e = c->es == 4 ? launch_diag<float>(field_args<float>(c), c->thermal, c->diag, c->stream)
-                              : launch_diag<double>(field_args<double>(c), c->thermal, c->diag, c->stream);
+    hipError_t e;
+    if (c->two_d)
+        e = c->es == 4 ? launch_diag<Lat2D, float>(field_args<float>(c), c->thermal, c->diag, c->stream)
+                       : launch_diag<Lat2D, double>(field_args<double>(c), c->thermal, c->diag, c->stream);
+    else
+        e = c->es == 4 ? launch_diag<Lat3D, float>(field_args<float>(c), c->thermal, c->diag, c->stream)
+                       : launch_diag<Lat3D, double>(field_args<double>(c), c->thermal, c->diag, c->stream);
     if (e != hipSuccess) return device_error(c, e, "diagnostics kernel");
     double d[LBM_DIAG_COUNT];
     int32_t unstable = 0;
@@ -955,10 +1020,12 @@ int64_t lbm_time(const lbm_ctx* c) { return c ? c->t : -1; }
 int64_t lbm_count_links(const lbm_params* p, const uint8_t* solid_labels, int32_t lattice)
 {
     try {
-        if (!validate(p).empty() || (lattice != 19 && lattice != 7) || solid_on_slip_layer(p, solid_labels))
-            return -1;
+        if (!validate(p).empty() || solid_on_slip_layer(p, solid_labels)) return -1;
+        const bool two_d = p->lattice == LBM_LATTICE_2D;
+        const int flow = two_d ? 9 : 19, temp = two_d ? 5 : 7;
+        if (lattice != flow && lattice != temp) return -1;
         const uint8_t* lab = any_solid(p, solid_labels) ? solid_labels : nullptr;
-        return build_links(p, lab, lattice == 7, nullptr);
+        return build_links(p, lab, lattice == temp, nullptr);
     } catch (...) {
         return -1;
     }
@@ -967,8 +1034,8 @@ int64_t lbm_count_links(const lbm_params* p, const uint8_t* solid_labels, int32_
 int64_t lbm_num_links(const lbm_ctx* c, int32_t lattice)
 {
     if (!c) return -1;
-    if (lattice == 19) return c->n_f;
-    if (lattice == 7) return c->n_g;
+    if (lattice == (c->two_d ? 9 : 19)) return c->n_f;
+    if (lattice == (c->two_d ? 5 : 7)) return c->n_g;
     return -1;
 }
 

@@ -42,7 +42,7 @@ struct Geometry {
 //           cell's index on its face (see Bounce::face_vel)
 //   meta  : bits 0..4 direction p (kernel order of its lattice),
 //           bits 5..13 force/heat group, bit 14 Dirichlet (D3Q7 only),
-//           bit 15 the link belongs to the D3Q7 lattice,
+//           bit 15 the link belongs to the temperature lattice (D3Q7 or D2Q5),
 //           bits 16..17 the D3Q19 rule (LinkRule), bits 18..19 the axis of
 //           the governing face
 // Links [0, n_wall) cross a box face; [n_wall, n_total) end in a solid cell.
@@ -51,18 +51,18 @@ constexpr uint32_t LINK_DIR_MASK = 31u;
 constexpr uint32_t LINK_GROUP_SHIFT = 5;
 constexpr uint32_t LINK_GROUP_MASK = 511u;
 constexpr uint32_t LINK_DIRICHLET = 1u << 14;
-constexpr uint32_t LINK_D3Q7 = 1u << 15;
+constexpr uint32_t LINK_TEMP = 1u << 15;
 constexpr uint32_t LINK_RULE_SHIFT = 16;
 constexpr uint32_t LINK_AXIS_SHIFT = 18;
 enum LinkRule : uint32_t { RULE_WALL = 0, RULE_SLIP = 1, RULE_VELOCITY = 2, RULE_PRESSURE = 3 };
 
 // Per-cell solid mask (only when the box has solid cells).  On a fluid cell,
-// bit q (1..18) is set when x + c_q is a solid cell reached without crossing
-// a wall face (a solid link).  On a solid cell, MASK_SOLID is set and bit q
+// bit q (1..18, or 1..8 for D2Q9) is set when x + c_q is a solid cell reached
+// without crossing a wall face (a solid link).  On a solid cell, MASK_SOLID is set and bit q
 // marks that (s + c_q, opp q) is such a solid link of a fluid neighbour,
 // which re-reads and re-stores the slot the solid cell's odd step would store
-// direction q to.  D3Q7 direction k (1..6) is the D3Q19 axis direction k, so bits 1..6
-// serve both lattices.
+// direction q to.  Temperature direction k (D3Q7: 1..6, D2Q5: 1..4) is the
+// flow lattice's axis direction k, so those bits serve both lattices.
 constexpr uint32_t MASK_SOLID = 1u << 31;
 
 // Which slots a link pass reads and writes.
@@ -154,18 +154,20 @@ struct FieldArgs {
 };
 
 // Launch wrappers (defined in lbm_kernels.hip).  Each returns the HIP error
-// of the launch.
-template <typename R> hipError_t launch_aa_step(const StepArgs<R>& a, bool thermal, hipStream_t s);
-template <typename R> hipError_t launch_ab_collide(const StepArgs<R>& a, bool thermal, hipStream_t s);
-template <typename R> hipError_t launch_ab_pull(const StepArgs<R>& a, bool thermal, hipStream_t s);
+// of the launch.  L is the lattice pair (Lat3D: D3Q19 + D3Q7, Lat2D: D2Q9 +
+// D2Q5 on one z layer); the link gather / scatter passes do not depend on it.
+template <class L, typename R> hipError_t launch_aa_step(const StepArgs<R>& a, bool thermal, hipStream_t s);
+template <class L, typename R> hipError_t launch_ab_collide(const StepArgs<R>& a, bool thermal, hipStream_t s);
+template <class L, typename R> hipError_t launch_ab_pull(const StepArgs<R>& a, bool thermal, hipStream_t s);
 template <typename R> hipError_t launch_link_gather(const LinkArgs<R>& a, hipStream_t s);
 template <typename R> hipError_t launch_link_scatter(const LinkArgs<R>& a, hipStream_t s);
 template <typename R> hipError_t launch_link_direct(const LinkArgs<R>& a, hipStream_t s);
-template <typename R> hipError_t launch_link_force(const LinkArgs<R>& a, hipStream_t s);
-template <typename R> hipError_t launch_init(const FieldArgs<R>& a, bool thermal, hipStream_t s);
-template <typename R> hipError_t launch_read(const FieldArgs<R>& a, bool thermal, hipStream_t s);
+template <class L, typename R> hipError_t launch_link_force(const LinkArgs<R>& a, hipStream_t s);
+template <class L, typename R> hipError_t launch_init(const FieldArgs<R>& a, bool thermal, hipStream_t s);
+template <class L, typename R> hipError_t launch_read(const FieldArgs<R>& a, bool thermal, hipStream_t s);
 // Volume sums of lbm_diagnostics() into out[LBM_DIAG_COUNT] (cleared by the caller).
-template <typename R> hipError_t launch_diag(const FieldArgs<R>& a, bool thermal, double* out, hipStream_t s);
+template <class L, typename R>
+hipError_t launch_diag(const FieldArgs<R>& a, bool thermal, double* out, hipStream_t s);
 hipError_t launch_zero_f64(double* p, int64_t n, hipStream_t s);
 
 }  // namespace lbm

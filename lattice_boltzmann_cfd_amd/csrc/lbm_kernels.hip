@@ -28,27 +28,29 @@ namespace {
 constexpr int BLOCK = 256;
 constexpr int LBM_GROUPS = 261;  // 6 faces + 255 solid labels
 
-// Run-time direction tables packed into 64-bit constants: 2 bits per
-// direction holding c + 1.
-__host__ __device__ constexpr uint64_t pack_dirs(int which, int Q)
+// Run-time direction tables of a flow lattice packed into 64-bit constants:
+// 2 bits per direction holding c + 1.
+template <class L>
+__host__ __device__ constexpr uint64_t pack_dirs(int which)
 {
     uint64_t v = 0;
-    for (int q = 0; q < Q; ++q) {
-        int c = 0;
-        if (Q == Q19) c = which == 0 ? cx19(q) : (which == 1 ? cy19(q) : cz19(q));
-        else c = which == 0 ? cx7(q) : (which == 1 ? cy7(q) : cz7(q));
+    for (int q = 0; q < L::Q; ++q) {
+        const int c = which == 0 ? L::cx(q) : (which == 1 ? L::cy(q) : L::cz(q));
         v |= (uint64_t)(c + 1) << (2 * q);
     }
     return v;
 }
-constexpr uint64_t CX19 = pack_dirs(0, Q19), CY19 = pack_dirs(1, Q19), CZ19 = pack_dirs(2, Q19);
+template <class L>
+struct Packed {
+    static constexpr uint64_t X = pack_dirs<L>(0), Y = pack_dirs<L>(1), Z = pack_dirs<L>(2);
+};
 
 __device__ __forceinline__ int dir_comp(uint64_t packed, int q) { return (int)((packed >> (2 * q)) & 3u) - 1; }
-__device__ __forceinline__ int opp_rt(int q) { return q == 0 ? 0 : ((q & 1) ? q + 1 : q - 1); }
-__device__ __forceinline__ double w19_rt(int q) { return q == 0 ? 1.0 / 3.0 : (q <= 6 ? 1.0 / 18.0 : 1.0 / 36.0); }
 
 // Wrapped neighbour offsets of one cell: a cell's coordinates are computed
 // once and each axis wraps with a compare and an add.
+// On one z layer (DIMS = 2) z is 0 and the z offsets vanish.
+template <int DIMS>
 struct Nbr {
     int32_t xm, xp, ym, yp, zm, zp;
     uint32_t faces;  // bit f: the cell touches box face f (x-, x+, y-, y+, z-, z+)
@@ -58,14 +60,19 @@ struct Nbr {
     {
         const uint32_t r = divide((uint32_t)cell, G.div_nx);
         x = cell - (int32_t)r * G.nx;
-        z = (int32_t)divide(r, G.div_ny);
-        y = (int32_t)r - z * G.ny;
+        if (DIMS == 2) {
+            z = 0;
+            y = (int32_t)r;
+        } else {
+            z = (int32_t)divide(r, G.div_ny);
+            y = (int32_t)r - z * G.ny;
+        }
         xm = (x == 0) ? G.nx - 1 : -1;
         xp = (x == G.nx - 1) ? 1 - G.nx : 1;
         ym = (y == 0) ? (G.ny - 1) * G.nx : -G.nx;
         yp = (y == G.ny - 1) ? (1 - G.ny) * G.nx : G.nx;
-        zm = ((int32_t)z == 0) ? (G.nz - 1) * G.nxy : -G.nxy;
-        zp = ((int32_t)z == G.nz - 1) ? (1 - G.nz) * G.nxy : G.nxy;
+        zm = DIMS == 2 ? 0 : (((int32_t)z == 0) ? (G.nz - 1) * G.nxy : -G.nxy);
+        zp = DIMS == 2 ? 0 : (((int32_t)z == G.nz - 1) ? (1 - G.nz) * G.nxy : G.nxy);
         faces = (x == 0 ? 1u : 0u) | (x == G.nx - 1 ? 2u : 0u) | (y == 0 ? 4u : 0u) | (y == G.ny - 1 ? 8u : 0u) |
                 ((int32_t)z == 0 ? 16u : 0u) | ((int32_t)z == G.nz - 1 ? 32u : 0u);
     }
@@ -95,18 +102,19 @@ __device__ __forceinline__ void st(R* plane, int32_t idx, R v)
 
 // ------------------------------------------------------ boundaries
 
-// D3Q19 directions leaving the box through face f (x-, x+, y-, y+, z-, z+).
+// Flow-lattice directions leaving the box through face f (x-, x+, y-, y+, z-, z+).
+template <class L>
 __host__ __device__ constexpr uint32_t dirs_through(int f)
 {
     uint32_t m = 0;
-    for (int q = 1; q < Q19; ++q) {
-        const int c = (f >> 1) == 0 ? cx19(q) : ((f >> 1) == 1 ? cy19(q) : cz19(q));
+    for (int q = 1; q < L::Q; ++q) {
+        const int c = (f >> 1) == 0 ? L::cx(q) : ((f >> 1) == 1 ? L::cy(q) : L::cz(q));
         if ((f & 1) ? c > 0 : c < 0) m |= 1u << q;
     }
     return m;
 }
 
-// Face crossed by D3Q7 direction k (1..6).
+// Face crossed by temperature-lattice direction k (1..6, or 1..4 in 2D).
 __host__ __device__ constexpr int face7(int k) { return (k - 1) ^ 1; }
 
 // Blocked directions of one cell for the in-kernel bounce-back: `wall` holds
@@ -119,15 +127,15 @@ struct Blocked {
     bool is_solid;
 };
 
-template <typename R>
+template <class L, typename R>
 __device__ __forceinline__ Blocked blocked_dirs(const Bounce<R>& bb, const uint32_t* mask, int32_t cell,
                                                 uint32_t faces)
 {
     Blocked b;
     const uint32_t fw = faces & (uint32_t)bb.walls;
-    b.wall = ((fw & 1u) ? dirs_through(0) : 0u) | ((fw & 2u) ? dirs_through(1) : 0u) |
-             ((fw & 4u) ? dirs_through(2) : 0u) | ((fw & 8u) ? dirs_through(3) : 0u) |
-             ((fw & 16u) ? dirs_through(4) : 0u) | ((fw & 32u) ? dirs_through(5) : 0u);
+    b.wall = ((fw & 1u) ? dirs_through<L>(0) : 0u) | ((fw & 2u) ? dirs_through<L>(1) : 0u) |
+             ((fw & 4u) ? dirs_through<L>(2) : 0u) | ((fw & 8u) ? dirs_through<L>(3) : 0u) |
+             ((fw & 16u) ? dirs_through<L>(4) : 0u) | ((fw & 32u) ? dirs_through<L>(5) : 0u);
     const uint32_t m = mask ? mask[cell] : 0u;
     b.is_solid = (m & MASK_SOLID) != 0;
     b.solid = b.is_solid ? 0u : m;
@@ -147,13 +155,14 @@ __device__ __forceinline__ R bounce7(const Bounce<R>& bb, const Blocked& b, int 
     return bb.solid_dirichlet ? bb.solid_gw - v : v;
 }
 
-// Reflection of D3Q19 direction p across a face of axis a: the a component
+// Reflection of flow direction p across a face of axis a: the a component
 // of c_p reversed.
-__host__ __device__ constexpr int refl19(int a, int p)
+template <class L>
+__host__ __device__ constexpr int refl(int a, int p)
 {
-    for (int r = 0; r < Q19; ++r)
-        if (cx19(r) == (a == 0 ? -cx19(p) : cx19(p)) && cy19(r) == (a == 1 ? -cy19(p) : cy19(p)) &&
-            cz19(r) == (a == 2 ? -cz19(p) : cz19(p)))
+    for (int r = 0; r < L::Q; ++r)
+        if (L::cx(r) == (a == 0 ? -L::cx(p) : L::cx(p)) && L::cy(r) == (a == 1 ? -L::cy(p) : L::cy(p)) &&
+            L::cz(r) == (a == 2 ? -L::cz(p) : L::cz(p)))
             return r;
     return 0;
 }
@@ -167,13 +176,13 @@ struct FaceRules {
     uint32_t slip, vel, pres;
 };
 
-template <typename R>
+template <class L, typename R>
 __device__ __forceinline__ FaceRules face_rules(const Bounce<R>& bb, uint32_t faces)
 {
     const uint32_t fw = faces & (uint32_t)bb.walls;
-    const uint32_t cx = ((fw & 1u) ? dirs_through(0) : 0u) | ((fw & 2u) ? dirs_through(1) : 0u);
-    const uint32_t cy = ((fw & 4u) ? dirs_through(2) : 0u) | ((fw & 8u) ? dirs_through(3) : 0u);
-    const uint32_t cz = ((fw & 16u) ? dirs_through(4) : 0u) | ((fw & 32u) ? dirs_through(5) : 0u);
+    const uint32_t cx = ((fw & 1u) ? dirs_through<L>(0) : 0u) | ((fw & 2u) ? dirs_through<L>(1) : 0u);
+    const uint32_t cy = ((fw & 4u) ? dirs_through<L>(2) : 0u) | ((fw & 8u) ? dirs_through<L>(3) : 0u);
+    const uint32_t cz = ((fw & 16u) ? dirs_through<L>(4) : 0u) | ((fw & 32u) ? dirs_through<L>(5) : 0u);
     FaceRules r;
     r.ax = cx;
     r.ay = cy & ~cx;
@@ -181,7 +190,7 @@ __device__ __forceinline__ FaceRules face_rules(const Bounce<R>& bb, uint32_t fa
     uint32_t sl = 0u, ve = 0u, pr = 0u;
 #pragma unroll
     for (int f = 0; f < 6; ++f) {
-        const uint32_t gov = (f < 2 ? r.ax : (f < 4 ? r.ay : r.az)) & dirs_through(f);
+        const uint32_t gov = (f < 2 ? r.ax : (f < 4 ? r.ay : r.az)) & dirs_through<L>(f);
         if ((bb.slip >> f) & 1) sl |= gov;
         if ((bb.vel >> f) & 1) ve |= gov;
         if ((bb.pres >> f) & 1) pr |= gov;
@@ -197,36 +206,37 @@ __device__ __forceinline__ int gov_axis(const FaceRules& r, int p)
 {
     return ((r.ax >> p) & 1u) ? 0 : (((r.ay >> p) & 1u) ? 1 : 2);
 }
+template <class L>
 __device__ __forceinline__ int gov_face(const FaceRules& r, int p)
 {
     const int a = gov_axis(r, p);
-    const int c = a == 0 ? cx19(p) : (a == 1 ? cy19(p) : cz19(p));
+    const int c = a == 0 ? L::cx(p) : (a == 1 ? L::cy(p) : L::cz(p));
     return 2 * a + (c > 0 ? 1 : 0);
 }
 
 // VELOCITY link (Ladd's moving wall): the returning population is
 // f_p^+ - 6 w_p rho_w c_p.u_w; this is the subtracted term.
-template <typename R>
+template <class L, typename R>
 __device__ __forceinline__ R vel_shift(const Bounce<R>& bb, int f, int p)
 {
-    const R cu = (R)cx19(p) * bb.face_u[f][0] + (R)cy19(p) * bb.face_u[f][1] + (R)cz19(p) * bb.face_u[f][2];
-    return (R)(6.0 * w19(p)) * bb.face_rho[f] * cu;
+    const R cu = (R)L::cx(p) * bb.face_u[f][0] + (R)L::cy(p) * bb.face_u[f][1] + (R)L::cz(p) * bb.face_u[f][2];
+    return (R)(6.0 * L::w(p)) * bb.face_rho[f] * cu;
 }
 
 // PRESSURE link (anti-bounce-back at the wall density): the returning
 // population f = -f_p^+ + 2 w_p rho_w [1 + 9/2 (c_p.u)^2 - 3/2 u.u], written
 // for shifted storage (f = h + w_p).
-template <typename R>
+template <class L, typename R>
 __device__ __forceinline__ R pres_value(const Bounce<R>& bb, int f, int p, R hout, R ux, R uy, R uz)
 {
-    const R cu = (R)cx19(p) * ux + (R)cy19(p) * uy + (R)cz19(p) * uz;
+    const R cu = (R)L::cx(p) * ux + (R)L::cy(p) * uy + (R)L::cz(p) * uz;
     const R uu = ux * ux + uy * uy + uz * uz;
-    return (R)(2.0 * w19(p)) * (bb.face_rho[f] * (R(1) + R(4.5) * cu * cu - R(1.5) * uu) - R(1)) - hout;
+    return (R)(2.0 * L::w(p)) * (bb.face_rho[f] * (R(1) + R(4.5) * cu * cu - R(1.5) * uu) - R(1)) - hout;
 }
 
 // A cell's slot in the velocity planes of PRESSURE face f.
-template <typename R>
-__device__ __forceinline__ int64_t face_slot(const Bounce<R>& bb, const Geometry& G, int f, const Nbr& nb)
+template <typename R, int D>
+__device__ __forceinline__ int64_t face_slot(const Bounce<R>& bb, const Geometry& G, int f, const Nbr<D>& nb)
 {
     const int32_t i = f < 2 ? nb.y + G.ny * nb.z : (f < 4 ? nb.x + G.nx * nb.z : nb.x + G.nx * nb.y);
     return bb.face_off[f] + i;
@@ -234,8 +244,8 @@ __device__ __forceinline__ int64_t face_slot(const Bounce<R>& bb, const Geometry
 
 // Keep a cell's velocity for each PRESSURE face it lies on (read by the
 // two-buffer pull and by the force pass).
-template <typename R>
-__device__ __forceinline__ void keep_face_velocity(const Bounce<R>& bb, const Geometry& G, const Nbr& nb, R ux,
+template <typename R, int D>
+__device__ __forceinline__ void keep_face_velocity(const Bounce<R>& bb, const Geometry& G, const Nbr<D>& nb, R ux,
                                                    R uy, R uz)
 {
     const uint32_t fp = nb.faces & (uint32_t)bb.pres;
@@ -255,39 +265,40 @@ __device__ __forceinline__ void keep_face_velocity(const Bounce<R>& bb, const Ge
 // slot (q, x) (an even step stores PRESSURE links already anti-bounced);
 // VELOCITY: the same, less the moving-wall term; SLIP: the population sent
 // from x - c_t along q reflected, at (opposite(q reflected), x - c_t).
-template <typename R, int BND>
-__device__ __forceinline__ R blocked_inflow(const R* f, int64_t S, int32_t cell, const Nbr& nb, const FaceRules& fr,
-                                            const Bounce<R>& bb, int q)
+template <class L, typename R, int BND>
+__device__ __forceinline__ R blocked_inflow(const R* f, int64_t S, int32_t cell, const Nbr<L::DIMS>& nb,
+                                            const FaceRules& fr, const Bounce<R>& bb, int q)
 {
-    const int p = opp19(q);
+    const int p = opp(q);
     if (BND == 2 && ((fr.slip >> p) & 1u)) {
         const int a = gov_axis(fr, p);
-        const int src = a == 0 ? refl19(0, q) : (a == 1 ? refl19(1, q) : refl19(2, q));
-        const int32_t y = cell + nb.at(a == 0 ? 0 : -cx19(q), a == 1 ? 0 : -cy19(q), a == 2 ? 0 : -cz19(q));
-        return ld(f + opp19(src) * S, y);
+        const int src = a == 0 ? refl<L>(0, q) : (a == 1 ? refl<L>(1, q) : refl<L>(2, q));
+        const int32_t y = cell + nb.at(a == 0 ? 0 : -L::cx(q), a == 1 ? 0 : -L::cy(q), a == 2 ? 0 : -L::cz(q));
+        return ld(f + opp(src) * S, y);
     }
     R v = ld(f + q * S, cell);
-    if (BND == 2 && ((fr.vel >> p) & 1u)) v -= vel_shift(bb, gov_face(fr, p), p);
+    if (BND == 2 && ((fr.vel >> p) & 1u)) v -= vel_shift<L>(bb, gov_face<L>(fr, p), p);
     return v;
 }
 
 // In place, an odd step's blocked outflow p of fluid cell x, stored where the
 // next (even) step reads the returning population: (opposite(p), x) with the
 // link's rule applied, or for SLIP (p reflected, x + c_t).
-template <typename R, int BND>
-__device__ __forceinline__ void blocked_outflow(R* f, int64_t S, int32_t cell, const Nbr& nb, const FaceRules& fr,
-                                                const Bounce<R>& bb, int p, R h, R ux, R uy, R uz)
+template <class L, typename R, int BND>
+__device__ __forceinline__ void blocked_outflow(R* f, int64_t S, int32_t cell, const Nbr<L::DIMS>& nb,
+                                                const FaceRules& fr, const Bounce<R>& bb, int p, R h, R ux, R uy,
+                                                R uz)
 {
     if (BND == 2 && ((fr.slip >> p) & 1u)) {
         const int a = gov_axis(fr, p);
-        const int dst = a == 0 ? refl19(0, p) : (a == 1 ? refl19(1, p) : refl19(2, p));
-        st(f + dst * S, cell + nb.at(a == 0 ? 0 : cx19(p), a == 1 ? 0 : cy19(p), a == 2 ? 0 : cz19(p)), h);
+        const int dst = a == 0 ? refl<L>(0, p) : (a == 1 ? refl<L>(1, p) : refl<L>(2, p));
+        st(f + dst * S, cell + nb.at(a == 0 ? 0 : L::cx(p), a == 1 ? 0 : L::cy(p), a == 2 ? 0 : L::cz(p)), h);
         return;
     }
     R v = h;
-    if (BND == 2 && ((fr.vel >> p) & 1u)) v = h - vel_shift(bb, gov_face(fr, p), p);
-    if (BND == 2 && ((fr.pres >> p) & 1u)) v = pres_value(bb, gov_face(fr, p), p, h, ux, uy, uz);
-    st(f + opp19(p) * S, cell, v);
+    if (BND == 2 && ((fr.vel >> p) & 1u)) v = h - vel_shift<L>(bb, gov_face<L>(fr, p), p);
+    if (BND == 2 && ((fr.pres >> p) & 1u)) v = pres_value<L>(bb, gov_face<L>(fr, p), p, h, ux, uy, uz);
+    st(f + opp(p) * S, cell, v);
 }
 
 // ------------------------------------------------------------ AA step
@@ -315,7 +326,7 @@ __device__ __forceinline__ void blocked_outflow(R* f, int64_t S, int32_t cell, c
 // A solid cell skips its odd-step stores into slots a fluid neighbour claims
 // this way (mask bits) and into wrapped slots across a face.  No slot is
 // touched by two cells in one step.
-template <typename R, bool TH, int BND>
+template <class L, typename R, bool TH, int BND>
 __global__ void __launch_bounds__(BLOCK) k_aa_step(StepArgs<R> a)
 {
     const Geometry& G = a.geo;
@@ -324,22 +335,22 @@ __global__ void __launch_bounds__(BLOCK) k_aa_step(StepArgs<R> a)
     const int64_t S = G.stride;
     R* __restrict__ f = a.f;
     R* __restrict__ gg = a.g;
-    R h[Q19];
-    R g[Q7];
+    R h[L::Q];
+    R g[L::QT];
     if (a.parity == 0) {
 #pragma unroll
-        for (int q = 0; q < Q19; ++q) h[q] = ld(f + q * S, cell);
+        for (int q = 0; q < L::Q; ++q) h[q] = ld(f + q * S, cell);
         if (TH) {
 #pragma unroll
-            for (int k = 0; k < Q7; ++k) g[k] = ld(gg + k * S, cell);
+            for (int k = 0; k < L::QT; ++k) g[k] = ld(gg + k * S, cell);
         }
         uint32_t pdirs = 0u;
         FaceRules fr{};
         R ux = R(0), uy = R(0), uz = R(0);
         if (BND == 2 && a.bb.pres) {
-            const Nbr nb(G, cell);
+            const Nbr<L::DIMS> nb(G, cell);
             if ((nb.faces & (uint32_t)a.bb.pres) && !(a.mask && (a.mask[cell] & MASK_SOLID))) {
-                fr = face_rules(a.bb, nb.faces);
+                fr = face_rules<L>(a.bb, nb.faces);
                 pdirs = fr.pres;
                 const Macro<R> m = macros<R, TH>(h, g, a.col);
                 ux = m.ux;
@@ -351,39 +362,39 @@ __global__ void __launch_bounds__(BLOCK) k_aa_step(StepArgs<R> a)
         collide<R, TH>(h, g, a.col);
         if (BND == 2 && pdirs) {
 #pragma unroll
-            for (int p = 1; p < Q19; ++p)
-                if ((pdirs >> p) & 1u) h[p] = pres_value(a.bb, gov_face(fr, p), p, h[p], ux, uy, uz);
+            for (int p = 1; p < L::Q; ++p)
+                if ((pdirs >> p) & 1u) h[p] = pres_value<L>(a.bb, gov_face<L>(fr, p), p, h[p], ux, uy, uz);
         }
 #pragma unroll
-        for (int q = 0; q < Q19; ++q) st(f + opp19(q) * S, cell, h[q]);
+        for (int q = 0; q < L::Q; ++q) st(f + opp(q) * S, cell, h[q]);
         if (TH) {
 #pragma unroll
-            for (int k = 0; k < Q7; ++k) st(gg + opp7(k) * S, cell, g[k]);
+            for (int k = 0; k < L::QT; ++k) st(gg + opp(k) * S, cell, g[k]);
         }
         return;
     }
-    const Nbr nb(G, cell);
+    const Nbr<L::DIMS> nb(G, cell);
     Blocked b{0u, 0u, 0u, false};
-    if (BND) b = blocked_dirs(a.bb, a.mask, cell, nb.faces);
+    if (BND) b = blocked_dirs<L>(a.bb, a.mask, cell, nb.faces);
     const uint32_t blk = b.wall | b.solid;           // a fluid cell's blocked directions
     const uint32_t skip = b.wall | b.claim;          // usual odd-step stores to leave out
     const bool near = BND && !b.is_solid && blk != 0;
     FaceRules fr{};
-    if (BND == 2 && near) fr = face_rules(a.bb, nb.faces);
+    if (BND == 2 && near) fr = face_rules<L>(a.bb, nb.faces);
 #pragma unroll
-    for (int q = 0; q < Q19; ++q) h[q] = ld(f + opp19(q) * S, cell + nb.at(-cx19(q), -cy19(q), -cz19(q)));
+    for (int q = 0; q < L::Q; ++q) h[q] = ld(f + opp(q) * S, cell + nb.at(-L::cx(q), -L::cy(q), -L::cz(q)));
     if (TH) {
 #pragma unroll
-        for (int k = 0; k < Q7; ++k) g[k] = ld(gg + opp7(k) * S, cell + nb.at(-cx7(k), -cy7(k), -cz7(k)));
+        for (int k = 0; k < L::QT; ++k) g[k] = ld(gg + opp(k) * S, cell + nb.at(-L::cxT(k), -L::cyT(k), -L::czT(k)));
     }
     if (near) {
 #pragma unroll
-        for (int q = 1; q < Q19; ++q)
-            if ((blk >> opp19(q)) & 1u) h[q] = blocked_inflow<R, BND>(f, S, cell, nb, fr, a.bb, q);
+        for (int q = 1; q < L::Q; ++q)
+            if ((blk >> opp(q)) & 1u) h[q] = blocked_inflow<L, R, BND>(f, S, cell, nb, fr, a.bb, q);
         if (TH) {
 #pragma unroll
-            for (int k = 1; k < Q7; ++k)
-                if ((blk >> opp7(k)) & 1u) g[k] = bounce7(a.bb, b, opp7(k), ld(gg + k * S, cell));
+            for (int k = 1; k < L::QT; ++k)
+                if ((blk >> opp(k)) & 1u) g[k] = bounce7(a.bb, b, opp(k), ld(gg + k * S, cell));
         }
     }
     R ux = R(0), uy = R(0), uz = R(0);
@@ -396,21 +407,21 @@ __global__ void __launch_bounds__(BLOCK) k_aa_step(StepArgs<R> a)
     }
     collide<R, TH>(h, g, a.col);
 #pragma unroll
-    for (int q = 0; q < Q19; ++q)
-        if (!BND || !((skip >> q) & 1u)) st(f + q * S, cell + nb.at(cx19(q), cy19(q), cz19(q)), h[q]);
+    for (int q = 0; q < L::Q; ++q)
+        if (!BND || !((skip >> q) & 1u)) st(f + q * S, cell + nb.at(L::cx(q), L::cy(q), L::cz(q)), h[q]);
     if (TH) {
 #pragma unroll
-        for (int k = 0; k < Q7; ++k)
-            if (!BND || !((skip >> k) & 1u)) st(gg + k * S, cell + nb.at(cx7(k), cy7(k), cz7(k)), g[k]);
+        for (int k = 0; k < L::QT; ++k)
+            if (!BND || !((skip >> k) & 1u)) st(gg + k * S, cell + nb.at(L::cxT(k), L::cyT(k), L::czT(k)), g[k]);
     }
     if (near) {
 #pragma unroll
-        for (int p = 1; p < Q19; ++p)
-            if ((blk >> p) & 1u) blocked_outflow<R, BND>(f, S, cell, nb, fr, a.bb, p, h[p], ux, uy, uz);
+        for (int p = 1; p < L::Q; ++p)
+            if ((blk >> p) & 1u) blocked_outflow<L, R, BND>(f, S, cell, nb, fr, a.bb, p, h[p], ux, uy, uz);
         if (TH) {
 #pragma unroll
-            for (int k = 1; k < Q7; ++k)
-                if ((blk >> k) & 1u) st(gg + opp7(k) * S, cell, bounce7(a.bb, b, k, g[k]));
+            for (int k = 1; k < L::QT; ++k)
+                if ((blk >> k) & 1u) st(gg + opp(k) * S, cell, bounce7(a.bb, b, k, g[k]));
         }
     }
 }
@@ -420,23 +431,23 @@ __global__ void __launch_bounds__(BLOCK) k_aa_step(StepArgs<R> a)
 // Collide in place: every population stays in its own slot (solid cells
 // compute on NaN in theirs; no fluid cell pulls from a solid slot).  Cells on
 // a PRESSURE face keep their velocity for the pull's anti-bounce-back.
-template <typename R, bool TH, int BND>
+template <class L, typename R, bool TH, int BND>
 __global__ void __launch_bounds__(BLOCK) k_ab_collide(StepArgs<R> a)
 {
     const Geometry& G = a.geo;
     const int32_t cell = (int32_t)(blockIdx.x * BLOCK + threadIdx.x);
     if (cell >= G.ncell) return;
     const int64_t S = G.stride;
-    R h[Q19];
-    R g[Q7];
+    R h[L::Q];
+    R g[L::QT];
 #pragma unroll
-    for (int q = 0; q < Q19; ++q) h[q] = ld(a.f + q * S, cell);
+    for (int q = 0; q < L::Q; ++q) h[q] = ld(a.f + q * S, cell);
     if (TH) {
 #pragma unroll
-        for (int k = 0; k < Q7; ++k) g[k] = ld(a.g + k * S, cell);
+        for (int k = 0; k < L::QT; ++k) g[k] = ld(a.g + k * S, cell);
     }
     if (BND == 2 && a.bb.pres) {
-        const Nbr nb(G, cell);
+        const Nbr<L::DIMS> nb(G, cell);
         if ((nb.faces & (uint32_t)a.bb.pres) && !(a.mask && (a.mask[cell] & MASK_SOLID))) {
             const Macro<R> m = macros<R, TH>(h, g, a.col);
             keep_face_velocity(a.bb, G, nb, m.ux, m.uy, m.uz);
@@ -444,10 +455,10 @@ __global__ void __launch_bounds__(BLOCK) k_ab_collide(StepArgs<R> a)
     }
     collide<R, TH>(h, g, a.col);
 #pragma unroll
-    for (int q = 0; q < Q19; ++q) st(a.f + q * S, cell, h[q]);
+    for (int q = 0; q < L::Q; ++q) st(a.f + q * S, cell, h[q]);
     if (TH) {
 #pragma unroll
-        for (int k = 0; k < Q7; ++k) st(a.g + k * S, cell, g[k]);
+        for (int k = 0; k < L::QT; ++k) st(a.g + k * S, cell, g[k]);
     }
 }
 
@@ -455,20 +466,20 @@ __global__ void __launch_bounds__(BLOCK) k_ab_collide(StepArgs<R> a)
 // x - c_q is across a face or a solid cell the population returns by the
 // link's rule: from x itself, B(q, x) = A(opp q, x) (bounce-back; less the
 // moving-wall term for VELOCITY; anti-bounce-back for PRESSURE, and for a
-// Dirichlet D3Q7 link), or for SLIP from x - c_t along q reflected.
-template <typename R, bool TH, int BND>
+// Dirichlet D3L::QT link), or for SLIP from x - c_t along q reflected.
+template <class L, typename R, bool TH, int BND>
 __global__ void __launch_bounds__(BLOCK) k_ab_pull(StepArgs<R> a)
 {
     const Geometry& G = a.geo;
     const int32_t cell = (int32_t)(blockIdx.x * BLOCK + threadIdx.x);
     if (cell >= G.ncell) return;
     const int64_t S = G.stride;
-    const Nbr nb(G, cell);
+    const Nbr<L::DIMS> nb(G, cell);
     Blocked b{0u, 0u, 0u, false};
-    if (BND) b = blocked_dirs(a.bb, a.mask, cell, nb.faces);
+    if (BND) b = blocked_dirs<L>(a.bb, a.mask, cell, nb.faces);
     const uint32_t blk = b.is_solid ? 0u : (b.wall | b.solid);
     FaceRules fr{};
-    if (BND == 2 && blk) fr = face_rules(a.bb, nb.faces);
+    if (BND == 2 && blk) fr = face_rules<L>(a.bb, nb.faces);
     R ux = R(0), uy = R(0), uz = R(0);
     if (BND == 2 && fr.pres) {
         const int f = __builtin_ctz(nb.faces & (uint32_t)a.bb.pres);  // any of its PRESSURE faces
@@ -478,28 +489,28 @@ __global__ void __launch_bounds__(BLOCK) k_ab_pull(StepArgs<R> a)
         uz = a.bb.face_vel[i + 2 * a.bb.face_area[f]];
     }
 #pragma unroll
-    for (int q = 0; q < Q19; ++q) {
-        R v = ld(a.f + q * S, cell + nb.at(-cx19(q), -cy19(q), -cz19(q)));
-        const int p = opp19(q);
+    for (int q = 0; q < L::Q; ++q) {
+        R v = ld(a.f + q * S, cell + nb.at(-L::cx(q), -L::cy(q), -L::cz(q)));
+        const int p = opp(q);
         if (BND && ((blk >> p) & 1u)) {
             if (BND == 2 && ((fr.slip >> p) & 1u)) {
                 const int ax = gov_axis(fr, p);
-                const int src = ax == 0 ? refl19(0, q) : (ax == 1 ? refl19(1, q) : refl19(2, q));
+                const int src = ax == 0 ? refl<L>(0, q) : (ax == 1 ? refl<L>(1, q) : refl<L>(2, q));
                 v = ld(a.f + src * S,
-                       cell + nb.at(ax == 0 ? 0 : -cx19(q), ax == 1 ? 0 : -cy19(q), ax == 2 ? 0 : -cz19(q)));
+                       cell + nb.at(ax == 0 ? 0 : -L::cx(q), ax == 1 ? 0 : -L::cy(q), ax == 2 ? 0 : -L::cz(q)));
             } else {
                 v = ld(a.f + p * S, cell);
-                if (BND == 2 && ((fr.vel >> p) & 1u)) v -= vel_shift(a.bb, gov_face(fr, p), p);
-                if (BND == 2 && ((fr.pres >> p) & 1u)) v = pres_value(a.bb, gov_face(fr, p), p, v, ux, uy, uz);
+                if (BND == 2 && ((fr.vel >> p) & 1u)) v -= vel_shift<L>(a.bb, gov_face<L>(fr, p), p);
+                if (BND == 2 && ((fr.pres >> p) & 1u)) v = pres_value<L>(a.bb, gov_face<L>(fr, p), p, v, ux, uy, uz);
             }
         }
         st(a.f2 + q * S, cell, v);
     }
     if (TH) {
 #pragma unroll
-        for (int k = 0; k < Q7; ++k) {
-            R v = ld(a.g + k * S, cell + nb.at(-cx7(k), -cy7(k), -cz7(k)));
-            if (BND && ((blk >> opp7(k)) & 1u)) v = bounce7(a.bb, b, opp7(k), ld(a.g + opp7(k) * S, cell));
+        for (int k = 0; k < L::QT; ++k) {
+            R v = ld(a.g + k * S, cell + nb.at(-L::cxT(k), -L::cyT(k), -L::czT(k)));
+            if (BND && ((blk >> opp(k)) & 1u)) v = bounce7(a.bb, b, opp(k), ld(a.g + opp(k) * S, cell));
             st(a.g2 + k * S, cell, v);
         }
     }
@@ -529,56 +540,57 @@ __device__ __forceinline__ LinkSlots link_slots(int mode, int p, int32_t cell, i
 {
     LinkSlots s;
     if (mode == LINK_AA_AFTER_EVEN) {
-        s.src_plane = opp_rt(p);
+        s.src_plane = opp(p);
         s.src_idx = cell;
         s.dst_plane = p;
         s.dst_idx = cellw;
     } else if (mode == LINK_AA_AFTER_ODD) {
         s.src_plane = p;
         s.src_idx = cellw;
-        s.dst_plane = opp_rt(p);
+        s.dst_plane = opp(p);
         s.dst_idx = cell;
     } else {
         s.src_plane = p;
         s.src_idx = cell;
-        s.dst_plane = opp_rt(p);
+        s.dst_plane = opp(p);
         s.dst_idx = cell;
     }
     return s;
 }
 
-// Per-link contribution to the group sums.  A D3Q19 link hands the boundary
+// Per-link contribution to the group sums.  A D3L::Q link hands the boundary
 // the momentum it carries out minus what it brings back, c_p f_out - c_in
 // f_in (stored values are f - w): 2 c_p f_p^+ for a wall or solid,
 // (c_p - c_p reflected) f_p^+ for SLIP, c_p (f_out + f_in) for VELOCITY and
-// PRESSURE.  A Dirichlet D3Q7 link passes w T_w - 2 g_p^+ into the fluid.
+// PRESSURE.  A Dirichlet D3L::QT link passes w T_w - 2 g_p^+ into the fluid.
 // `returned` says whether v is the returning value (else the leaving one);
 // a PRESSURE link needs only the cell's velocity, from the face planes.
 struct LinkSum {
     double fx, fy, fz, q;
 };
 
+template <class L>
 __device__ __forceinline__ int refl_rt(int a, int p)
 {
-    const int c[3] = {dir_comp(CX19, p), dir_comp(CY19, p), dir_comp(CZ19, p)};
-    for (int r = 1; r < Q19; ++r)
-        if (dir_comp(CX19, r) == (a == 0 ? -c[0] : c[0]) && dir_comp(CY19, r) == (a == 1 ? -c[1] : c[1]) &&
-            dir_comp(CZ19, r) == (a == 2 ? -c[2] : c[2]))
+    const int c[3] = {dir_comp(Packed<L>::X, p), dir_comp(Packed<L>::Y, p), dir_comp(Packed<L>::Z, p)};
+    for (int r = 1; r < L::Q; ++r)
+        if (dir_comp(Packed<L>::X, r) == (a == 0 ? -c[0] : c[0]) && dir_comp(Packed<L>::Y, r) == (a == 1 ? -c[1] : c[1]) &&
+            dir_comp(Packed<L>::Z, r) == (a == 2 ? -c[2] : c[2]))
             return r;
     return 0;
 }
 
-template <typename R>
+template <class L, typename R>
 __device__ __forceinline__ LinkSum link_sum(const LinkArgs<R>& a, uint32_t meta, int p, int32_t grp, R v,
                                             bool returned, int64_t l)
 {
     LinkSum c{0.0, 0.0, 0.0, 0.0};
-    if (meta & LINK_D3Q7) {
+    if (meta & LINK_TEMP) {
         if (meta & LINK_DIRICHLET) c.q = a.omega * a.wall_T[grp] - 2.0 * (double)v;
         return c;
     }
-    const double cp[3] = {(double)dir_comp(CX19, p), (double)dir_comp(CY19, p), (double)dir_comp(CZ19, p)};
-    const double w = w19_rt(p);
+    const double cp[3] = {(double)dir_comp(Packed<L>::X, p), (double)dir_comp(Packed<L>::Y, p), (double)dir_comp(Packed<L>::Z, p)};
+    const double w = L::w(p);
     const uint32_t rule = (meta >> LINK_RULE_SHIFT) & 3u;
     double s = 0.0;  // F = s c_p, except SLIP
     if (rule == RULE_WALL) {
@@ -614,7 +626,7 @@ __device__ __forceinline__ LinkSum link_sum(const LinkArgs<R>& a, uint32_t meta,
 template <typename R>
 __device__ __forceinline__ R link_value(const LinkArgs<R>& a, uint32_t meta, int32_t grp, R v)
 {
-    if ((meta & LINK_D3Q7) && (meta & LINK_DIRICHLET)) return (R)(a.omega * a.wall_T[grp]) - v;
+    if ((meta & LINK_TEMP) && (meta & LINK_DIRICHLET)) return (R)(a.omega * a.wall_T[grp]) - v;
     return v;
 }
 
@@ -630,7 +642,7 @@ __global__ void __launch_bounds__(BLOCK) k_link_gather(LinkArgs<R> a)
     const int64_t S = a.geo.stride;
     const uint32_t meta = a.meta[l];
     const LinkSlots sl = link_slots(a.mode, (int)(meta & LINK_DIR_MASK), a.cell[l], a.cellw[l]);
-    const R* src = (meta & LINK_D3Q7) ? a.g_src : a.f_src;
+    const R* src = (meta & LINK_TEMP) ? a.g_src : a.f_src;
     a.scratch[l] = ld(src + sl.src_plane * S, sl.src_idx);
 }
 
@@ -644,7 +656,7 @@ __global__ void __launch_bounds__(BLOCK) k_link_scatter(LinkArgs<R> a)
     const uint32_t meta = a.meta[l];
     const int32_t grp = (int32_t)((meta >> LINK_GROUP_SHIFT) & LINK_GROUP_MASK);
     const LinkSlots sl = link_slots(a.mode, (int)(meta & LINK_DIR_MASK), a.cell[l], a.cellw[l]);
-    R* dst = (meta & LINK_D3Q7) ? a.g_dst : a.f_dst;
+    R* dst = (meta & LINK_TEMP) ? a.g_dst : a.f_dst;
     st(dst + sl.dst_plane * S, sl.dst_idx, link_value(a, meta, grp, a.scratch[l]));
 }
 
@@ -659,7 +671,7 @@ __global__ void __launch_bounds__(BLOCK) k_link_direct(LinkArgs<R> a)
     const uint32_t meta = a.meta[l];
     const int32_t grp = (int32_t)((meta >> LINK_GROUP_SHIFT) & LINK_GROUP_MASK);
     const LinkSlots sl = link_slots(a.mode, (int)(meta & LINK_DIR_MASK), a.cell[l], a.cellw[l]);
-    const bool g7 = (meta & LINK_D3Q7) != 0;
+    const bool g7 = (meta & LINK_TEMP) != 0;
     const R v = ld((g7 ? a.g_src : a.f_src) + sl.src_plane * S, sl.src_idx);
     st((g7 ? a.g_dst : a.f_dst) + sl.dst_plane * S, sl.dst_idx, link_value(a, meta, grp, v));
 }
@@ -668,13 +680,13 @@ __global__ void __launch_bounds__(BLOCK) k_link_direct(LinkArgs<R> a)
 // the bounced population f_p^+ of each link where the step left it: with
 // in-kernel bounce-back (opp p, x) in place (the even step's usual store or
 // the odd step's bounce-back store); with link passes the scatter
-// destination; with two buffers B(opp p, x).  Values a D3Q7 Dirichlet link stores after
+// destination; with two buffers B(opp p, x).  Values a D3L::QT Dirichlet link stores after
 // anti-bounce-back are converted back.  It sums the momentum exchange
 // 2 c_p f_p^+ and the heat w T_w - 2 g_p^+ per group: wavefront shuffles, then
 // fp64 LDS atomics per block, then one global atomic per block and touched
 // group; a grid-stride loop keeps the block count (and the global atomics)
 // small.
-template <typename R>
+template <class L, typename R>
 __global__ void __launch_bounds__(BLOCK) k_link_force(LinkArgs<R> a)
 {
     __shared__ double acc[4 * LBM_GROUPS];
@@ -689,12 +701,12 @@ __global__ void __launch_bounds__(BLOCK) k_link_force(LinkArgs<R> a)
             const uint32_t meta = a.meta[l];
             const int p = (int)(meta & LINK_DIR_MASK);
             grp = (int32_t)((meta >> LINK_GROUP_SHIFT) & LINK_GROUP_MASK);
-            const bool g7 = (meta & LINK_D3Q7) != 0;
+            const bool g7 = (meta & LINK_TEMP) != 0;
             int32_t plane, idx;
             bool transformed;
             if (a.in_kernel && a.mode != LINK_AB) {
                 // even step: the usual store; odd step: the bounce-back store
-                plane = opp_rt(p);
+                plane = opp(p);
                 idx = a.cell[l];
                 transformed = a.mode == LINK_AA_AFTER_ODD;
             } else {
@@ -706,12 +718,12 @@ __global__ void __launch_bounds__(BLOCK) k_link_force(LinkArgs<R> a)
             }
             if (!g7 && transformed && ((meta >> LINK_RULE_SHIFT) & 3u) == RULE_SLIP) {
                 // the reflected population landed at x + c_t
-                plane = refl_rt((int)((meta >> LINK_AXIS_SHIFT) & 3u), p);
+                plane = refl_rt<L>((int)((meta >> LINK_AXIS_SHIFT) & 3u), p);
                 idx = a.cellw[l];
             }
             R v = ld((g7 ? a.g_dst : a.f_dst) + plane * S, idx);
             if (transformed && g7 && (meta & LINK_DIRICHLET)) v = (R)(a.omega * a.wall_T[grp]) - v;
-            c = link_sum(a, meta, p, grp, v, transformed, l);
+            c = link_sum<L>(a, meta, p, grp, v, transformed, l);
         }
         const int32_t lead = __shfl(grp, 0, 64);
         if (__all(grp == lead || grp < 0)) {
@@ -739,31 +751,31 @@ __global__ void __launch_bounds__(BLOCK) k_link_force(LinkArgs<R> a)
 
 // ------------------------------------------------------ init / read
 
-template <typename R, bool TH>
+template <class L, typename R, bool TH>
 __global__ void __launch_bounds__(BLOCK) k_init(FieldArgs<R> a)
 {
     const Geometry& G = a.geo;
     const int32_t cell = (int32_t)(blockIdx.x * BLOCK + threadIdx.x);
     if (cell >= G.ncell) return;
     const int64_t S = G.stride;
-    R h[Q19];
-    R g[Q7];
+    R h[L::Q];
+    R g[L::QT];
     if (a.mask && (a.mask[cell] & MASK_SOLID)) {
         const R nan = (R)__builtin_nan("");
 #pragma unroll
-        for (int q = 0; q < Q19; ++q) h[q] = nan;
+        for (int q = 0; q < L::Q; ++q) h[q] = nan;
 #pragma unroll
-        for (int k = 0; k < Q7; ++k) g[k] = nan;
+        for (int k = 0; k < L::QT; ++k) g[k] = nan;
     } else {
         const int32_t n = G.ncell;
         const R T = (TH && a.T) ? a.T[cell] : R(0);
         equilibrium<R, TH>(a.rho[cell], a.u[cell], a.u[n + cell], a.u[2 * n + cell], T, a.col.a_T, h, g);
     }
 #pragma unroll
-    for (int q = 0; q < Q19; ++q) a.f[q * S + cell] = h[q];
+    for (int q = 0; q < L::Q; ++q) a.f[q * S + cell] = h[q];
     if (TH) {
 #pragma unroll
-        for (int k = 0; k < Q7; ++k) a.g[k * S + cell] = g[k];
+        for (int k = 0; k < L::QT; ++k) a.g[k * S + cell] = g[k];
     }
 }
 
@@ -771,40 +783,40 @@ __global__ void __launch_bounds__(BLOCK) k_init(FieldArgs<R> a)
 // (or with two buffers) in the cell's own slots, after an odd number where
 // the last odd step stored them, (opposite(q), x - c_q), with in-kernel
 // bounce-back's re-read of blocked inflows.  Returns false for a solid cell.
-template <typename R, bool TH>
+template <class L, typename R, bool TH>
 __device__ __forceinline__ bool load_cell(const FieldArgs<R>& a, int32_t cell, R* h, R* g)
 {
     const Geometry& G = a.geo;
     const int64_t S = G.stride;
     if (a.ab || a.parity == 0) {
 #pragma unroll
-        for (int q = 0; q < Q19; ++q) h[q] = a.f[q * S + cell];
+        for (int q = 0; q < L::Q; ++q) h[q] = a.f[q * S + cell];
         if (TH) {
 #pragma unroll
-            for (int k = 0; k < Q7; ++k) g[k] = a.g[k * S + cell];
+            for (int k = 0; k < L::QT; ++k) g[k] = a.g[k * S + cell];
         }
     } else {
-        const Nbr nb(G, cell);
+        const Nbr<L::DIMS> nb(G, cell);
 #pragma unroll
-        for (int q = 0; q < Q19; ++q) h[q] = a.f[opp19(q) * S + (cell + nb.at(-cx19(q), -cy19(q), -cz19(q)))];
+        for (int q = 0; q < L::Q; ++q) h[q] = a.f[opp(q) * S + (cell + nb.at(-L::cx(q), -L::cy(q), -L::cz(q)))];
         if (TH) {
 #pragma unroll
-            for (int k = 0; k < Q7; ++k) g[k] = a.g[opp7(k) * S + (cell + nb.at(-cx7(k), -cy7(k), -cz7(k)))];
+            for (int k = 0; k < L::QT; ++k) g[k] = a.g[opp(k) * S + (cell + nb.at(-L::cxT(k), -L::cyT(k), -L::czT(k)))];
         }
         // with in-kernel boundary rules, an inflow from across a face or a
         // solid is the returning population the even step left behind
         if (a.bb.in_kernel) {
-            const Blocked b = blocked_dirs(a.bb, a.mask, cell, nb.faces);
+            const Blocked b = blocked_dirs<L>(a.bb, a.mask, cell, nb.faces);
             const uint32_t blk = b.is_solid ? 0u : (b.wall | b.solid);
             if (blk != 0) {
-                const FaceRules fr = face_rules(a.bb, nb.faces);
+                const FaceRules fr = face_rules<L>(a.bb, nb.faces);
 #pragma unroll
-                for (int q = 1; q < Q19; ++q)
-                    if ((blk >> opp19(q)) & 1u) h[q] = blocked_inflow<R, 2>(a.f, S, cell, nb, fr, a.bb, q);
+                for (int q = 1; q < L::Q; ++q)
+                    if ((blk >> opp(q)) & 1u) h[q] = blocked_inflow<L, R, 2>(a.f, S, cell, nb, fr, a.bb, q);
                 if (TH) {
 #pragma unroll
-                    for (int k = 1; k < Q7; ++k)
-                        if ((blk >> opp7(k)) & 1u) g[k] = bounce7(a.bb, b, opp7(k), a.g[k * S + cell]);
+                    for (int k = 1; k < L::QT; ++k)
+                        if ((blk >> opp(k)) & 1u) g[k] = bounce7(a.bb, b, opp(k), a.g[k * S + cell]);
                 }
             }
         }
@@ -819,17 +831,17 @@ __device__ __forceinline__ bool finite_macros(const Macro<R>& m)
            __builtin_isfinite(m.uy) && __builtin_isfinite(m.uz);
 }
 
-template <typename R, bool TH>
+template <class L, typename R, bool TH>
 __global__ void __launch_bounds__(BLOCK) k_read(FieldArgs<R> a)
 {
     const Geometry& G = a.geo;
     const int32_t cell = (int32_t)(blockIdx.x * BLOCK + threadIdx.x);
     if (cell >= G.ncell) return;
     const int32_t n = G.ncell;
-    R h[Q19];
-    R g[Q7];
+    R h[L::Q];
+    R g[L::QT];
     Macro<R> m;
-    if (!load_cell<R, TH>(a, cell, h, g)) {
+    if (!load_cell<L, R, TH>(a, cell, h, g)) {
         const R nan = (R)__builtin_nan("");
         m.rho = m.ux = m.uy = m.uz = m.T = nan;
     } else {
@@ -851,7 +863,7 @@ __global__ void __launch_bounds__(BLOCK) k_read(FieldArgs<R> a)
 // read-back).  Grid-stride over cells; wavefront shuffles, then LDS across
 // the block's wavefronts, then one global atomic per block and value (the
 // maximum through the ordering of non-negative doubles' bit patterns).
-template <typename R, bool TH>
+template <class L, typename R, bool TH>
 __global__ void __launch_bounds__(BLOCK) k_diag(FieldArgs<R> a, double* out)
 {
     constexpr int NS = LBM_DIAG_COUNT;  // slot LBM_DIAG_UMAX holds max |u|^2
@@ -862,9 +874,9 @@ __global__ void __launch_bounds__(BLOCK) k_diag(FieldArgs<R> a, double* out)
     const int32_t n = a.geo.ncell;
     for (int32_t cell = (int32_t)(blockIdx.x * BLOCK + threadIdx.x); cell < n;
          cell += (int32_t)(gridDim.x * BLOCK)) {
-        R h[Q19];
-        R g[Q7];
-        if (!load_cell<R, TH>(a, cell, h, g)) continue;
+        R h[L::Q];
+        R g[L::QT];
+        if (!load_cell<L, R, TH>(a, cell, h, g)) continue;
         const Macro<R> m = macros<R, TH>(h, g, a.col);
         if (!finite_macros(m)) atomicOr(a.unstable, 1);
         const double rho = m.rho, ux = m.ux, uy = m.uy, uz = m.uz, T = TH ? (double)m.T : 0.0;
@@ -931,31 +943,31 @@ inline dim3 grid_for(int64_t n) { return dim3((unsigned)((n + BLOCK - 1) / BLOCK
         const dim3 grid_ = grid_for((a).geo.ncell);                                                         \
         const int bnd_ = (a).bb.in_kernel ? (((a).bb.slip | (a).bb.vel | (a).bb.pres) ? 2 : 1) : 0;        \
         if (thermal) {                                                                                      \
-            if (bnd_ == 2) hipLaunchKernelGGL((KERNEL<R, true, 2>), grid_, dim3(BLOCK), 0, s, a);           \
-            else if (bnd_ == 1) hipLaunchKernelGGL((KERNEL<R, true, 1>), grid_, dim3(BLOCK), 0, s, a);      \
-            else hipLaunchKernelGGL((KERNEL<R, true, 0>), grid_, dim3(BLOCK), 0, s, a);                     \
+            if (bnd_ == 2) hipLaunchKernelGGL((KERNEL<L, R, true, 2>), grid_, dim3(BLOCK), 0, s, a);        \
+            else if (bnd_ == 1) hipLaunchKernelGGL((KERNEL<L, R, true, 1>), grid_, dim3(BLOCK), 0, s, a);   \
+            else hipLaunchKernelGGL((KERNEL<L, R, true, 0>), grid_, dim3(BLOCK), 0, s, a);                  \
         } else {                                                                                            \
-            if (bnd_ == 2) hipLaunchKernelGGL((KERNEL<R, false, 2>), grid_, dim3(BLOCK), 0, s, a);          \
-            else if (bnd_ == 1) hipLaunchKernelGGL((KERNEL<R, false, 1>), grid_, dim3(BLOCK), 0, s, a);     \
-            else hipLaunchKernelGGL((KERNEL<R, false, 0>), grid_, dim3(BLOCK), 0, s, a);                    \
+            if (bnd_ == 2) hipLaunchKernelGGL((KERNEL<L, R, false, 2>), grid_, dim3(BLOCK), 0, s, a);       \
+            else if (bnd_ == 1) hipLaunchKernelGGL((KERNEL<L, R, false, 1>), grid_, dim3(BLOCK), 0, s, a);  \
+            else hipLaunchKernelGGL((KERNEL<L, R, false, 0>), grid_, dim3(BLOCK), 0, s, a);                 \
         }                                                                                                   \
     } while (0)
 
-template <typename R>
+template <class L, typename R>
 hipError_t launch_aa_step(const StepArgs<R>& a, bool thermal, hipStream_t s)
 {
     LBM_CELL_LAUNCH(k_aa_step, a, thermal, s);
     return hipGetLastError();
 }
 
-template <typename R>
+template <class L, typename R>
 hipError_t launch_ab_collide(const StepArgs<R>& a, bool thermal, hipStream_t s)
 {
     LBM_CELL_LAUNCH(k_ab_collide, a, thermal, s);
     return hipGetLastError();
 }
 
-template <typename R>
+template <class L, typename R>
 hipError_t launch_ab_pull(const StepArgs<R>& a, bool thermal, hipStream_t s)
 {
     LBM_CELL_LAUNCH(k_ab_pull, a, thermal, s);
@@ -986,37 +998,37 @@ hipError_t launch_link_direct(const LinkArgs<R>& a, hipStream_t s)
     return hipGetLastError();
 }
 
-template <typename R>
+template <class L, typename R>
 hipError_t launch_link_force(const LinkArgs<R>& a, hipStream_t s)
 {
     if (a.end <= a.begin) return hipSuccess;
     const int64_t blocks = std::min<int64_t>((a.end - a.begin + BLOCK - 1) / BLOCK, 1024);
-    hipLaunchKernelGGL((k_link_force<R>), dim3((unsigned)blocks), dim3(BLOCK), 0, s, a);
+    hipLaunchKernelGGL((k_link_force<L, R>), dim3((unsigned)blocks), dim3(BLOCK), 0, s, a);
     return hipGetLastError();
 }
 
-template <typename R>
+template <class L, typename R>
 hipError_t launch_init(const FieldArgs<R>& a, bool thermal, hipStream_t s)
 {
-    if (thermal) hipLaunchKernelGGL((k_init<R, true>), grid_for(a.geo.ncell), dim3(BLOCK), 0, s, a);
-    else hipLaunchKernelGGL((k_init<R, false>), grid_for(a.geo.ncell), dim3(BLOCK), 0, s, a);
+    if (thermal) hipLaunchKernelGGL((k_init<L, R, true>), grid_for(a.geo.ncell), dim3(BLOCK), 0, s, a);
+    else hipLaunchKernelGGL((k_init<L, R, false>), grid_for(a.geo.ncell), dim3(BLOCK), 0, s, a);
     return hipGetLastError();
 }
 
-template <typename R>
+template <class L, typename R>
 hipError_t launch_read(const FieldArgs<R>& a, bool thermal, hipStream_t s)
 {
-    if (thermal) hipLaunchKernelGGL((k_read<R, true>), grid_for(a.geo.ncell), dim3(BLOCK), 0, s, a);
-    else hipLaunchKernelGGL((k_read<R, false>), grid_for(a.geo.ncell), dim3(BLOCK), 0, s, a);
+    if (thermal) hipLaunchKernelGGL((k_read<L, R, true>), grid_for(a.geo.ncell), dim3(BLOCK), 0, s, a);
+    else hipLaunchKernelGGL((k_read<L, R, false>), grid_for(a.geo.ncell), dim3(BLOCK), 0, s, a);
     return hipGetLastError();
 }
 
-template <typename R>
+template <class L, typename R>
 hipError_t launch_diag(const FieldArgs<R>& a, bool thermal, double* out, hipStream_t s)
 {
     const unsigned blocks = (unsigned)std::min<int64_t>(((int64_t)a.geo.ncell + BLOCK - 1) / BLOCK, 2048);
-    if (thermal) hipLaunchKernelGGL((k_diag<R, true>), dim3(blocks), dim3(BLOCK), 0, s, a, out);
-    else hipLaunchKernelGGL((k_diag<R, false>), dim3(blocks), dim3(BLOCK), 0, s, a, out);
+    if (thermal) hipLaunchKernelGGL((k_diag<L, R, true>), dim3(blocks), dim3(BLOCK), 0, s, a, out);
+    else hipLaunchKernelGGL((k_diag<L, R, false>), dim3(blocks), dim3(BLOCK), 0, s, a, out);
     return hipGetLastError();
 }
 
@@ -1027,17 +1039,20 @@ hipError_t launch_zero_f64(double* p, int64_t n, hipStream_t s)
     return hipGetLastError();
 }
 
-#define LBM_INSTANTIATE(R)                                                               \
-    template hipError_t launch_aa_step<R>(const StepArgs<R>&, bool, hipStream_t);        \
-    template hipError_t launch_ab_collide<R>(const StepArgs<R>&, bool, hipStream_t);     \
-    template hipError_t launch_ab_pull<R>(const StepArgs<R>&, bool, hipStream_t);        \
-    template hipError_t launch_link_gather<R>(const LinkArgs<R>&, hipStream_t);          \
-    template hipError_t launch_link_scatter<R>(const LinkArgs<R>&, hipStream_t);         \
-    template hipError_t launch_link_direct<R>(const LinkArgs<R>&, hipStream_t);          \
-    template hipError_t launch_link_force<R>(const LinkArgs<R>&, hipStream_t);           \
-    template hipError_t launch_init<R>(const FieldArgs<R>&, bool, hipStream_t);          \
-    template hipError_t launch_read<R>(const FieldArgs<R>&, bool, hipStream_t);          \
-    template hipError_t launch_diag<R>(const FieldArgs<R>&, bool, double*, hipStream_t);
+#define LBM_INSTANTIATE_LATTICE(L, R)                                                      \
+    template hipError_t launch_aa_step<L, R>(const StepArgs<R>&, bool, hipStream_t);       \
+    template hipError_t launch_ab_collide<L, R>(const StepArgs<R>&, bool, hipStream_t);    \
+    template hipError_t launch_ab_pull<L, R>(const StepArgs<R>&, bool, hipStream_t);       \
+    template hipError_t launch_link_force<L, R>(const LinkArgs<R>&, hipStream_t);          \
+    template hipError_t launch_init<L, R>(const FieldArgs<R>&, bool, hipStream_t);         \
+    template hipError_t launch_read<L, R>(const FieldArgs<R>&, bool, hipStream_t);         \
+    template hipError_t launch_diag<L, R>(const FieldArgs<R>&, bool, double*, hipStream_t);
+#define LBM_INSTANTIATE(R)                                                                 \
+    template hipError_t launch_link_gather<R>(const LinkArgs<R>&, hipStream_t);            \
+    template hipError_t launch_link_scatter<R>(const LinkArgs<R>&, hipStream_t);           \
+    template hipError_t launch_link_direct<R>(const LinkArgs<R>&, hipStream_t);            \
+    LBM_INSTANTIATE_LATTICE(Lat3D, R)                                                      \
+    LBM_INSTANTIATE_LATTICE(Lat2D, R)
 
 LBM_INSTANTIATE(float)
 LBM_INSTANTIATE(double)

@@ -33,9 +33,12 @@ def gpu_run(w: inputs.Workload, submissions, dtype=4, streaming=binding.LBM_STRE
                 forces.append(s.wall_force())
         rho, u, T = s.macros()
         torch.cuda.synchronize()
+        # links19 / links7: the flow and temperature lattices' link counts
+        # (D2Q9 and D2Q5 on a 2D box)
+        flow, temp = (9, 5) if int(w.params.get("lattice", 0)) == 1 else (19, 7)
         out = dict(rho=rho.cpu().double().numpy(), u=u.cpu().double().numpy(),
                    T=T.cpu().double().numpy() if T is not None else None, forces=forces, time=s.time,
-                   links19=s.num_links(19), links7=s.num_links(7))
+                   links19=s.num_links(flow), links7=s.num_links(temp))
         if want_diag:
             out["diag"] = s.diagnostics()
         s.wall_force()  # raises LBM_E_UNSTABLE if the read-back saw a non-finite value

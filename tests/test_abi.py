@@ -43,7 +43,10 @@ def test_struct_layout_matches_header():
     assert P.T0.offset == 136 + 8 * (19 + 7 + 1 + 3 + 3)
     assert P.face_u.offset == P.T0.offset + 8
     assert P.face_rho.offset == P.face_u.offset + 8 * 18
-    assert binding.ctypes.sizeof(P) == P.face_rho.offset + 8 * 6
+    assert P.lattice.offset == P.face_rho.offset + 8 * 6
+    assert P.s9.offset == P.lattice.offset + 8
+    assert P.s5.offset == P.s9.offset + 8 * 9
+    assert binding.ctypes.sizeof(P) == P.s5.offset + 8 * 5
 
 
 def periodic(n=8, **kw):
@@ -189,3 +192,63 @@ def test_solid_link_counts_brute_force(lib, case):
     assert binding.lbm_count_links(p, lab, 19) == brute_force_links(p, lab, D3Q19)
     assert binding.lbm_count_links(p, lab, 7) == brute_force_links(p, lab, D3Q7)
     assert binding.lbm_required_bytes(p, lab) > binding.lbm_required_bytes(p, None)
+
+
+# ------------------------------------------------------------ 2D variant
+
+def square(n=8, **kw):
+    return inputs.base_params_2d(n, n, inputs.mrt_rates_2d(0.6), **kw)
+
+
+@pytest.mark.parametrize("mutate", [
+    lambda p: p.update(nz=2),
+    lambda p: p.update(face_kind=[0, 0, 0, 0, 1, 1]),
+    lambda p: p.update(lattice=2),
+    lambda p: p.__setitem__("s9", [2.5] + p["s9"][1:]),
+    lambda p: p.__setitem__("s5", [0.0, -0.1, 1.0, 1.0, 1.0]),
+    lambda p: p.update(a_T=-4.0),
+    lambda p: p.update(accel=[0.0, 0.0, 1e-5]),
+    lambda p: p.update(gbeta=[0.0, 0.0, 1e-5]),
+    lambda p: p.update(face_kind=[3, 3, 0, 0, 0, 0], face_u=[0, 0, 1e-3] + [0.0] * 15),
+])
+def test_invalid_2d_params_rejected(lib, mutate):
+    p = square()
+    assert binding.lbm_required_bytes(p) > 0
+    mutate(p)
+    assert binding.lbm_required_bytes(p) == 0
+    with pytest.raises(binding.LbmError) as e:
+        binding.lbm_create(p, None, 256, 1 << 30)
+    assert e.value.status == binding.LBM_E_INVALID
+
+
+def test_2d_sizes_and_lattice_numbers(lib):
+    n = 64
+    p = square(n, thermal=True, s5=[0, 1, 1, 1, 1])
+    b = binding.lbm_required_bytes(p, dtype=8)
+    assert 14 * n * n * 8 <= b < 19 * n * n * 8  # 9 + 5 planes, not 19 + 7
+    # a 2D box has D2Q9 / D2Q5 link lists only
+    assert binding.lbm_count_links(p, None, 19) == -1 and binding.lbm_count_links(p, None, 7) == -1
+    assert binding.lbm_count_links(p, None, 9) == 0 and binding.lbm_count_links(p, None, 5) == 0
+
+
+@pytest.mark.parametrize("n", [1, 2, 5, 16])
+def test_square_cavity_link_counts_closed_form(lib, n):
+    """All-wall square: D2Q9 links = 4 n (axis) + 4 (2n - 1) (diagonals);
+    D2Q5 links = 4 n."""
+    p = square(n, face_kind=[1] * 4, thermal=True, s5=[0, 1, 1, 1, 1])
+    assert binding.lbm_count_links(p, None, 9) == 4 * n + 4 * (2 * n - 1)
+    assert binding.lbm_count_links(p, None, 5) == 4 * n
+
+
+D2Q9 = [(a, b, 0) for a in (-1, 0, 1) for b in (-1, 0, 1)]
+D2Q5 = [(0, 0, 0), (1, 0, 0), (-1, 0, 0), (0, 1, 0), (0, -1, 0)]
+
+
+def test_2d_solid_link_counts_brute_force(lib):
+    nx, ny = 40, 31
+    lab = inputs.sphere_labels(nx, ny, 1, 6.0, centre=(12.0, 15.5, 0.5))
+    lab |= inputs.sphere_labels(nx, ny, 1, 4.0, centre=(38.0, 2.0, 0.5), label=2)  # wraps through x and y
+    p = inputs.base_params_2d(nx, ny, inputs.mrt_rates_2d(0.6), face_kind=[0, 0, 1, 1], thermal=True,
+                              s5=[0, 1, 1, 1, 1])
+    assert binding.lbm_count_links(p, lab, 9) == brute_force_links(p, lab, D2Q9)
+    assert binding.lbm_count_links(p, lab, 5) == brute_force_links(p, lab, D2Q5)
