@@ -264,3 +264,18 @@ def test_graph_replays_match_eager_steps(streaming, links):
     finally:
         eager.close()
         graph.close()
+
+
+def test_sphere_drag_series_2000_steps():
+    """The sphere recipe's read-back pattern (a submission of 100 steps, then
+    the drag, 20 times) on a reduced box against the oracle's per-step force
+    record: every read-out within the force bar."""
+    say("CASE sphere drag series 32x26x24 R=5, 20 x 100 steps")
+    w = inputs.sphere128(shape=(32, 26, 24), R=5.0, gx=1e-5)
+    g = gpu_run(w, [100] * 20, dtype=4)
+    o = oracle_run(w, 2000, want_diag=True)
+    for i, f in enumerate(g["forces"]):
+        check_forces(f, o["diag"][100 * (i + 1) - 1], 4, g["links19"], f"drag at {100 * (i + 1)}")
+    drag = np.array([f[6, 0] for f in g["forces"]])
+    assert np.all(np.diff(drag) > 0)  # the flow spins up from rest: the drag grows
+    check_fields(g, o, w, 4, "sphere 2000")
