@@ -30,7 +30,14 @@ struct Geometry {
     int32_t nxy;
     int32_t ncell;
     int32_t pad0;
-    int64_t stride;  // elements between consecutive population planes
+    // population buffers: cells in tiles of 2^tile_lg consecutive cells, each
+    // tile holding its planes one after another (tile_lg = 31: one tile, the
+    // plain structure of arrays)
+    int64_t qstride;     // elements between planes inside a tile
+    uint32_t tile_f;     // elements between consecutive tiles of a flow-lattice buffer (< 2^24)
+    uint32_t tile_g;     // elements between consecutive tiles of a temperature-lattice buffer (< 2^24)
+    uint32_t tile_lg;
+    uint32_t tile_mask;  // 2^tile_lg - 1
     DivMagic div_nx, div_ny;
 };
 

@@ -1,9 +1,12 @@
 // lbm_kernels.hip -- the HIP kernels of the fused lattice Boltzmann step (gfx950).
 //
-// Layout: structure of arrays, one plane of `stride` elements per population
-// direction, cell index x + nx*(y + ny*z) inside a plane ("Multi-GPU thermal
-// lattice Boltzmann simulations using OpenACC and MPI", Sec. 3: SoA so that
-// neighbouring threads touch neighbouring data).  One thread per cell, cells
+// Layout: structure of arrays, one plane per population direction, cell
+// index x + nx*(y + ny*z) inside a plane ("Multi-GPU thermal lattice
+// Boltzmann simulations using OpenACC and MPI", Sec. 3: SoA so that
+// neighbouring threads touch neighbouring data), optionally cut into tiles of
+// consecutive cells that hold all planes of the tile (the collected SoA of
+// "GPU Optimization for High-Quality Kinetic Fluid Simulation", Sec. 4.1);
+// see pos().  One thread per cell, cells
 // flattened, so a 64-lane wavefront reads and writes 64 consecutive elements
 // of each plane (256 B in fp32) whatever the box shape.
 //
@@ -84,20 +87,45 @@ struct Nbr {
     }
 };
 
-// Element `idx` of a population plane.  The plane base is uniform across the
-// wavefront (a scalar register) and the byte offset is a 32-bit unsigned
-// value, so loads and stores take the scalar-base + 32-bit-offset addressing
-// form instead of a 64-bit address per lane.  Requires stride * sizeof(R) <
-// 2^32 (checked on the host).
-template <typename R>
-__device__ __forceinline__ R ld(const R* plane, int32_t idx)
+// Position of population q of cell idx in a population buffer.  Cells are
+// grouped in tiles of 2^tile_lg consecutive cells; a tile holds the buffer's
+// planes one after another (plane q at q * qstride inside the tile) and
+// consecutive tiles lie ts elements apart.  With tile_lg = 31 the whole box
+// is one tile: plain structure of arrays, planes qstride apart.  The plane
+// part q * qstride is uniform across the wavefront (a scalar base) and the
+// per-lane part, the same for every plane, is a 32-bit element offset kept
+// below 2^32 bytes by the host's choice of layout, so loads and stores take
+// the scalar-base + 32-bit-offset addressing form instead of a 64-bit
+// address per lane.
+struct Slot {
+    int64_t plane;  // uniform: element offset of the plane's base
+    uint32_t off;   // per lane: element offset from the plane's base
+};
+
+__device__ __forceinline__ Slot pos(const Geometry& G, uint32_t ts, int q, int32_t idx)
 {
-    return *reinterpret_cast<const R*>(reinterpret_cast<const char*>(plane) + (uint32_t)idx * (uint32_t)sizeof(R));
+    const uint32_t u = (uint32_t)idx;
+    return Slot{(int64_t)q * G.qstride, __umul24(u >> G.tile_lg, ts) + (u & G.tile_mask)};
+}
+// flow-lattice (f) and temperature-lattice (g) buffers
+__device__ __forceinline__ Slot posf(const Geometry& G, int q, int32_t idx) { return pos(G, G.tile_f, q, idx); }
+__device__ __forceinline__ Slot posg(const Geometry& G, int q, int32_t idx) { return pos(G, G.tile_g, q, idx); }
+__device__ __forceinline__ Slot posb(const Geometry& G, bool temp, int q, int32_t idx)
+{
+    return temp ? posg(G, q, idx) : posf(G, q, idx);
+}
+
+template <typename R>
+__device__ __forceinline__ R ld(const R* base, Slot p)
+{
+    const char* plane = reinterpret_cast<const char*>(base + p.plane);
+    return *reinterpret_cast<const R*>(plane + p.off * (uint32_t)sizeof(R));
 }
 template <typename R>
-__device__ __forceinline__ void st(R* plane, int32_t idx, R v)
+__device__ __forceinline__ void st(R* base, Slot p, R v)
 {
-    *reinterpret_cast<R*>(reinterpret_cast<char*>(plane) + (uint32_t)idx * (uint32_t)sizeof(R)) = v;
+    char* plane = reinterpret_cast<char*>(base + p.plane);
+    *reinterpret_cast<R*>(plane + p.off * (uint32_t)sizeof(R)) = v;
 }
 
 // ------------------------------------------------------ boundaries
@@ -266,7 +294,7 @@ __device__ __forceinline__ void keep_face_velocity(const Bounce<R>& bb, const Ge
 // VELOCITY: the same, less the moving-wall term; SLIP: the population sent
 // from x - c_t along q reflected, at (opposite(q reflected), x - c_t).
 template <class L, typename R, int BND>
-__device__ __forceinline__ R blocked_inflow(const R* f, int64_t S, int32_t cell, const Nbr<L::DIMS>& nb,
+__device__ __forceinline__ R blocked_inflow(const R* f, const Geometry& G, int32_t cell, const Nbr<L::DIMS>& nb,
                                             const FaceRules& fr, const Bounce<R>& bb, int q)
 {
     const int p = opp(q);
@@ -274,9 +302,9 @@ __device__ __forceinline__ R blocked_inflow(const R* f, int64_t S, int32_t cell,
         const int a = gov_axis(fr, p);
         const int src = a == 0 ? refl<L>(0, q) : (a == 1 ? refl<L>(1, q) : refl<L>(2, q));
         const int32_t y = cell + nb.at(a == 0 ? 0 : -L::cx(q), a == 1 ? 0 : -L::cy(q), a == 2 ? 0 : -L::cz(q));
-        return ld(f + opp(src) * S, y);
+        return ld(f, posf(G, opp(src), y));
     }
-    R v = ld(f + q * S, cell);
+    R v = ld(f, posf(G, q, cell));
     if (BND == 2 && ((fr.vel >> p) & 1u)) v -= vel_shift<L>(bb, gov_face<L>(fr, p), p);
     return v;
 }
@@ -285,20 +313,21 @@ __device__ __forceinline__ R blocked_inflow(const R* f, int64_t S, int32_t cell,
 // next (even) step reads the returning population: (opposite(p), x) with the
 // link's rule applied, or for SLIP (p reflected, x + c_t).
 template <class L, typename R, int BND>
-__device__ __forceinline__ void blocked_outflow(R* f, int64_t S, int32_t cell, const Nbr<L::DIMS>& nb,
+__device__ __forceinline__ void blocked_outflow(R* f, const Geometry& G, int32_t cell, const Nbr<L::DIMS>& nb,
                                                 const FaceRules& fr, const Bounce<R>& bb, int p, R h, R ux, R uy,
                                                 R uz)
 {
     if (BND == 2 && ((fr.slip >> p) & 1u)) {
         const int a = gov_axis(fr, p);
         const int dst = a == 0 ? refl<L>(0, p) : (a == 1 ? refl<L>(1, p) : refl<L>(2, p));
-        st(f + dst * S, cell + nb.at(a == 0 ? 0 : L::cx(p), a == 1 ? 0 : L::cy(p), a == 2 ? 0 : L::cz(p)), h);
+        st(f, posf(G, dst, cell + nb.at(a == 0 ? 0 : L::cx(p), a == 1 ? 0 : L::cy(p), a == 2 ? 0 : L::cz(p))),
+           h);
         return;
     }
     R v = h;
     if (BND == 2 && ((fr.vel >> p) & 1u)) v = h - vel_shift<L>(bb, gov_face<L>(fr, p), p);
     if (BND == 2 && ((fr.pres >> p) & 1u)) v = pres_value<L>(bb, gov_face<L>(fr, p), p, h, ux, uy, uz);
-    st(f + opp(p) * S, cell, v);
+    st(f, posf(G, opp(p), cell), v);
 }
 
 // ------------------------------------------------------------ AA step
@@ -332,17 +361,16 @@ __global__ void __launch_bounds__(BLOCK) k_aa_step(StepArgs<R> a)
     const Geometry& G = a.geo;
     const int32_t cell = (int32_t)(blockIdx.x * BLOCK + threadIdx.x);
     if (cell >= G.ncell) return;
-    const int64_t S = G.stride;
     R* __restrict__ f = a.f;
     R* __restrict__ gg = a.g;
     R h[L::Q];
     R g[L::QT];
     if (a.parity == 0) {
 #pragma unroll
-        for (int q = 0; q < L::Q; ++q) h[q] = ld(f + q * S, cell);
+        for (int q = 0; q < L::Q; ++q) h[q] = ld(f, posf(G, q, cell));
         if (TH) {
 #pragma unroll
-            for (int k = 0; k < L::QT; ++k) g[k] = ld(gg + k * S, cell);
+            for (int k = 0; k < L::QT; ++k) g[k] = ld(gg, posg(G, k, cell));
         }
         uint32_t pdirs = 0u;
         FaceRules fr{};
@@ -366,10 +394,10 @@ __global__ void __launch_bounds__(BLOCK) k_aa_step(StepArgs<R> a)
                 if ((pdirs >> p) & 1u) h[p] = pres_value<L>(a.bb, gov_face<L>(fr, p), p, h[p], ux, uy, uz);
         }
 #pragma unroll
-        for (int q = 0; q < L::Q; ++q) st(f + opp(q) * S, cell, h[q]);
+        for (int q = 0; q < L::Q; ++q) st(f, posf(G, opp(q), cell), h[q]);
         if (TH) {
 #pragma unroll
-            for (int k = 0; k < L::QT; ++k) st(gg + opp(k) * S, cell, g[k]);
+            for (int k = 0; k < L::QT; ++k) st(gg, posg(G, opp(k), cell), g[k]);
         }
         return;
     }
@@ -382,19 +410,20 @@ __global__ void __launch_bounds__(BLOCK) k_aa_step(StepArgs<R> a)
     FaceRules fr{};
     if (BND == 2 && near) fr = face_rules<L>(a.bb, nb.faces);
 #pragma unroll
-    for (int q = 0; q < L::Q; ++q) h[q] = ld(f + opp(q) * S, cell + nb.at(-L::cx(q), -L::cy(q), -L::cz(q)));
+    for (int q = 0; q < L::Q; ++q) h[q] = ld(f, posf(G, opp(q), cell + nb.at(-L::cx(q), -L::cy(q), -L::cz(q))));
     if (TH) {
 #pragma unroll
-        for (int k = 0; k < L::QT; ++k) g[k] = ld(gg + opp(k) * S, cell + nb.at(-L::cxT(k), -L::cyT(k), -L::czT(k)));
+        for (int k = 0; k < L::QT; ++k)
+            g[k] = ld(gg, posg(G, opp(k), cell + nb.at(-L::cxT(k), -L::cyT(k), -L::czT(k))));
     }
     if (near) {
 #pragma unroll
         for (int q = 1; q < L::Q; ++q)
-            if ((blk >> opp(q)) & 1u) h[q] = blocked_inflow<L, R, BND>(f, S, cell, nb, fr, a.bb, q);
+            if ((blk >> opp(q)) & 1u) h[q] = blocked_inflow<L, R, BND>(f, G, cell, nb, fr, a.bb, q);
         if (TH) {
 #pragma unroll
             for (int k = 1; k < L::QT; ++k)
-                if ((blk >> opp(k)) & 1u) g[k] = bounce7(a.bb, b, opp(k), ld(gg + k * S, cell));
+                if ((blk >> opp(k)) & 1u) g[k] = bounce7(a.bb, b, opp(k), ld(gg, posg(G, k, cell)));
         }
     }
     R ux = R(0), uy = R(0), uz = R(0);
@@ -408,20 +437,21 @@ __global__ void __launch_bounds__(BLOCK) k_aa_step(StepArgs<R> a)
     collide<R, TH>(h, g, a.col);
 #pragma unroll
     for (int q = 0; q < L::Q; ++q)
-        if (!BND || !((skip >> q) & 1u)) st(f + q * S, cell + nb.at(L::cx(q), L::cy(q), L::cz(q)), h[q]);
+        if (!BND || !((skip >> q) & 1u)) st(f, posf(G, q, cell + nb.at(L::cx(q), L::cy(q), L::cz(q))), h[q]);
     if (TH) {
 #pragma unroll
         for (int k = 0; k < L::QT; ++k)
-            if (!BND || !((skip >> k) & 1u)) st(gg + k * S, cell + nb.at(L::cxT(k), L::cyT(k), L::czT(k)), g[k]);
+            if (!BND || !((skip >> k) & 1u))
+                st(gg, posg(G, k, cell + nb.at(L::cxT(k), L::cyT(k), L::czT(k))), g[k]);
     }
     if (near) {
 #pragma unroll
         for (int p = 1; p < L::Q; ++p)
-            if ((blk >> p) & 1u) blocked_outflow<L, R, BND>(f, S, cell, nb, fr, a.bb, p, h[p], ux, uy, uz);
+            if ((blk >> p) & 1u) blocked_outflow<L, R, BND>(f, G, cell, nb, fr, a.bb, p, h[p], ux, uy, uz);
         if (TH) {
 #pragma unroll
             for (int k = 1; k < L::QT; ++k)
-                if ((blk >> k) & 1u) st(gg + opp(k) * S, cell, bounce7(a.bb, b, k, g[k]));
+                if ((blk >> k) & 1u) st(gg, posg(G, opp(k), cell), bounce7(a.bb, b, k, g[k]));
         }
     }
 }
@@ -437,14 +467,13 @@ __global__ void __launch_bounds__(BLOCK) k_ab_collide(StepArgs<R> a)
     const Geometry& G = a.geo;
     const int32_t cell = (int32_t)(blockIdx.x * BLOCK + threadIdx.x);
     if (cell >= G.ncell) return;
-    const int64_t S = G.stride;
     R h[L::Q];
     R g[L::QT];
 #pragma unroll
-    for (int q = 0; q < L::Q; ++q) h[q] = ld(a.f + q * S, cell);
+    for (int q = 0; q < L::Q; ++q) h[q] = ld(a.f, posf(G, q, cell));
     if (TH) {
 #pragma unroll
-        for (int k = 0; k < L::QT; ++k) g[k] = ld(a.g + k * S, cell);
+        for (int k = 0; k < L::QT; ++k) g[k] = ld(a.g, posg(G, k, cell));
     }
     if (BND == 2 && a.bb.pres) {
         const Nbr<L::DIMS> nb(G, cell);
@@ -455,10 +484,10 @@ __global__ void __launch_bounds__(BLOCK) k_ab_collide(StepArgs<R> a)
     }
     collide<R, TH>(h, g, a.col);
 #pragma unroll
-    for (int q = 0; q < L::Q; ++q) st(a.f + q * S, cell, h[q]);
+    for (int q = 0; q < L::Q; ++q) st(a.f, posf(G, q, cell), h[q]);
     if (TH) {
 #pragma unroll
-        for (int k = 0; k < L::QT; ++k) st(a.g + k * S, cell, g[k]);
+        for (int k = 0; k < L::QT; ++k) st(a.g, posg(G, k, cell), g[k]);
     }
 }
 
@@ -473,7 +502,6 @@ __global__ void __launch_bounds__(BLOCK) k_ab_pull(StepArgs<R> a)
     const Geometry& G = a.geo;
     const int32_t cell = (int32_t)(blockIdx.x * BLOCK + threadIdx.x);
     if (cell >= G.ncell) return;
-    const int64_t S = G.stride;
     const Nbr<L::DIMS> nb(G, cell);
     Blocked b{0u, 0u, 0u, false};
     if (BND) b = blocked_dirs<L>(a.bb, a.mask, cell, nb.faces);
@@ -490,28 +518,28 @@ __global__ void __launch_bounds__(BLOCK) k_ab_pull(StepArgs<R> a)
     }
 #pragma unroll
     for (int q = 0; q < L::Q; ++q) {
-        R v = ld(a.f + q * S, cell + nb.at(-L::cx(q), -L::cy(q), -L::cz(q)));
+        R v = ld(a.f, posf(G, q, cell + nb.at(-L::cx(q), -L::cy(q), -L::cz(q))));
         const int p = opp(q);
         if (BND && ((blk >> p) & 1u)) {
             if (BND == 2 && ((fr.slip >> p) & 1u)) {
                 const int ax = gov_axis(fr, p);
                 const int src = ax == 0 ? refl<L>(0, q) : (ax == 1 ? refl<L>(1, q) : refl<L>(2, q));
-                v = ld(a.f + src * S,
-                       cell + nb.at(ax == 0 ? 0 : -L::cx(q), ax == 1 ? 0 : -L::cy(q), ax == 2 ? 0 : -L::cz(q)));
+                v = ld(a.f, posf(G, src,
+                                cell + nb.at(ax == 0 ? 0 : -L::cx(q), ax == 1 ? 0 : -L::cy(q), ax == 2 ? 0 : -L::cz(q))));
             } else {
-                v = ld(a.f + p * S, cell);
+                v = ld(a.f, posf(G, p, cell));
                 if (BND == 2 && ((fr.vel >> p) & 1u)) v -= vel_shift<L>(a.bb, gov_face<L>(fr, p), p);
                 if (BND == 2 && ((fr.pres >> p) & 1u)) v = pres_value<L>(a.bb, gov_face<L>(fr, p), p, v, ux, uy, uz);
             }
         }
-        st(a.f2 + q * S, cell, v);
+        st(a.f2, posf(G, q, cell), v);
     }
     if (TH) {
 #pragma unroll
         for (int k = 0; k < L::QT; ++k) {
-            R v = ld(a.g + k * S, cell + nb.at(-L::cxT(k), -L::cyT(k), -L::czT(k)));
-            if (BND && ((blk >> opp(k)) & 1u)) v = bounce7(a.bb, b, opp(k), ld(a.g + opp(k) * S, cell));
-            st(a.g2 + k * S, cell, v);
+            R v = ld(a.g, posg(G, k, cell + nb.at(-L::cxT(k), -L::cyT(k), -L::czT(k))));
+            if (BND && ((blk >> opp(k)) & 1u)) v = bounce7(a.bb, b, opp(k), ld(a.g, posg(G, opp(k), cell)));
+            st(a.g2, posg(G, k, cell), v);
         }
     }
 }
@@ -639,11 +667,11 @@ __global__ void __launch_bounds__(BLOCK) k_link_gather(LinkArgs<R> a)
 {
     const int64_t l = a.begin + (int64_t)blockIdx.x * BLOCK + threadIdx.x;
     if (l >= a.end) return;
-    const int64_t S = a.geo.stride;
     const uint32_t meta = a.meta[l];
+    const bool t7 = (meta & LINK_TEMP) != 0;
     const LinkSlots sl = link_slots(a.mode, (int)(meta & LINK_DIR_MASK), a.cell[l], a.cellw[l]);
-    const R* src = (meta & LINK_TEMP) ? a.g_src : a.f_src;
-    a.scratch[l] = ld(src + sl.src_plane * S, sl.src_idx);
+    const R* src = t7 ? a.g_src : a.f_src;
+    a.scratch[l] = ld(src, posb(a.geo, t7, sl.src_plane, sl.src_idx));
 }
 
 // Scatter (wall links): write each gathered value where the next step reads it.
@@ -652,12 +680,12 @@ __global__ void __launch_bounds__(BLOCK) k_link_scatter(LinkArgs<R> a)
 {
     const int64_t l = a.begin + (int64_t)blockIdx.x * BLOCK + threadIdx.x;
     if (l >= a.end) return;
-    const int64_t S = a.geo.stride;
     const uint32_t meta = a.meta[l];
+    const bool t7 = (meta & LINK_TEMP) != 0;
     const int32_t grp = (int32_t)((meta >> LINK_GROUP_SHIFT) & LINK_GROUP_MASK);
     const LinkSlots sl = link_slots(a.mode, (int)(meta & LINK_DIR_MASK), a.cell[l], a.cellw[l]);
-    R* dst = (meta & LINK_TEMP) ? a.g_dst : a.f_dst;
-    st(dst + sl.dst_plane * S, sl.dst_idx, link_value(a, meta, grp, a.scratch[l]));
+    R* dst = t7 ? a.g_dst : a.f_dst;
+    st(dst, posb(a.geo, t7, sl.dst_plane, sl.dst_idx), link_value(a, meta, grp, a.scratch[l]));
 }
 
 // Direct pass (wall links with two buffers): sources lie in one buffer and
@@ -667,13 +695,12 @@ __global__ void __launch_bounds__(BLOCK) k_link_direct(LinkArgs<R> a)
 {
     const int64_t l = a.begin + (int64_t)blockIdx.x * BLOCK + threadIdx.x;
     if (l >= a.end) return;
-    const int64_t S = a.geo.stride;
     const uint32_t meta = a.meta[l];
     const int32_t grp = (int32_t)((meta >> LINK_GROUP_SHIFT) & LINK_GROUP_MASK);
     const LinkSlots sl = link_slots(a.mode, (int)(meta & LINK_DIR_MASK), a.cell[l], a.cellw[l]);
     const bool g7 = (meta & LINK_TEMP) != 0;
-    const R v = ld((g7 ? a.g_src : a.f_src) + sl.src_plane * S, sl.src_idx);
-    st((g7 ? a.g_dst : a.f_dst) + sl.dst_plane * S, sl.dst_idx, link_value(a, meta, grp, v));
+    const R v = ld(g7 ? a.g_src : a.f_src, posb(a.geo, g7, sl.src_plane, sl.src_idx));
+    st(g7 ? a.g_dst : a.f_dst, posb(a.geo, g7, sl.dst_plane, sl.dst_idx), link_value(a, meta, grp, v));
 }
 
 // Force pass, on a submission's last step only, over every link.  It reads
@@ -692,7 +719,6 @@ __global__ void __launch_bounds__(BLOCK) k_link_force(LinkArgs<R> a)
     __shared__ double acc[4 * LBM_GROUPS];
     for (int i = threadIdx.x; i < 4 * LBM_GROUPS; i += BLOCK) acc[i] = 0.0;
     __syncthreads();
-    const int64_t S = a.geo.stride;
     for (int64_t base = a.begin + (int64_t)blockIdx.x * BLOCK; base < a.end; base += (int64_t)gridDim.x * BLOCK) {
         const int64_t l = base + threadIdx.x;
         LinkSum c{0.0, 0.0, 0.0, 0.0};
@@ -721,7 +747,7 @@ __global__ void __launch_bounds__(BLOCK) k_link_force(LinkArgs<R> a)
                 plane = refl_rt<L>((int)((meta >> LINK_AXIS_SHIFT) & 3u), p);
                 idx = a.cellw[l];
             }
-            R v = ld((g7 ? a.g_dst : a.f_dst) + plane * S, idx);
+            R v = ld(g7 ? a.g_dst : a.f_dst, posb(a.geo, g7, plane, idx));
             if (transformed && g7 && (meta & LINK_DIRICHLET)) v = (R)(a.omega * a.wall_T[grp]) - v;
             c = link_sum<L>(a, meta, p, grp, v, transformed, l);
         }
@@ -757,7 +783,6 @@ __global__ void __launch_bounds__(BLOCK) k_init(FieldArgs<R> a)
     const Geometry& G = a.geo;
     const int32_t cell = (int32_t)(blockIdx.x * BLOCK + threadIdx.x);
     if (cell >= G.ncell) return;
-    const int64_t S = G.stride;
     R h[L::Q];
     R g[L::QT];
     if (a.mask && (a.mask[cell] & MASK_SOLID)) {
@@ -772,10 +797,10 @@ __global__ void __launch_bounds__(BLOCK) k_init(FieldArgs<R> a)
         equilibrium<R, TH>(a.rho[cell], a.u[cell], a.u[n + cell], a.u[2 * n + cell], T, a.col.a_T, h, g);
     }
 #pragma unroll
-    for (int q = 0; q < L::Q; ++q) a.f[q * S + cell] = h[q];
+    for (int q = 0; q < L::Q; ++q) st(a.f, posf(G, q, cell), h[q]);
     if (TH) {
 #pragma unroll
-        for (int k = 0; k < L::QT; ++k) a.g[k * S + cell] = g[k];
+        for (int k = 0; k < L::QT; ++k) st(a.g, posg(G, k, cell), g[k]);
     }
 }
 
@@ -787,21 +812,21 @@ template <class L, typename R, bool TH>
 __device__ __forceinline__ bool load_cell(const FieldArgs<R>& a, int32_t cell, R* h, R* g)
 {
     const Geometry& G = a.geo;
-    const int64_t S = G.stride;
     if (a.ab || a.parity == 0) {
 #pragma unroll
-        for (int q = 0; q < L::Q; ++q) h[q] = a.f[q * S + cell];
+        for (int q = 0; q < L::Q; ++q) h[q] = ld(a.f, posf(G, q, cell));
         if (TH) {
 #pragma unroll
-            for (int k = 0; k < L::QT; ++k) g[k] = a.g[k * S + cell];
+            for (int k = 0; k < L::QT; ++k) g[k] = ld(a.g, posg(G, k, cell));
         }
     } else {
         const Nbr<L::DIMS> nb(G, cell);
 #pragma unroll
-        for (int q = 0; q < L::Q; ++q) h[q] = a.f[opp(q) * S + (cell + nb.at(-L::cx(q), -L::cy(q), -L::cz(q)))];
+        for (int q = 0; q < L::Q; ++q) h[q] = ld(a.f, posf(G, opp(q), cell + nb.at(-L::cx(q), -L::cy(q), -L::cz(q))));
         if (TH) {
 #pragma unroll
-            for (int k = 0; k < L::QT; ++k) g[k] = a.g[opp(k) * S + (cell + nb.at(-L::cxT(k), -L::cyT(k), -L::czT(k)))];
+            for (int k = 0; k < L::QT; ++k)
+                g[k] = ld(a.g, posg(G, opp(k), cell + nb.at(-L::cxT(k), -L::cyT(k), -L::czT(k))));
         }
         // with in-kernel boundary rules, an inflow from across a face or a
         // solid is the returning population the even step left behind
@@ -812,11 +837,11 @@ __device__ __forceinline__ bool load_cell(const FieldArgs<R>& a, int32_t cell, R
                 const FaceRules fr = face_rules<L>(a.bb, nb.faces);
 #pragma unroll
                 for (int q = 1; q < L::Q; ++q)
-                    if ((blk >> opp(q)) & 1u) h[q] = blocked_inflow<L, R, 2>(a.f, S, cell, nb, fr, a.bb, q);
+                    if ((blk >> opp(q)) & 1u) h[q] = blocked_inflow<L, R, 2>(a.f, G, cell, nb, fr, a.bb, q);
                 if (TH) {
 #pragma unroll
                     for (int k = 1; k < L::QT; ++k)
-                        if ((blk >> opp(k)) & 1u) g[k] = bounce7(a.bb, b, opp(k), a.g[k * S + cell]);
+                        if ((blk >> opp(k)) & 1u) g[k] = bounce7(a.bb, b, opp(k), ld(a.g, posg(G, k, cell)));
                 }
             }
         }

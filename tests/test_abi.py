@@ -143,8 +143,28 @@ def test_link_counts_do_not_depend_on_face_kind(lib, kinds):
 
 
 def test_box_too_large_rejected(lib):
+    # a population plane is addressed with 32-bit byte offsets: 2^30 fp32 cells are too many
     p = inputs.base_params(2048, 1024, 512, inputs.mrt_rates(0.6))
     assert binding.lbm_required_bytes(p) == 0
+    p = inputs.base_params(1024, 1024, 512, inputs.mrt_rates(0.6))
+    assert binding.lbm_required_bytes(p) >= 19 * 4 * 2 ** 29
+
+
+@pytest.mark.parametrize("shape,thermal,lattice", [((256, 256, 256), False, 0), ((70, 37, 23), True, 0),
+                                                   ((512, 512, 512), True, 0), ((8193, 8193, 1), True, 1)])
+def test_population_bytes_within_one_tile_of_the_minimum(lib, shape, thermal, lattice):
+    """The tiled population layout wastes at most one partial tile (plus the
+    plane shift of untiled boxes) per plane."""
+    nx, ny, nz = shape
+    if lattice:
+        p = inputs.base_params_2d(nx, ny, inputs.mrt_rates_2d(0.6), thermal=thermal, s5=[0, 1, 1, 1, 1])
+        q = 9 + (5 if thermal else 0)
+    else:
+        p = inputs.base_params(nx, ny, nz, inputs.mrt_rates(0.6), thermal=thermal, s7=[0, 1, 1, 1, 1, 1, 1])
+        q = 19 + (7 if thermal else 0)
+    b = binding.lbm_required_bytes(p, dtype=4)
+    n = nx * ny * nz
+    assert q * n * 4 <= b <= q * (n + 16384 + 1088) * 4 + (1 << 20)
 
 
 @pytest.mark.parametrize("n", [1, 2, 5, 16])
