@@ -128,6 +128,20 @@ enum { LBM_LINKS_IN_KERNEL = 0, LBM_LINKS_PASSES = 1 };
  * lbm_init_fields). */
 enum { LBM_LATTICE_3D = 0, LBM_LATTICE_2D = 1 };
 
+/* Population layout in the device buffer (no effect on results, only on
+ * speed).  Cells, in the order x + nx*(y + ny*z), are cut into tiles of 2^k
+ * consecutive cells and each tile stores its planes one after another (the
+ * collected structure of arrays of "GPU Optimization for High-Quality
+ * Kinetic Fluid Simulation", Sec. 4.1); thermal boxes may keep the
+ * temperature planes in the same tiles.  tile_log2 = 0 picks the layout
+ * measured fastest on MI355X: tiles of 32 KiB per plane (2^13 fp32 or 2^12
+ * fp64 cells) when the box holds at least four tiles, shared tiles for
+ * thermal fp32.  6..20 asks for tiles of 2^k cells (shared for thermal
+ * boxes).  31 asks for one plane per population over the whole box (the
+ * structure of arrays of "Multi-GPU thermal lattice Boltzmann simulations
+ * using OpenACC and MPI", Sec. 3).  Whatever is asked, a buffer that would
+ * reach 4 GiB tiled is stored one plane per population. */
+
 /* Faces are numbered 0..5 = x-, x+, y-, y+, z-, z+.  Force/heat group g is
  * face g for g < 6 and solid label g - 5 for g >= 6. */
 typedef struct lbm_params {
@@ -153,6 +167,8 @@ typedef struct lbm_params {
     int32_t pad1;
     double s9[9];            /* D2Q9 relaxation rates (LBM_LATTICE_2D), row order below, each in [0, 2) */
     double s5[5];            /* D2Q5 relaxation rates (LBM_LATTICE_2D), row order below, each in [0, 2) */
+    int32_t tile_log2;       /* population layout, see below: 0 automatic, 6..20 tiles of 2^k cells, 31 none */
+    int32_t pad2;
 } lbm_params;
 
 typedef struct lbm_ctx lbm_ctx;

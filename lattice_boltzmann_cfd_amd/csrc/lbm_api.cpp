@@ -105,40 +105,53 @@ bool finite(double v) { return std::isfinite(v); }
 // slower in either precision, so the value is not arbitrary).
 int64_t plane_stride(int64_t n) { return (n + 63) / 64 * 64 + 1024; }
 
-// Cells per tile of the population buffers, as a power of two (31: no tiles,
-// one plane per population over the whole box).  2^13 measured fastest on
-// MI355X among 2^11 .. 2^16 (the 256^3 step 6 % and the 256^3 thermal step
-// 5 % faster than one plane per population).
-#ifndef LBM_TILE_LG
-#define LBM_TILE_LG 13
-#endif
+// Automatic tiling (lbm_params.tile_log2 = 0): tiles hold 32 KiB of each
+// plane (2^13 fp32 or 2^12 fp64 cells), and a thermal fp32 box keeps its
+// temperature planes in the same tiles as its flow planes.  Measured on
+// MI355X in same-box A/B runs of this library against one plane per
+// population: 256^3 fp32 step -6.1 %, 256^3 thermal fp32 -5.1 % (-1.2 % more
+// with shared tiles), the 8193^2 2D cell in fp32 -9.3 % (-2.0 % more), 256^3
+// fp64 -2.8 % with 2^12 instead of 2^13 cells; shared tiles cost 0.7 % in fp64.
+constexpr int64_t TILE_PLANE_BYTES = 32768;
 
 // Tile geometry of the population buffers (see Geometry).  Tiles are used
-// when the box holds at least four of them and every population buffer stays
-// below 4 GiB, so that a lane's offset from its plane's base fits in 32 bits;
+// when asked for (tile_log2 in 6..20) or, automatically, when the box holds
+// at least four of them, and only while every population buffer stays below
+// 4 GiB, so that a lane's offset from its plane's base fits in 32 bits;
 // otherwise one plane per population over the whole box (each plane < 4 GiB,
 // checked by validate()).  Splitting larger buffers into groups of planes
 // that each stay below 4 GiB measured slower on MI355X (512^3 thermal 1 %,
 // the 8193^2 fp64 2D cell 5 %) than one plane per population.  Writes the
-// element counts of the flow and temperature buffers.
-void tile_geometry(const lbm_params* p, Geometry* G, int64_t* elems_f, int64_t* elems_g)
+// element counts of the flow and temperature buffers and, when the
+// temperature planes share the flow planes' tiles, the element offset of the
+// temperature buffer inside the flow buffer (else -1).
+void tile_geometry(const lbm_params* p, Geometry* G, int64_t* elems_f, int64_t* elems_g, int64_t* g_in_f)
 {
     const int64_t n = (int64_t)p->nx * p->ny * p->nz;
     const bool two_d = p->lattice == LBM_LATTICE_2D;
     const int64_t Q = two_d ? Q9 : Q19, QT = two_d ? Q5 : Q7;
-    const uint32_t lg = LBM_TILE_LG;
-    if (lg < 31 && n >= (int64_t(4) << lg)) {
+    const bool automatic = p->tile_log2 == 0;
+    uint32_t lg = (uint32_t)p->tile_log2;
+    if (automatic) {
+        lg = 0;
+        while ((int64_t(1) << (lg + 1)) * p->dtype <= TILE_PLANE_BYTES) ++lg;
+    }
+    *g_in_f = -1;
+    if (lg < 31 && (!automatic || n >= (int64_t(4) << lg))) {
         const int64_t A = int64_t(1) << lg;
         const int64_t tiles = (n + A - 1) >> lg;
         const int64_t limit = (int64_t(1) << 32) - (int64_t(1) << 20);
-        if (Q * A < (int64_t(1) << 24) && tiles * Q * A * p->dtype < limit) {
+        const bool shared = p->thermal && (automatic ? p->dtype == 4 : true);
+        const int64_t QF = shared ? Q + QT : Q;
+        if (QF * A < (int64_t(1) << 24) && tiles * QF * A * p->dtype < limit) {
             G->tile_lg = lg;
             G->tile_mask = (uint32_t)(A - 1);
             G->qstride = A;
-            G->tile_f = (uint32_t)(Q * A);
-            G->tile_g = (uint32_t)(QT * A);
-            *elems_f = tiles * Q * A;
-            *elems_g = tiles * QT * A;
+            G->tile_f = (uint32_t)(QF * A);
+            G->tile_g = (uint32_t)(shared ? QF * A : QT * A);
+            *elems_f = tiles * QF * A;
+            *elems_g = shared ? 0 : tiles * QT * A;
+            if (shared) *g_in_f = Q * A;
             return;
         }
     }
@@ -207,6 +220,8 @@ std::string validate(const lbm_params* p)
     if (p->solid_thermal != LBM_ADIABATIC && p->solid_thermal != LBM_DIRICHLET) return "bad solid_thermal";
     if (!finite(p->solid_T)) return "solid_T must be finite";
     if (p->lattice != LBM_LATTICE_3D && p->lattice != LBM_LATTICE_2D) return "lattice must be 0 (3D) or 1 (2D)";
+    if (!(p->tile_log2 == 0 || p->tile_log2 == 31 || (p->tile_log2 >= 6 && p->tile_log2 <= 20)))
+        return "tile_log2 must be 0 (automatic), 6..20 or 31 (no tiles)";
     if (p->lattice == LBM_LATTICE_3D) {
         for (int k = 0; k < 19; ++k)
             if (!(p->s19[k] >= 0.0 && p->s19[k] < 2.0)) return "s19 rates must lie in [0, 2)";
@@ -579,8 +594,8 @@ Layout make_layout(const lbm_params* p, bool solids, int64_t n_links)
 {
     Layout L{};
     const int64_t n = (int64_t)p->nx * p->ny * p->nz;
-    int64_t ef = 0, eg = 0;
-    tile_geometry(p, &L.tiles, &ef, &eg);
+    int64_t ef = 0, eg = 0, g_in_f = -1;
+    tile_geometry(p, &L.tiles, &ef, &eg, &g_in_f);
     const size_t es = (size_t)p->dtype;
     const size_t fb = align_up((size_t)ef * es);
     const size_t gb = p->thermal ? align_up((size_t)eg * es) : 0;
@@ -590,6 +605,11 @@ Layout make_layout(const lbm_params* p, bool solids, int64_t n_links)
     L.g = off; off += gb;
     L.f2 = off; off += ab ? fb : 0;
     L.g2 = off; off += ab ? gb : 0;
+    if (g_in_f >= 0) {
+        // the temperature planes share the flow planes' tiles
+        L.g = L.f + (size_t)g_in_f * es;
+        L.g2 = L.f2 + (size_t)g_in_f * es;
+    }
     L.mask = off; off += solids ? align_up(4 * (size_t)n) : 0;
     L.lcell = off; off += align_up(4 * (size_t)n_links);
     L.lcellw = off; off += align_up(4 * (size_t)n_links);

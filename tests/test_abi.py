@@ -46,7 +46,8 @@ def test_struct_layout_matches_header():
     assert P.lattice.offset == P.face_rho.offset + 8 * 6
     assert P.s9.offset == P.lattice.offset + 8
     assert P.s5.offset == P.s9.offset + 8 * 9
-    assert binding.ctypes.sizeof(P) == P.s5.offset + 8 * 5
+    assert P.tile_log2.offset == P.s5.offset + 8 * 5
+    assert binding.ctypes.sizeof(P) == P.tile_log2.offset + 8
 
 
 def periodic(n=8, **kw):
@@ -77,6 +78,9 @@ def test_required_bytes_sizes(lib):
     lambda p: p.update(face_kind=[4, 4, 0, 0, 0, 0], face_rho=[0.0] * 6),
     lambda p: p.update(face_kind=[3, 1, 0, 0, 0, 0], face_u=[float("inf")] + [0.0] * 17),
     lambda p: p.update(face_kind=[2, 2, 0, 0, 0, 0], links=binding.LBM_LINKS_PASSES),
+    lambda p: p.update(tile_log2=5),
+    lambda p: p.update(tile_log2=21),
+    lambda p: p.update(tile_log2=-1),
 ])
 def test_invalid_params_rejected_without_device_work(lib, mutate):
     p = periodic()
@@ -272,3 +276,18 @@ def test_2d_solid_link_counts_brute_force(lib):
                               s5=[0, 1, 1, 1, 1])
     assert binding.lbm_count_links(p, lab, 9) == brute_force_links(p, lab, D2Q9)
     assert binding.lbm_count_links(p, lab, 5) == brute_force_links(p, lab, D2Q5)
+
+
+def test_tile_layout_buffer_sizes(lib):
+    """On a box that is a whole number of tiles, tiles (any size; the thermal
+    planes sharing the flow planes' tiles) need exactly the population bytes,
+    while one plane per population adds the 1024-element plane shift to each
+    of the 26 planes; the link arrays are the same for every layout."""
+    w = inputs.cavity256(shape=(64, 64, 64))
+    sizes = {}
+    for d in (4, 8):
+        for tile in (31, 13, 9, 6, 0):
+            w.params["tile_log2"] = tile
+            sizes[tile, d] = binding.lbm_required_bytes(w.params, None, dtype=d)
+        for tile in (13, 9, 6, 0):
+            assert abs((sizes[31, d] - sizes[tile, d]) - 26 * 1024 * d) <= 2 * 256, (tile, d)
