@@ -1,14 +1,18 @@
 // lbm_kernels.hip -- the HIP kernels of the fused lattice Boltzmann step (gfx950).
 //
+// Every kernel is written once for both lattice pairs of the
+// double-distribution model (D3Q19 + D3Q7, and D2Q9 + D2Q5 on one z layer),
+// given as a compile-time descriptor L (lbm_lattice.hpp).
+//
 // Layout: structure of arrays, one plane per population direction, cell
 // index x + nx*(y + ny*z) inside a plane ("Multi-GPU thermal lattice
 // Boltzmann simulations using OpenACC and MPI", Sec. 3: SoA so that
-// neighbouring threads touch neighbouring data), optionally cut into tiles of
+// neighbouring threads touch neighbouring data), cut into tiles of
 // consecutive cells that hold all planes of the tile (the collected SoA of
-// "GPU Optimization for High-Quality Kinetic Fluid Simulation", Sec. 4.1);
-// see pos().  One thread per cell, cells
-// flattened, so a 64-lane wavefront reads and writes 64 consecutive elements
-// of each plane (256 B in fp32) whatever the box shape.
+// "GPU Optimization for High-Quality Kinetic Fluid Simulation", Sec. 4.1)
+// where the buffers allow; see pos().  One thread per cell, cells flattened,
+// so a 64-lane wavefront reads and writes 64 consecutive elements of each
+// plane (256 B in fp32) whatever the box shape.
 //
 // In-place AA streaming ("GPU lattice Boltzmann: streaming layout and
 // performance", OneCAD docs): even steps read population q of cell x at
@@ -171,7 +175,7 @@ __device__ __forceinline__ Blocked blocked_dirs(const Bounce<R>& bb, const uint3
     return b;
 }
 
-// The value a D3Q7 population takes when it bounces in direction k's face or
+// The value a temperature population takes when it bounces in direction k's face or
 // off a solid: anti-bounce-back gw - g (Dirichlet) or g (adiabatic).
 template <typename R>
 __device__ __forceinline__ R bounce7(const Bounce<R>& bb, const Blocked& b, int k, R v)
@@ -495,7 +499,7 @@ __global__ void __launch_bounds__(BLOCK) k_ab_collide(StepArgs<R> a)
 // x - c_q is across a face or a solid cell the population returns by the
 // link's rule: from x itself, B(q, x) = A(opp q, x) (bounce-back; less the
 // moving-wall term for VELOCITY; anti-bounce-back for PRESSURE, and for a
-// Dirichlet D3L::QT link), or for SLIP from x - c_t along q reflected.
+// Dirichlet temperature link), or for SLIP from x - c_t along q reflected.
 template <class L, typename R, bool TH, int BND>
 __global__ void __launch_bounds__(BLOCK) k_ab_pull(StepArgs<R> a)
 {
@@ -586,11 +590,11 @@ __device__ __forceinline__ LinkSlots link_slots(int mode, int p, int32_t cell, i
     return s;
 }
 
-// Per-link contribution to the group sums.  A D3L::Q link hands the boundary
+// Per-link contribution to the group sums.  A flow-lattice link hands the boundary
 // the momentum it carries out minus what it brings back, c_p f_out - c_in
 // f_in (stored values are f - w): 2 c_p f_p^+ for a wall or solid,
 // (c_p - c_p reflected) f_p^+ for SLIP, c_p (f_out + f_in) for VELOCITY and
-// PRESSURE.  A Dirichlet D3L::QT link passes w T_w - 2 g_p^+ into the fluid.
+// PRESSURE.  A Dirichlet temperature link passes w T_w - 2 g_p^+ into the fluid.
 // `returned` says whether v is the returning value (else the leaving one);
 // a PRESSURE link needs only the cell's velocity, from the face planes.
 struct LinkSum {
@@ -707,7 +711,7 @@ __global__ void __launch_bounds__(BLOCK) k_link_direct(LinkArgs<R> a)
 // the bounced population f_p^+ of each link where the step left it: with
 // in-kernel bounce-back (opp p, x) in place (the even step's usual store or
 // the odd step's bounce-back store); with link passes the scatter
-// destination; with two buffers B(opp p, x).  Values a D3L::QT Dirichlet link stores after
+// destination; with two buffers B(opp p, x).  Values a Dirichlet temperature link stores after
 // anti-bounce-back are converted back.  It sums the momentum exchange
 // 2 c_p f_p^+ and the heat w T_w - 2 g_p^+ per group: wavefront shuffles, then
 // fp64 LDS atomics per block, then one global atomic per block and touched
