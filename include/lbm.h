@@ -142,6 +142,19 @@ enum { LBM_LATTICE_3D = 0, LBM_LATTICE_2D = 1 };
  * using OpenACC and MPI", Sec. 3).  Whatever is asked, a buffer that would
  * reach 4 GiB tiled is stored one plane per population. */
 
+/* Occupancy of the step kernels (no effect on results, only on speed).
+ * occupancy[0] governs the even steps of the in-place scheme and the collide
+ * kernel of the two-buffer one, occupancy[1] the odd steps and the pull
+ * kernel.  k in 1..8 lets at most k blocks of 256 cells run at once on one
+ * compute unit (the launch reserves local data share that the kernel never
+ * touches); -1 leaves the count to the kernel's register use; 0 picks the
+ * value measured fastest on MI355X for the kernel instance (lattice,
+ * precision, thermal or not, boundary rules compiled in) and -1 where none
+ * was measured.  Fewer resident blocks keep fewer population streams open in
+ * HBM at once, which favours the aligned, local accesses of the even step;
+ * kernels whose loads wait on other loads (the boundary rules) need more
+ * blocks to hide that latency. */
+
 /* Faces are numbered 0..5 = x-, x+, y-, y+, z-, z+.  Force/heat group g is
  * face g for g < 6 and solid label g - 5 for g >= 6. */
 typedef struct lbm_params {
@@ -169,6 +182,7 @@ typedef struct lbm_params {
     double s5[5];            /* D2Q5 relaxation rates (LBM_LATTICE_2D), row order below, each in [0, 2) */
     int32_t tile_log2;       /* population layout, see below: 0 automatic, 6..20 tiles of 2^k cells, 31 none */
     int32_t pad2;
+    int32_t occupancy[2];    /* resident blocks per compute unit, even / odd steps, see below: 0 automatic */
 } lbm_params;
 
 typedef struct lbm_ctx lbm_ctx;

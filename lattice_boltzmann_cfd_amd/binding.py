@@ -51,7 +51,7 @@ class LbmParams(ctypes.Structure):
         ("face_u", ctypes.c_double * 18), ("face_rho", ctypes.c_double * 6),
         ("lattice", ctypes.c_int32), ("pad1", ctypes.c_int32),
         ("s9", ctypes.c_double * 9), ("s5", ctypes.c_double * 5),
-        ("tile_log2", ctypes.c_int32), ("pad2", ctypes.c_int32),
+        ("tile_log2", ctypes.c_int32), ("pad2", ctypes.c_int32), ("occupancy", ctypes.c_int32 * 2),
     ]
 
 
@@ -126,6 +126,8 @@ def to_params(d: dict, dtype: int = 4, streaming: int = LBM_STREAM_AUTO) -> LbmP
     for i in range(5):
         p.s5[i] = float(d.get("s5", [0.0] * 5)[i])
     p.tile_log2 = int(d.get("tile_log2", 0))
+    occ = d.get("occupancy", (0, 0))
+    p.occupancy[0], p.occupancy[1] = int(occ[0]), int(occ[1])
     p.a_T = float(d.get("a_T", 0.0))
     for i in range(3):
         p.accel[i] = float(d.get("accel", [0.0] * 3)[i])

@@ -43,6 +43,7 @@ struct lbm_ctx {
     int64_t t = 0;
     bool initialised = false;
     bool in_kernel = false;  // bounce-back inside the step kernel
+    size_t lds[2] = {0, 0};  // per parity: local data share reserved per block of the step kernel
     // replay of one even+odd pair of steps as a HIP graph (captured once on a
     // private stream, launched on the caller's)
     hipStream_t capture_stream = nullptr;
@@ -222,6 +223,9 @@ std::string validate(const lbm_params* p)
     if (p->lattice != LBM_LATTICE_3D && p->lattice != LBM_LATTICE_2D) return "lattice must be 0 (3D) or 1 (2D)";
     if (!(p->tile_log2 == 0 || p->tile_log2 == 31 || (p->tile_log2 >= 6 && p->tile_log2 <= 20)))
         return "tile_log2 must be 0 (automatic), 6..20 or 31 (no tiles)";
+    for (int k = 0; k < 2; ++k)
+        if (p->occupancy[k] < -1 || p->occupancy[k] > 8)
+            return "occupancy values must be -1 (no bound), 0 (automatic) or 1..8 blocks per compute unit";
     if (p->lattice == LBM_LATTICE_3D) {
         for (int k = 0; k < 19; ++k)
             if (!(p->s19[k] >= 0.0 && p->s19[k] < 2.0)) return "s19 rates must lie in [0, 2)";
@@ -362,6 +366,48 @@ Bounce<R> make_bounce(const lbm_params* p, bool in_kernel, void* face_vel)
     b.solid_dirichlet = p->solid_thermal == LBM_DIRICHLET ? 1 : 0;
     b.in_kernel = in_kernel ? 1 : 0;
     return b;
+}
+
+// ------------------------------------------------------------- occupancy
+
+// Blocks per compute unit that occupancy = 0 gives the in-place step kernel,
+// for the even and the odd step (-1: no bound).  Chosen by interleaved
+// timings on MI355X of whole steps at bounds of 1 to 4 blocks and none:
+// D3Q19 fp32 on a periodic 256^3 box, the same in fp64, the heated 256^3
+// cavity (D3Q19 + D3Q7) in fp32 and fp64, the 512^3 box with random spheres,
+// the heated 8193^2 square (D2Q9 + D2Q5) in fp32 and fp64 and the 256x128x128
+// channel with a velocity inlet and a pressure outlet.  Instances not listed
+// were not measured and keep the bound their registers give.
+struct OccupancyChoice {
+    int lattice, dtype, thermal, rules, even, odd;
+};
+constexpr OccupancyChoice OCCUPANCY_TABLE[] = {
+    {LBM_LATTICE_3D, 4, 0, 0, 2, 2},
+    {LBM_LATTICE_3D, 4, 1, 1, 2, -1},
+    {LBM_LATTICE_3D, 8, 0, 0, 1, 2},
+    {LBM_LATTICE_3D, 8, 1, 1, 1, 2},
+    {LBM_LATTICE_2D, 4, 1, 1, 3, 4},
+    {LBM_LATTICE_2D, 8, 1, 1, 2, 2},
+};
+
+int automatic_occupancy(const lbm_params* p, bool ab, int rules, int parity)
+{
+    if (ab) return -1;
+    for (const OccupancyChoice& o : OCCUPANCY_TABLE)
+        if (o.lattice == p->lattice && o.dtype == p->dtype && o.thermal == p->thermal && o.rules == rules)
+            return parity ? o.odd : o.even;
+    return -1;
+}
+
+// Bytes of local data share to reserve per block so that at most `blocks`
+// blocks fit on a compute unit holding lds_cu bytes (0: no reservation).
+// The step kernels use no local data share themselves.
+size_t occupancy_lds(int blocks, int lds_cu)
+{
+    if (blocks < 1 || lds_cu <= 0) return 0;
+    const size_t per = (size_t)lds_cu / (size_t)blocks / 1024 * 1024 - 1024;
+    if (per == 0 || per * (size_t)blocks > (size_t)lds_cu || per * (size_t)(blocks + 1) <= (size_t)lds_cu) return 0;
+    return per;
 }
 
 // ------------------------------------------------------------- links
@@ -687,7 +733,7 @@ lbm_status enqueue_step(lbm_ctx* c, hipStream_t stream, bool last)
         s.f = (R*)c->f;
         s.g = (R*)c->g;
         s.parity = parity;
-        LBM_HIP(c, (launch_aa_step<L, R>(s, c->thermal, stream)), "AA step kernel");
+        LBM_HIP(c, (launch_aa_step<L, R>(s, c->thermal, c->lds[parity], stream)), "AA step kernel");
         la = link_args<R>(c, parity == 0 ? LINK_AA_AFTER_EVEN : LINK_AA_AFTER_ODD, c->f, c->f, c->g, c->g);
         if (passes) {
             // link passes: gather every source, then scatter
@@ -705,8 +751,8 @@ lbm_status enqueue_step(lbm_ctx* c, hipStream_t stream, bool last)
         s.g = (R*)ga;
         s.f2 = (R*)fb;
         s.g2 = (R*)gb;
-        LBM_HIP(c, (launch_ab_collide<L, R>(s, c->thermal, stream)), "A-B collide kernel");
-        LBM_HIP(c, (launch_ab_pull<L, R>(s, c->thermal, stream)), "A-B pull kernel");
+        LBM_HIP(c, (launch_ab_collide<L, R>(s, c->thermal, c->lds[0], stream)), "A-B collide kernel");
+        LBM_HIP(c, (launch_ab_pull<L, R>(s, c->thermal, c->lds[1], stream)), "A-B pull kernel");
         la = link_args<R>(c, LINK_AB, fa, fb, ga, gb);
         if (passes) {
             // sources in one buffer, destinations in the other: one pass
@@ -909,6 +955,17 @@ lbm_status lbm_create(const lbm_params* p, const uint8_t* solid_labels, void* de
         c->cold = make_collision<double>(p);
         const bool walls = nonperiodic(p, 0) || nonperiodic(p, 2) || nonperiodic(p, 4);
         c->in_kernel = p->links == LBM_LINKS_IN_KERNEL && (walls || solids);
+        {
+            int dev = 0, lds_cu = 0;
+            if (hipGetDevice(&dev) != hipSuccess ||
+                hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess)
+                lds_cu = 0;
+            const int rules = boundary_rules(make_bounce<float>(p, c->in_kernel, nullptr));
+            for (int k = 0; k < 2; ++k) {
+                const int blocks = p->occupancy[k] ? p->occupancy[k] : automatic_occupancy(p, c->ab, rules, k);
+                c->lds[k] = occupancy_lds(blocks, lds_cu);
+            }
+        }
 
         // order the links of both lattices and upload
         LinkList all;

@@ -160,12 +160,26 @@ struct FieldArgs {
     Collision<R> col;
 };
 
+// Boundary rules compiled into a cell kernel instance: 0 none (periodic box,
+// or bounce-back left to the link passes), 1 walls and solids, 2 also SLIP,
+// VELOCITY or PRESSURE faces.
+template <typename R>
+inline int boundary_rules(const Bounce<R>& b)
+{
+    return b.in_kernel ? ((b.slip | b.vel | b.pres) ? 2 : 1) : 0;
+}
+
 // Launch wrappers (defined in lbm_kernels.hip).  Each returns the HIP error
 // of the launch.  L is the lattice pair (Lat3D: D3Q19 + D3Q7, Lat2D: D2Q9 +
 // D2Q5 on one z layer); the link gather / scatter passes do not depend on it.
-template <class L, typename R> hipError_t launch_aa_step(const StepArgs<R>& a, bool thermal, hipStream_t s);
-template <class L, typename R> hipError_t launch_ab_collide(const StepArgs<R>& a, bool thermal, hipStream_t s);
-template <class L, typename R> hipError_t launch_ab_pull(const StepArgs<R>& a, bool thermal, hipStream_t s);
+// `lds`: bytes of local data share reserved per block and never used, which
+// bounds the blocks resident on one compute unit (0: no reservation).
+template <class L, typename R>
+hipError_t launch_aa_step(const StepArgs<R>& a, bool thermal, size_t lds, hipStream_t s);
+template <class L, typename R>
+hipError_t launch_ab_collide(const StepArgs<R>& a, bool thermal, size_t lds, hipStream_t s);
+template <class L, typename R>
+hipError_t launch_ab_pull(const StepArgs<R>& a, bool thermal, size_t lds, hipStream_t s);
 template <typename R> hipError_t launch_link_gather(const LinkArgs<R>& a, hipStream_t s);
 template <typename R> hipError_t launch_link_scatter(const LinkArgs<R>& a, hipStream_t s);
 template <typename R> hipError_t launch_link_direct(const LinkArgs<R>& a, hipStream_t s);

@@ -965,42 +965,50 @@ inline dim3 grid_for(int64_t n) { return dim3((unsigned)((n + BLOCK - 1) / BLOCK
 
 }  // namespace
 
+// One launch of a cell kernel over the whole box.  A reservation of more
+// than 64 KiB of local data share needs the kernel's limit raised first.
+template <auto K, typename A>
+hipError_t launch_cells(const A& a, size_t lds, hipStream_t s)
+{
+    if (lds > 65536) {
+        const hipError_t e = hipFuncSetAttribute((const void*)K, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(K, grid_for(a.geo.ncell), dim3(BLOCK), lds, s, a);
+    return hipGetLastError();
+}
+
 // Pick the <thermal, boundary rules> instance of a cell kernel: no in-kernel
 // boundary, walls and solids only, or also SLIP / VELOCITY / PRESSURE faces.
-#define LBM_CELL_LAUNCH(KERNEL, a, thermal, s)                                                              \
-    do {                                                                                                    \
-        const dim3 grid_ = grid_for((a).geo.ncell);                                                         \
-        const int bnd_ = (a).bb.in_kernel ? (((a).bb.slip | (a).bb.vel | (a).bb.pres) ? 2 : 1) : 0;        \
-        if (thermal) {                                                                                      \
-            if (bnd_ == 2) hipLaunchKernelGGL((KERNEL<L, R, true, 2>), grid_, dim3(BLOCK), 0, s, a);        \
-            else if (bnd_ == 1) hipLaunchKernelGGL((KERNEL<L, R, true, 1>), grid_, dim3(BLOCK), 0, s, a);   \
-            else hipLaunchKernelGGL((KERNEL<L, R, true, 0>), grid_, dim3(BLOCK), 0, s, a);                  \
-        } else {                                                                                            \
-            if (bnd_ == 2) hipLaunchKernelGGL((KERNEL<L, R, false, 2>), grid_, dim3(BLOCK), 0, s, a);       \
-            else if (bnd_ == 1) hipLaunchKernelGGL((KERNEL<L, R, false, 1>), grid_, dim3(BLOCK), 0, s, a);  \
-            else hipLaunchKernelGGL((KERNEL<L, R, false, 0>), grid_, dim3(BLOCK), 0, s, a);                 \
-        }                                                                                                   \
+#define LBM_CELL_LAUNCH(KERNEL, a, thermal, lds, s)                                       \
+    do {                                                                                  \
+        const int bnd_ = boundary_rules((a).bb);                                          \
+        if (thermal) {                                                                    \
+            if (bnd_ == 2) return launch_cells<KERNEL<L, R, true, 2>>(a, lds, s);         \
+            if (bnd_ == 1) return launch_cells<KERNEL<L, R, true, 1>>(a, lds, s);         \
+            return launch_cells<KERNEL<L, R, true, 0>>(a, lds, s);                        \
+        }                                                                                 \
+        if (bnd_ == 2) return launch_cells<KERNEL<L, R, false, 2>>(a, lds, s);            \
+        if (bnd_ == 1) return launch_cells<KERNEL<L, R, false, 1>>(a, lds, s);            \
+        return launch_cells<KERNEL<L, R, false, 0>>(a, lds, s);                           \
     } while (0)
 
 template <class L, typename R>
-hipError_t launch_aa_step(const StepArgs<R>& a, bool thermal, hipStream_t s)
+hipError_t launch_aa_step(const StepArgs<R>& a, bool thermal, size_t lds, hipStream_t s)
 {
-    LBM_CELL_LAUNCH(k_aa_step, a, thermal, s);
-    return hipGetLastError();
+    LBM_CELL_LAUNCH(k_aa_step, a, thermal, lds, s);
 }
 
 template <class L, typename R>
-hipError_t launch_ab_collide(const StepArgs<R>& a, bool thermal, hipStream_t s)
+hipError_t launch_ab_collide(const StepArgs<R>& a, bool thermal, size_t lds, hipStream_t s)
 {
-    LBM_CELL_LAUNCH(k_ab_collide, a, thermal, s);
-    return hipGetLastError();
+    LBM_CELL_LAUNCH(k_ab_collide, a, thermal, lds, s);
 }
 
 template <class L, typename R>
-hipError_t launch_ab_pull(const StepArgs<R>& a, bool thermal, hipStream_t s)
+hipError_t launch_ab_pull(const StepArgs<R>& a, bool thermal, size_t lds, hipStream_t s)
 {
-    LBM_CELL_LAUNCH(k_ab_pull, a, thermal, s);
-    return hipGetLastError();
+    LBM_CELL_LAUNCH(k_ab_pull, a, thermal, lds, s);
 }
 
 template <typename R>
@@ -1069,9 +1077,9 @@ hipError_t launch_zero_f64(double* p, int64_t n, hipStream_t s)
 }
 
 #define LBM_INSTANTIATE_LATTICE(L, R)                                                      \
-    template hipError_t launch_aa_step<L, R>(const StepArgs<R>&, bool, hipStream_t);       \
-    template hipError_t launch_ab_collide<L, R>(const StepArgs<R>&, bool, hipStream_t);    \
-    template hipError_t launch_ab_pull<L, R>(const StepArgs<R>&, bool, hipStream_t);       \
+    template hipError_t launch_aa_step<L, R>(const StepArgs<R>&, bool, size_t, hipStream_t);    \
+    template hipError_t launch_ab_collide<L, R>(const StepArgs<R>&, bool, size_t, hipStream_t); \
+    template hipError_t launch_ab_pull<L, R>(const StepArgs<R>&, bool, size_t, hipStream_t);    \
     template hipError_t launch_link_force<L, R>(const LinkArgs<R>&, hipStream_t);          \
     template hipError_t launch_init<L, R>(const FieldArgs<R>&, bool, hipStream_t);         \
     template hipError_t launch_read<L, R>(const FieldArgs<R>&, bool, hipStream_t);         \

@@ -47,7 +47,8 @@ def test_struct_layout_matches_header():
     assert P.s9.offset == P.lattice.offset + 8
     assert P.s5.offset == P.s9.offset + 8 * 9
     assert P.tile_log2.offset == P.s5.offset + 8 * 5
-    assert binding.ctypes.sizeof(P) == P.tile_log2.offset + 8
+    assert P.occupancy.offset == P.tile_log2.offset + 8
+    assert binding.ctypes.sizeof(P) == P.occupancy.offset + 8
 
 
 def periodic(n=8, **kw):
@@ -81,6 +82,8 @@ def test_required_bytes_sizes(lib):
     lambda p: p.update(tile_log2=5),
     lambda p: p.update(tile_log2=21),
     lambda p: p.update(tile_log2=-1),
+    lambda p: p.update(occupancy=[9, 0]),
+    lambda p: p.update(occupancy=[0, -2]),
 ])
 def test_invalid_params_rejected_without_device_work(lib, mutate):
     p = periodic()
