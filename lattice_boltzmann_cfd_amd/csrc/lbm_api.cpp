@@ -372,21 +372,26 @@ Bounce<R> make_bounce(const lbm_params* p, bool in_kernel, void* face_vel)
 
 // Blocks per compute unit that occupancy = 0 gives the in-place step kernel,
 // for the even and the odd step (-1: no bound).  Chosen by interleaved
-// timings on MI355X of whole steps at bounds of 1 to 4 blocks and none:
-// D3Q19 fp32 on a periodic 256^3 box, the same in fp64, the heated 256^3
-// cavity (D3Q19 + D3Q7) in fp32 and fp64, the 512^3 box with random spheres,
-// the heated 8193^2 square (D2Q9 + D2Q5) in fp32 and fp64 and the 256x128x128
-// channel with a velocity inlet and a pressure outlet.  Instances not listed
-// were not measured and keep the bound their registers give.
+// timings on MI355X of whole steps at bounds of 1 to 4 blocks and none, on
+// 256^3 periodic boxes (D3Q19, fp32 and fp64), a sphere in a 256^3 box (fp32,
+// fp64), the heated 256^3 cavity (D3Q19 + D3Q7, fp32 and fp64), a 512^3 box
+// with random spheres, 8192^2 periodic and 8193^2 heated squares (D2Q9, and
+// with D2Q5, fp32 and fp64) and channels of 256x128x128 and 512x256x256
+// cells with a velocity inlet and a pressure outlet (open faces: every bound
+// was slower).  Instances not listed keep the bound their registers give.
 struct OccupancyChoice {
     int lattice, dtype, thermal, rules, even, odd;
 };
 constexpr OccupancyChoice OCCUPANCY_TABLE[] = {
     {LBM_LATTICE_3D, 4, 0, 0, 2, 2},
+    {LBM_LATTICE_3D, 4, 0, 1, 2, 3},
     {LBM_LATTICE_3D, 4, 1, 1, 2, -1},
     {LBM_LATTICE_3D, 8, 0, 0, 1, 2},
+    {LBM_LATTICE_3D, 8, 0, 1, 1, 2},
     {LBM_LATTICE_3D, 8, 1, 1, 1, 2},
+    {LBM_LATTICE_2D, 4, 0, 0, 3, 3},
     {LBM_LATTICE_2D, 4, 1, 1, 3, 4},
+    {LBM_LATTICE_2D, 8, 0, 0, 2, 2},
     {LBM_LATTICE_2D, 8, 1, 1, 2, 2},
 };
 
