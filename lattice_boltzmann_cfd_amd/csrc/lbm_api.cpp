@@ -175,14 +175,12 @@ bool solid_on_slip_layer(const lbm_params* p, const uint8_t* labels)
     const int n[3] = {p->nx, p->ny, p->nz};
     for (int f = 0; f < 6; ++f) {
         if (p->face_kind[f] != LBM_FACE_SLIP) continue;
-        const int a = f / 2;
-        const int layer = (f & 1) ? n[a] - 1 : 0;
-        for (int z = 0; z < n[2]; ++z)
-            for (int y = 0; y < n[1]; ++y)
-                for (int x = 0; x < n[0]; ++x) {
-                    const int c[3] = {x, y, z};
-                    if (c[a] == layer && labels[x + (int64_t)n[0] * (y + (int64_t)n[1] * z)]) return true;
-                }
+        const int a = f / 2, b = (a + 1) % 3, d = (a + 2) % 3;  // the face's normal axis and its two in-plane axes
+        int c[3];
+        c[a] = (f & 1) ? n[a] - 1 : 0;
+        for (c[d] = 0; c[d] < n[d]; ++c[d])
+            for (c[b] = 0; c[b] < n[b]; ++c[b])
+                if (labels[c[0] + (int64_t)n[0] * (c[1] + (int64_t)n[1] * c[2])]) return true;
     }
     return false;
 }

@@ -138,6 +138,26 @@ def test_solid_on_a_slip_layer_rejected(lib):
     assert e.value.status == binding.LBM_E_INVALID
 
 
+@pytest.mark.parametrize("face", range(6))
+def test_solid_on_each_slip_layer_rejected(lib, face):
+    """On a 6x7x5 box with the two faces of one axis SLIP: a solid cell one
+    layer inside is accepted, one on the face's own layer is rejected."""
+    shape = (6, 7, 5)
+    a = face // 2
+    kinds = [0] * 6
+    kinds[2 * a] = kinds[2 * a + 1] = 2
+    p = inputs.base_params(*shape, inputs.mrt_rates(0.6), face_kind=kinds)
+    layer = shape[a] - 1 if face & 1 else 0
+    inner = shape[a] - 2 if face & 1 else 1
+    for pos, accepted in ((inner, True), (layer, False)):
+        c = [3, 4, 2]
+        c[a] = pos
+        lab = np.zeros(shape[::-1], np.uint8)
+        lab[c[2], c[1], c[0]] = 1
+        lab = lab.reshape(-1)
+        assert (binding.lbm_required_bytes(p, lab) > 0) == accepted, (face, pos)
+
+
 @pytest.mark.parametrize("kinds", [[2] * 6, [3, 4, 2, 2, 1, 3], [4] * 6])
 def test_link_counts_do_not_depend_on_face_kind(lib, kinds):
     """Every non-periodic face blocks the same links whatever its rule."""
