@@ -135,9 +135,10 @@ enum { LBM_LATTICE_3D = 0, LBM_LATTICE_2D = 1 };
  * Kinetic Fluid Simulation", Sec. 4.1); thermal boxes may keep the
  * temperature planes in the same tiles.  tile_log2 = 0 picks the layout
  * measured fastest on MI355X: tiles of 32 KiB per plane (2^13 fp32 or 2^12
- * fp64 cells) when the box holds at least four tiles, shared tiles for
- * thermal fp32.  6..20 asks for tiles of 2^k cells (shared for thermal
- * boxes).  31 asks for one plane per population over the whole box (the
+ * fp64 cells; 64 KiB, 2^14 cells, for isothermal fp32 D3Q19) when the box
+ * holds at least four tiles, shared tiles for thermal fp32.  6..20 asks for
+ * tiles of 2^k cells (shared for thermal boxes).  31 asks for one plane per
+ * population over the whole box (the
  * structure of arrays of "Multi-GPU thermal lattice Boltzmann simulations
  * using OpenACC and MPI", Sec. 3).  Whatever is asked, a buffer that would
  * reach 4 GiB tiled is stored one plane per population. */

@@ -44,7 +44,7 @@ struct lbm_ctx {
     bool initialised = false;
     bool in_kernel = false;  // bounce-back inside the step kernel
     size_t lds[2] = {0, 0};  // per parity: local data share reserved per block of the step kernel
-    // replay of one even+odd pair of steps as a HIP graph (captured once on a
+    // replay of 8 even+odd pairs of steps as a HIP graph (captured once on a
     // private stream, launched on the caller's)
     hipStream_t capture_stream = nullptr;
     hipGraphExec_t pair = nullptr;
@@ -107,13 +107,23 @@ bool finite(double v) { return std::isfinite(v); }
 int64_t plane_stride(int64_t n) { return (n + 63) / 64 * 64 + 1024; }
 
 // Automatic tiling (lbm_params.tile_log2 = 0): tiles hold 32 KiB of each
-// plane (2^13 fp32 or 2^12 fp64 cells), and a thermal fp32 box keeps its
-// temperature planes in the same tiles as its flow planes.  Measured on
-// MI355X in same-box A/B runs of this library against one plane per
-// population: 256^3 fp32 step -6.1 %, 256^3 thermal fp32 -5.1 % (-1.2 % more
-// with shared tiles), the 8193^2 2D cell in fp32 -9.3 % (-2.0 % more), 256^3
-// fp64 -2.8 % with 2^12 instead of 2^13 cells; shared tiles cost 0.7 % in fp64.
+// plane (2^13 fp32 or 2^12 fp64 cells), 64 KiB (2^14 cells) for an
+// isothermal fp32 D3Q19 box, and a thermal fp32 box keeps its temperature
+// planes in the same tiles as its flow planes.  Measured on MI355X in
+// same-box A/B runs of this library against one plane per population:
+// 256^3 fp32 step -6.1 %, 256^3 thermal fp32 -5.1 % (-1.2 % more with
+// shared tiles), the 8193^2 2D cell in fp32 -9.3 % (-2.0 % more), 256^3 fp64
+// -2.8 % with 2^12 instead of 2^13 cells; shared tiles cost 0.7 % in fp64.
+// With the occupancy bounds, 2^14 instead of 2^13 cells: 256^3 isothermal
+// fp32 -1.4 % (a sphere in that box and the open channel: within 0.4 %);
+// every other instance as fast or faster at 32 KiB per plane.
 constexpr int64_t TILE_PLANE_BYTES = 32768;
+
+int64_t tile_plane_bytes(const lbm_params* p)
+{
+    const bool iso3d_fp32 = p->lattice == LBM_LATTICE_3D && !p->thermal && p->dtype == 4;
+    return iso3d_fp32 ? 2 * TILE_PLANE_BYTES : TILE_PLANE_BYTES;
+}
 
 // Tile geometry of the population buffers (see Geometry).  Tiles are used
 // when asked for (tile_log2 in 6..20) or, automatically, when the box holds
@@ -135,7 +145,7 @@ void tile_geometry(const lbm_params* p, Geometry* G, int64_t* elems_f, int64_t* 
     uint32_t lg = (uint32_t)p->tile_log2;
     if (automatic) {
         lg = 0;
-        while ((int64_t(1) << (lg + 1)) * p->dtype <= TILE_PLANE_BYTES) ++lg;
+        while ((int64_t(1) << (lg + 1)) * p->dtype <= tile_plane_bytes(p)) ++lg;
     }
     *g_in_f = -1;
     if (lg < 31 && (!automatic || n >= (int64_t(4) << lg))) {
@@ -776,10 +786,11 @@ lbm_status enqueue_step(lbm_ctx* c, hipStream_t stream, bool last)
     return LBM_OK;
 }
 
-// Capture even/odd step pairs (kernel arguments and all) as one graph, once
-// per context: 8 pairs for boxes up to 2^21 cells, where launch overhead is
-// comparable to a step, else 1.  Any failure leaves the context on per-step
-// launches.
+// Capture 8 even/odd step pairs (kernel arguments and all) as one graph,
+// once per context.  Replays of 16 steps measured 0.4-1.7 % faster than of 2
+// steps on boxes of 4 M to 67 M cells (no slower on any), the gaps between
+// graph launches being a larger share of a short step.  Any failure leaves
+// the context on per-step launches.
 template <class L, typename R>
 void capture_pair(lbm_ctx* c)
 {
@@ -793,7 +804,7 @@ void capture_pair(lbm_ctx* c)
     const std::string err_saved = c->err;
     c->t = 0;
     hipGraph_t graph = nullptr;
-    const int steps = c->geo.ncell <= (1 << 21) ? 16 : 2;
+    const int steps = 16;
     bool ok = hipStreamBeginCapture(c->capture_stream, hipStreamCaptureModeThreadLocal) == hipSuccess;
     if (ok) {
         bool launched = true;

@@ -5,7 +5,9 @@ with tiles must give the fields of the same run stored one plane per
 population bit for bit (that run is checked against the oracle by the other
 parity tests).  Forced small tiles (64 and 512 cells) make every box here span
 many tiles with a ragged last one, and put tile boundaries inside rows and
-across walls, solids and open faces; thermal boxes keep their temperature
+across walls, solids and open faces; forced tiles of 2^14 cells, the size
+chosen automatically for isothermal fp32 boxes, leave a box of this size in
+one or a few tiles with a ragged tail.  Thermal boxes keep their temperature
 planes in the flow planes' tiles.  Automatic tiling is checked where it
 engages at these sizes (fp64).  Submissions of 7 and 93 steps cover both step
 parities and the graph replays."""
@@ -48,7 +50,7 @@ def same_fields(a, b, w, label):
 
 
 @pytest.mark.parametrize("dtype", [4, 8])
-@pytest.mark.parametrize("tile", [6, 9, 0])
+@pytest.mark.parametrize("tile", [6, 9, 14, 0])
 @pytest.mark.parametrize("case", sorted(CASES))
 def test_tiled_equals_untiled_bitwise(case, tile, dtype):
     say(f"CASE tiles {case} tile_log2={tile} dtype={dtype}")
