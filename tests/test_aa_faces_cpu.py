@@ -249,10 +249,35 @@ def case(name):
                                face_u=fu, face_rho=[1.0, 0.998, 1, 1, 1.001, 1.0], accel=(1e-4, 0, 0))
         rho, u = inputs.taylor_green(nx, ny, nz, u0=0.03, seed=25)
         return p, None, rho, u, None
-    raise KeyError(name)
+    return degenerate_face_case(name)
 
 
-@pytest.mark.parametrize("name", ["slip_sphere", "lid", "inlet_outlet_thermal", "mixed_edges"])
+def degenerate_face_case(name):
+    """One cell thick along the axis of the open faces: a SLIP gap (each cell
+    reflects off both faces) and an inlet/outlet pair one cell apart in y and
+    z (every x-neighbour link of the end cells is an open-face link)."""
+    rng = np.random.default_rng(26)
+    if name == "slip_gap":
+        nx, ny, nz = 1, 6, 4
+        p = inputs.base_params(nx, ny, nz, inputs.mrt_rates(0.7), accel=(0, 2e-4, -1e-4),
+                               face_kind=[SLIP, SLIP, PER, PER, PER, PER])
+    elif name == "open_rod":
+        nx, ny, nz = 6, 1, 1
+        fu = np.zeros((6, 3))
+        fu[0] = (0.03, 0.01, 0.0)
+        p = inputs.base_params(nx, ny, nz, inputs.mrt_rates(0.65), thermal=True, face_kind=[VEL, PRES, PER, PER, PER, PER],
+                               face_u=fu, face_rho=[1.0, 0.998, 1, 1, 1, 1], face_thermal=[1, 0, 0, 0, 0, 0],
+                               face_T=[0.5, 0, 0, 0, 0, 0], s7=inputs.thermal_rates(0.05))
+    else:
+        raise KeyError(name)
+    n = nx * ny * nz
+    rho = 1.0 + rng.uniform(-1e-2, 1e-2, n)
+    u = rng.uniform(-0.03, 0.03, (3, n))
+    T = rng.uniform(-0.5, 0.5, n) if p["thermal"] else None
+    return p, None, rho, u, T
+
+
+@pytest.mark.parametrize("name", ["slip_sphere", "lid", "inlet_outlet_thermal", "mixed_edges", "slip_gap", "open_rod"])
 def test_in_place_face_rules_equal_two_buffer_bitwise(name):
     p, lab, rho, u, T = case(name)
     model = Model(p, lab, rho, u, T)

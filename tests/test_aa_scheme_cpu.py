@@ -265,11 +265,47 @@ def case(name):
         p = dict(p, solid_thermal=1, solid_T=-0.3, face_kind=[WALL] * 6, face_thermal=[1, 1, 0, 0, 1, 1],
                  face_T=[0.1, -0.1, 0, 0, 0.5, -0.5])
         return p, lab, rho, u, T
-    raise KeyError(name)
+    return degenerate_case(name)
+
+
+def degenerate_case(name):
+    """Boxes where the slot bookkeeping meets itself: one cell (every
+    neighbour is the cell), one cell thick between two walls (each cell
+    bounces off both), 2x2x2 walled (every cell a corner) and one fluid cell
+    closed in by solids (every link blocked)."""
+    WALL, PER = inputs.FACE_WALL, inputs.FACE_PERIODIC
+    shapes = {"one_cell": (1, 1, 1), "one_thick_gap": (1, 6, 4), "corners": (2, 2, 2), "caged_cell": (4, 4, 4)}
+    nx, ny, nz = shapes[name]
+    n = nx * ny * nz
+    rng = np.random.default_rng(21)
+    rho = 1.0 + rng.uniform(-1e-2, 1e-2, n)
+    u = rng.uniform(-0.03, 0.03, (3, n))
+    T = rng.uniform(-0.5, 0.5, n)
+    lab = None
+    kinds, therm, temps = [PER] * 6, [0] * 6, [0.0] * 6
+    if name == "one_thick_gap":
+        kinds[0] = kinds[1] = WALL
+        therm[0] = therm[1] = 1
+        temps[0], temps[1] = 0.5, -0.5
+    elif name == "corners":
+        kinds = [WALL] * 6
+        therm = [1, 1, 0, 0, 1, 0]
+        temps = [0.5, -0.5, 0, 0, 0.2, 0]
+    elif name == "caged_cell":
+        lab = np.ones(n, np.uint8)
+        lab[cell_index(1, 2, 1, (nx, ny, nz))] = 0
+        lab[cell_index(3, 3, 3, (nx, ny, nz))] = 2
+    p = inputs.base_params(nx, ny, nz, inputs.mrt_rates(0.65), thermal=True, face_kind=kinds, face_thermal=therm,
+                           face_T=temps, s7=inputs.thermal_rates(0.05), accel=(2e-4, -1e-4, 5e-5),
+                           gbeta=(0, 0, 1e-3), solid_thermal=1, solid_T=0.3)
+    return p, lab, rho, u, T
+
+
+DEGENERATE = ["one_cell", "one_thick_gap", "corners", "caged_cell"]
 
 
 @pytest.mark.parametrize("scheme", ["links", "inkernel"])
-@pytest.mark.parametrize("name", ["walls_solids", "cavity_thermal", "rb_spheres", "dirichlet_solid"])
+@pytest.mark.parametrize("name", ["walls_solids", "cavity_thermal", "rb_spheres", "dirichlet_solid"] + DEGENERATE)
 def test_aa_equals_two_buffer_bitwise(name, scheme):
     p, lab, rho, u, T = case(name)
     model = AAModel(p, lab, rho, u, T, scheme=scheme)

@@ -1,0 +1,90 @@
+"""GPU parity on the method's degenerate boxes.
+
+Boxes where a cell's neighbours are the cell itself or where every link of a
+cell is blocked: one cell (periodic), one cell thick between two no-slip
+Dirichlet walls (each cell bounces off both), 2x2x2 with walls (every cell a
+corner), one fluid cell closed in by solids, one cell thick between two SLIP
+faces, a one-cell-thick channel from a velocity inlet to a pressure outlet,
+and the 2D lattice's single cell and one-cell-wide strip.  The same boxes run
+through the CPU models of the in-place scheme (tests/test_aa_scheme_cpu.py,
+tests/test_aa_faces_cpu.py), which match the oracle bit for bit.  Bar as in
+the other parity tests; the other layouts and launch choices must give the
+same fields bit for bit."""
+import numpy as np
+import pytest
+
+from harness import fluid_mask, gpu_run, oracle_run, say
+from lattice_boltzmann_cfd_amd import binding, inputs
+from test_aa_faces_cpu import degenerate_face_case
+from test_aa_scheme_cpu import degenerate_case
+from test_gpu_parity import check_fields, check_forces
+
+pytestmark = pytest.mark.gpu
+
+
+def two_d_case(name):
+    rng = np.random.default_rng(31)
+    WALL, PER = inputs.FACE_WALL, inputs.FACE_PERIODIC
+    if name == "one_cell_2d":
+        nx, ny = 1, 1
+        kinds, therm, temps = [PER] * 4, [0] * 4, [0.0] * 4
+    else:  # one_wide_strip_2d
+        nx, ny = 1, 7
+        kinds, therm, temps = [WALL, WALL, PER, PER], [1, 1, 0, 0], [0.5, -0.5, 0.0, 0.0]
+    p = inputs.base_params_2d(nx, ny, inputs.mrt_rates_2d(0.65), thermal=True, face_kind=kinds, face_thermal=therm,
+                              face_T=temps, s5=inputs.thermal_rates_2d(0.05), accel=(2e-4, -1e-4), gbeta=(0, 1e-3))
+    n = nx * ny
+    rho = 1.0 + rng.uniform(-1e-2, 1e-2, n)
+    u = rng.uniform(-0.03, 0.03, (3, n))
+    u[2] = 0.0
+    T = rng.uniform(-0.5, 0.5, n)
+    return p, None, rho, u, T
+
+
+BUILDERS = {
+    "one_cell": degenerate_case,
+    "one_thick_gap": degenerate_case,
+    "corners": degenerate_case,
+    "caged_cell": degenerate_case,
+    "slip_gap": degenerate_face_case,
+    "open_rod": degenerate_face_case,
+    "one_cell_2d": two_d_case,
+    "one_wide_strip_2d": two_d_case,
+}
+OPEN_FACES = {"slip_gap", "open_rod"}
+
+
+def workload(name):
+    p, lab, rho, u, T = BUILDERS[name](name)
+    return inputs.Workload(name, p, rho, u, T, lab, 31)
+
+
+@pytest.mark.parametrize("dtype", [4, 8])
+@pytest.mark.parametrize("name", sorted(BUILDERS))
+def test_degenerate_box_parity(name, dtype):
+    say(f"CASE degenerate {name} dtype={dtype}")
+    w = workload(name)
+    g = gpu_run(w, [7, 24], dtype=dtype)
+    o = oracle_run(w, 31, want_diag=True)
+    check_fields(g, o, w, dtype, name)
+    check_forces(g["forces"][-1], o["diag"][-1], dtype, g["links19"] + g["links7"], name)
+
+
+@pytest.mark.parametrize("name", sorted(BUILDERS))
+def test_degenerate_box_layouts_and_launches_bitwise(name):
+    say(f"CASE degenerate variants {name}")
+    w = workload(name)
+    ref = gpu_run(w, [7, 24])
+    fl = fluid_mask(w)
+    variants = [("two buffers", {}, binding.LBM_STREAM_AB), ("tiles of 64 cells", {"tile_log2": 6}, None),
+                ("occupancy 1/2", {"occupancy": [1, 2]}, None)]
+    if name not in OPEN_FACES:
+        variants.append(("link passes", {"links": binding.LBM_LINKS_PASSES}, None))
+    for label, extra, streaming in variants:
+        v = inputs.Workload(w.name, dict(w.params, **extra), w.rho, w.u, w.T, w.labels, w.steps)
+        got = gpu_run(v, [7, 24], streaming=streaming if streaming is not None else binding.LBM_STREAM_AUTO)
+        for k in ("rho", "u", "T"):
+            if ref[k] is None:
+                continue
+            a, b = got[k][..., fl], ref[k][..., fl]
+            assert np.array_equal(a, b), f"{name} {label}: {k} differs by {np.abs(a - b).max():.3e}"
