@@ -796,7 +796,7 @@ __global__ void __launch_bounds__(BLOCK) k_init(FieldArgs<R> a)
 #pragma unroll
         for (int k = 0; k < L::QT; ++k) g[k] = nan;
     } else {
-        const int32_t n = G.ncell;
+        const int64_t n = G.ncell;  // the velocity planes u[k * n + cell] reach 3 n > 2^31
         const R T = (TH && a.T) ? a.T[cell] : R(0);
         equilibrium<R, TH>(a.rho[cell], a.u[cell], a.u[n + cell], a.u[2 * n + cell], T, a.col.a_T, h, g);
     }
@@ -866,7 +866,7 @@ __global__ void __launch_bounds__(BLOCK) k_read(FieldArgs<R> a)
     const Geometry& G = a.geo;
     const int32_t cell = (int32_t)(blockIdx.x * BLOCK + threadIdx.x);
     if (cell >= G.ncell) return;
-    const int32_t n = G.ncell;
+    const int64_t n = G.ncell;  // the velocity planes u_out[k * n + cell] reach 3 n > 2^31
     R h[L::Q];
     R g[L::QT];
     Macro<R> m;

@@ -1,0 +1,153 @@
+"""GPU parity at the largest boxes the library accepts.
+
+A population plane (one plane per population) or a whole tiled buffer must
+stay below 2^32 - 2^20 bytes, because lanes address it with 32-bit offsets.
+These boxes sit just under that limit, where an offset overflow would show:
+  * fp32 D3Q19, one plane per population: 1.07e9 cells (81 GB), walls on z;
+  * fp64 D3Q19, one plane per population: 5.37e8 cells (81 GB), periodic;
+  * fp32 D3Q19 in tiles of 2^14 cells: the largest tiled buffer, walls on z;
+  * fp32 D3Q19 + D3Q7 in shared tiles of 2^13 cells: the largest tiled
+    thermal buffer, a heated cavity.
+One layer more is rejected (one plane per population) or stored untiled
+(tiles), checked on the host.  The initial state is an analytic field
+generated on the device; after 9 steps, windows at the box's first cells,
+its middle and its last cells are compared element by element with the
+oracle stepping the same windows (cells farther than 9 from a cut window edge
+are exact), to the parity bar.  Only the windows are read back."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from harness import say, window_indices, window_valid
+from lattice_boltzmann_cfd_amd import binding, inputs
+
+pytestmark = pytest.mark.gpu
+
+LIMIT = 2 ** 32 - 2 ** 20
+TOL = {4: 1e-4, 8: 1e-11}
+STEPS = 9
+WIN = 32
+WALL, PER = inputs.FACE_WALL, inputs.FACE_PERIODIC
+
+
+def case(name):
+    if name == "planes_f32":
+        shape, dtype, thermal = (1021, 1030, 1020), 4, False
+        kinds = [PER, PER, PER, PER, WALL, WALL]
+    elif name == "planes_f64":
+        shape, dtype, thermal = (811, 812, 815), 8, False
+        kinds = [PER] * 6
+    elif name == "tiles_f32":
+        shape, dtype, thermal = (383, 383, 385), 4, False
+        kinds = [PER, PER, PER, PER, WALL, WALL]
+    elif name == "tiles_thermal_f32":
+        shape, dtype, thermal = (345, 344, 347), 4, True
+        kinds = [WALL] * 6
+    else:
+        raise KeyError(name)
+    kw = dict(face_kind=kinds, accel=(1e-5, 2e-6, 0.0))
+    if thermal:
+        kw.update(thermal=True, face_thermal=[1, 1, 0, 0, 0, 0], face_T=[0.5, -0.5, 0, 0, 0, 0],
+                  s7=inputs.thermal_rates(0.02), gbeta=(0.0, 0.0, 1e-4))
+    p = inputs.base_params(*shape, inputs.mrt_rates(0.6), **kw)
+    return p, dtype
+
+
+def state_np(shape, idx, thermal):
+    """The initial state at cell indices idx (fp64)."""
+    nx, ny, nz = shape
+    x, y, z = idx % nx, (idx // nx) % ny, idx // (nx * ny)
+    sx, sy, sz = (np.sin(2 * math.pi * x / nx), np.sin(2 * math.pi * y / ny), np.sin(2 * math.pi * z / nz))
+    rho = 1.0 + 0.01 * sx * sy
+    u = np.stack([0.03 * sy, 0.03 * sz, 0.03 * sx])
+    T = 0.4 * sx * sz if thermal else None
+    return rho, u, T
+
+
+def state_device(torch, shape, dtype, thermal, chunk=1 << 26):
+    """The same state on the device, chunk by chunk, in the run's precision."""
+    nx, ny, nz = shape
+    n = nx * ny * nz
+    td = torch.float32 if dtype == 4 else torch.float64
+    rho = torch.empty(n, dtype=td, device="cuda")
+    u = torch.empty((3, n), dtype=td, device="cuda")
+    T = torch.empty(n, dtype=td, device="cuda") if thermal else None
+    for s in range(0, n, chunk):
+        idx = torch.arange(s, min(n, s + chunk), dtype=torch.int64, device="cuda")
+        x, y, z = idx % nx, (idx // nx) % ny, idx // (nx * ny)
+        sx = torch.sin(2 * math.pi * x.double() / nx)
+        sy = torch.sin(2 * math.pi * y.double() / ny)
+        sz = torch.sin(2 * math.pi * z.double() / nz)
+        rho[s:s + idx.numel()] = (1.0 + 0.01 * sx * sy).to(td)
+        u[0, s:s + idx.numel()] = (0.03 * sy).to(td)
+        u[1, s:s + idx.numel()] = (0.03 * sz).to(td)
+        u[2, s:s + idx.numel()] = (0.03 * sx).to(td)
+        if thermal:
+            T[s:s + idx.numel()] = (0.4 * sx * sz).to(td)
+        del idx, x, y, z, sx, sy, sz
+    return rho, u, T
+
+
+def required(p, dtype, **extra):
+    return binding.lbm_required_bytes(dict(p, **extra), None, dtype=dtype)
+
+
+@pytest.mark.parametrize("name", ["planes_f32", "planes_f64", "tiles_f32", "tiles_thermal_f32"])
+def test_largest_box_windows(name):
+    import torch
+
+    p, dtype = case(name)
+    shape = (p["nx"], p["ny"], p["nz"])
+    n = shape[0] * shape[1] * shape[2]
+    thermal = bool(p["thermal"])
+    say(f"CASE largest box {name} {shape} = {n:,} cells, dtype={dtype}")
+    bigger = dict(p, nz=p["nz"] + 1)
+    if name.startswith("planes"):
+        # one plane per population: the plane is just under the limit, one layer more is rejected
+        assert ((n + 63) // 64 * 64 + 1024) * dtype < LIMIT
+        assert required(p, dtype) == required(p, dtype, tile_log2=31)
+        assert required(bigger, dtype) == 0
+    else:
+        # tiled: the whole tiled buffer just under the limit; one layer more is stored untiled
+        tiled, untiled = required(p, dtype), required(p, dtype, tile_log2=31)
+        assert tiled != untiled
+        planes = 26 if thermal else 19
+        lg = 13 if thermal else 14
+        tiles = -(-n // (1 << lg))
+        assert tiles * planes * (1 << lg) * dtype < LIMIT
+        assert required(bigger, dtype) == required(bigger, dtype, tile_log2=31)
+
+    s = binding.Solver(p, None, dtype=dtype)
+    try:
+        rho0, u0, T0 = state_device(torch, shape, dtype, thermal)
+        s.init(rho0, u0, T0)
+        s.step(STEPS)
+        rho, u, T = s.macros()
+        torch.cuda.synchronize()
+        del rho0, u0, T0
+        windows = [((0, 0, 0), (WIN,) * 3),
+                   ((shape[0] // 2, shape[1] // 2, shape[2] // 2), (WIN,) * 3),
+                   ((shape[0] - WIN, shape[1] - WIN, shape[2] - WIN), (WIN,) * 3)]
+        worst = 0.0
+        for lo, wn in windows:
+            idx = window_indices(shape, lo, wn)
+            it = torch.from_numpy(idx).cuda()
+            g_rho = rho.index_select(0, it).double().cpu().numpy()
+            g_u = u.index_select(1, it).double().cpu().numpy()
+            g_T = T.index_select(0, it).double().cpu().numpy() if thermal else None
+            r0, v0, t0 = state_np(shape, idx, thermal)
+            o = oracle.run(p, STEPS, r0, v0, t0, window=(lo, wn))
+            valid = window_valid(p, lo, wn, STEPS)
+            d = [np.abs(g_rho[valid] - o["rho"][valid]).max(), np.abs(g_u[:, valid] - o["u"][:, valid]).max()]
+            if thermal:
+                d.append(np.abs(g_T[valid] - o["T"][valid]).max())
+            say(f"  window lo={lo}: {int(valid.sum())} cells (last index {int(idx.max()):,}), max diff {max(d):.3e}")
+            worst = max(worst, max(d))
+        assert worst <= TOL[dtype], worst
+        del rho, u, T
+    finally:
+        s.close()
+        del s
+        torch.cuda.empty_cache()
