@@ -32,7 +32,7 @@ HBM_PEAK_GBPS = 8000.0
 # algorithmic bytes per cell update: every population read once and written once
 def bytes_per_cell(thermal: bool, dtype: int, streaming: int, two_d: bool = False) -> int:
     q = (9 + (5 if thermal else 0)) if two_d else (19 + (7 if thermal else 0))
-    passes = 2 if streaming == 2 else 1  # two-buffer: collide in place, then pull
+    passes = 2 if streaming == 2 else 1  # two buffers in two passes: collide in place, then pull
     return 2 * q * dtype * passes
 
 
@@ -51,6 +51,12 @@ WORKLOAD_INFO = {
                 "Ra=1e8, Pr=0.71, buoyancy +y (the thermal-LBM page's 2D case; it runs fp64)",
     "tg2d": "D2Q9 MRT, 256x256 periodic Taylor-Green, tau=0.6",
 }
+
+
+# streaming mode: (record tag, kernels of one step, description)
+STREAMING = {1: ("aa", "k_aa_step", "AA in place"),
+             2: ("ab", "k_ab_collide+k_ab_pull", "A-B two buffers, collide then pull"),
+             3: ("abpush", "k_ab_push", "A-B two buffers, one pass (collide and push)")}
 
 
 def kernel_source_hash() -> str:
@@ -72,7 +78,7 @@ def load_traffic(workload: str, dtype: int, streaming: int):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current kernel sources (else null)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{'f32' if dtype == 4 else 'f64'}"
-                        f"_{'ab' if streaming == 2 else 'aa'}.json")
+                        f"_{STREAMING[streaming][0]}.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
@@ -137,7 +143,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="sol256", choices=sorted(WORKLOAD_INFO))
     ap.add_argument("--dtype", type=int, default=4, choices=(4, 8))
-    ap.add_argument("--streaming", type=int, default=1, choices=(1, 2), help="1 in place (AA), 2 two buffers")
+    ap.add_argument("--streaming", type=int, default=1, choices=(1, 2, 3),
+                    help="1 in place (AA), 2 two buffers in two passes, 3 two buffers in one pass")
     ap.add_argument("--cpu-steps", type=int, default=6, help="oracle steps for the CPU baseline (0: skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run torch's device copy of 1 GiB 10 times (reference kernel for HBM counters)")
@@ -190,13 +197,13 @@ def main(argv=None):
     bpc = bytes_per_cell(thermal, args.dtype, args.streaming, two_d)
     flow, temp = (9, 5) if two_d else (19, 7)
     has_links = (solver.num_links(flow) + solver.num_links(temp)) > 0
-    launches = 1 if args.streaming == 1 else 2
+    launches = 2 if args.streaming == 2 else 1
     per_launch_bytes = bpc * w.cells / launches
     # periodic boxes run exactly `launches` bulk kernels per step and nothing else
     kernel_ms = ms_per_step / launches
     achieved = per_launch_bytes / (kernel_ms / 1e3) / 1e9
     traffic = load_traffic(args.workload, args.dtype, args.streaming)
-    kernel = "k_aa_step" if args.streaming == 1 else "k_ab_collide+k_ab_pull"
+    kernel = STREAMING[args.streaming][1]
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": kernel,
                 "bytes_per_cell": bpc, "launch_includes_links": has_links}
@@ -207,7 +214,7 @@ def main(argv=None):
         "vs_baseline": None, "dtype": "f32" if args.dtype == 4 else "f64", "data": "synthetic",
         "config": {"workload": args.workload, "description": WORKLOAD_INFO[args.workload],
                    "shape": list(w.shape), "cells": w.cells,
-                   "streaming": "AA in place" if args.streaming == 1 else "A-B two buffers",
+                   "streaming": STREAMING[args.streaming][2],
                    "hbm_TBps_algorithmic": round(bpc * w.cells * args.steps / (ms / 1e3) / 1e12, 3)},
         "roofline": roofline,
     }

@@ -95,7 +95,15 @@ typedef enum lbm_status {
  * non-periodic face's thermal rule (face_thermal) whatever its kind. */
 enum { LBM_FACE_PERIODIC = 0, LBM_FACE_WALL = 1, LBM_FACE_SLIP = 2, LBM_FACE_VELOCITY = 3, LBM_FACE_PRESSURE = 4 };
 enum { LBM_ADIABATIC = 0, LBM_DIRICHLET = 1 };
-enum { LBM_STREAM_AUTO = 0, LBM_STREAM_AA = 1, LBM_STREAM_AB = 2 };
+/* Streaming.  AA (AUTO): one population buffer, streamed in place with the
+ * AA pattern.  AB: two buffers, the two passes of "GPU lattice Boltzmann:
+ * streaming layout and performance" -- collide in place, then pull into the
+ * other buffer (304 B per fp32 D3Q19 cell update).  AB_PUSH: two buffers in
+ * one pass -- each cell loads its populations from one buffer, collides and
+ * pushes them into the other (152 B per update, as AA); it applies the
+ * boundary rules itself, so it needs links = LBM_LINKS_IN_KERNEL.  All three
+ * give the same populations bit for bit. */
+enum { LBM_STREAM_AUTO = 0, LBM_STREAM_AA = 1, LBM_STREAM_AB = 2, LBM_STREAM_AB_PUSH = 3 };
 enum { LBM_MAX_GROUPS = 261 }; /* 6 faces + 255 solid labels */
 /* Where half-way bounce-back happens.  IN_KERNEL: inside the step kernel (a
  * fluid cell next to a wall or solid re-reads and re-stores the bounced
@@ -144,9 +152,8 @@ enum { LBM_LATTICE_3D = 0, LBM_LATTICE_2D = 1 };
  * reach 4 GiB tiled is stored one plane per population. */
 
 /* Occupancy of the step kernels (no effect on results, only on speed).
- * occupancy[0] governs the even steps of the in-place scheme and the collide
- * kernel of the two-buffer one, occupancy[1] the odd steps and the pull
- * kernel.  k in 1..8 lets at most k blocks of 256 cells run at once on one
+ * occupancy[0] governs the even steps (in place or AB_PUSH) and the collide
+ * kernel of AB, occupancy[1] the odd steps and AB's pull kernel.  k in 1..8 lets at most k blocks of 256 cells run at once on one
  * compute unit (the launch reserves local data share that the kernel never
  * touches); -1 leaves the count to the kernel's register use; 0 picks the
  * value measured fastest on MI355X for the kernel instance (lattice,

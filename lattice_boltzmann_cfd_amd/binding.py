@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblbm_hip.
 
 LBM_OK, LBM_E_INVALID, LBM_E_NOMEM, LBM_E_DEVICE, LBM_E_UNSTABLE = 0, 1, 2, 3, 4
 STATUS_NAMES = {0: "LBM_OK", 1: "LBM_E_INVALID", 2: "LBM_E_NOMEM", 3: "LBM_E_DEVICE", 4: "LBM_E_UNSTABLE"}
-LBM_STREAM_AUTO, LBM_STREAM_AA, LBM_STREAM_AB = 0, 1, 2
+LBM_STREAM_AUTO, LBM_STREAM_AA, LBM_STREAM_AB, LBM_STREAM_AB_PUSH = 0, 1, 2, 3
 LBM_LINKS_IN_KERNEL, LBM_LINKS_PASSES = 0, 1
 LBM_LATTICE_3D, LBM_LATTICE_2D = 0, 1
 LBM_FACE_PERIODIC, LBM_FACE_WALL, LBM_FACE_SLIP, LBM_FACE_VELOCITY, LBM_FACE_PRESSURE = 0, 1, 2, 3, 4

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstring>
 #include <exception>
+#include <iterator>
 #include <new>
 #include <string>
 #include <thread>
@@ -21,7 +22,8 @@ struct lbm_ctx {
     lbm_params p;
     int es = 4;
     bool thermal = false;
-    bool ab = false;
+    bool ab = false;    // two population buffers
+    bool push = false;  // ... stepped in one pass (collide and push)
     bool two_d = false;  // D2Q9 + D2Q5 on one z layer
     hipStream_t stream = nullptr;
     Geometry geo{};
@@ -206,7 +208,7 @@ std::string validate(const lbm_params* p)
     // kernels address a population plane with 32-bit byte offsets
     if (plane_stride(n) * (int64_t)p->dtype >= (int64_t(1) << 32) - (int64_t(1) << 20))
         return "nx*ny*nz*dtype too large for 32-bit plane offsets";
-    if (p->streaming < 0 || p->streaming > 2) return "streaming must be 0, 1 or 2";
+    if (p->streaming < 0 || p->streaming > 3) return "streaming must be 0, 1, 2 or 3";
     if (p->thermal != 0 && p->thermal != 1) return "thermal must be 0 or 1";
     if (p->links != LBM_LINKS_IN_KERNEL && p->links != LBM_LINKS_PASSES) return "links must be 0 or 1";
     bool open = false;
@@ -226,6 +228,8 @@ std::string validate(const lbm_params* p)
             return "the two faces of an axis must both be periodic or both be non-periodic";
     if (open && p->links != LBM_LINKS_IN_KERNEL)
         return "SLIP, VELOCITY and PRESSURE faces need links = LBM_LINKS_IN_KERNEL";
+    if (p->streaming == LBM_STREAM_AB_PUSH && p->links != LBM_LINKS_IN_KERNEL)
+        return "streaming = LBM_STREAM_AB_PUSH needs links = LBM_LINKS_IN_KERNEL";
     if (p->solid_thermal != LBM_ADIABATIC && p->solid_thermal != LBM_DIRICHLET) return "bad solid_thermal";
     if (!finite(p->solid_T)) return "solid_T must be finite";
     if (p->lattice != LBM_LATTICE_3D && p->lattice != LBM_LATTICE_2D) return "lattice must be 0 (3D) or 1 (2D)";
@@ -402,13 +406,30 @@ constexpr OccupancyChoice OCCUPANCY_TABLE[] = {
     {LBM_LATTICE_2D, 8, 0, 0, 2, 2},
     {LBM_LATTICE_2D, 8, 1, 1, 2, 2},
 };
+// The same for the one-pass two-buffer kernel (LBM_STREAM_AB_PUSH), timed on
+// the same boxes at bounds of 1 to 4 blocks and none; open faces again ran
+// fastest unbounded.  The two-pass two-buffer kernels keep no bound.
+constexpr OccupancyChoice PUSH_OCCUPANCY_TABLE[] = {
+    {LBM_LATTICE_3D, 4, 0, 0, 3, 3},
+    {LBM_LATTICE_3D, 4, 0, 1, 3, 3},
+    {LBM_LATTICE_3D, 4, 1, 1, 2, 2},
+    {LBM_LATTICE_3D, 8, 0, 0, 2, 2},
+    {LBM_LATTICE_3D, 8, 1, 1, 2, 2},
+    {LBM_LATTICE_2D, 4, 0, 0, 3, 3},
+    {LBM_LATTICE_2D, 4, 1, 1, 2, 2},
+    {LBM_LATTICE_2D, 8, 1, 1, 2, 2},
+};
 
-int automatic_occupancy(const lbm_params* p, bool ab, int rules, int parity)
+int automatic_occupancy(const lbm_params* p, bool ab, bool push, int rules, int parity)
 {
-    if (ab) return -1;
-    for (const OccupancyChoice& o : OCCUPANCY_TABLE)
+    if (ab && !push) return -1;
+    const OccupancyChoice* table = push ? PUSH_OCCUPANCY_TABLE : OCCUPANCY_TABLE;
+    const size_t n = push ? std::size(PUSH_OCCUPANCY_TABLE) : std::size(OCCUPANCY_TABLE);
+    for (size_t i = 0; i < n; ++i) {
+        const OccupancyChoice& o = table[i];
         if (o.lattice == p->lattice && o.dtype == p->dtype && o.thermal == p->thermal && o.rules == rules)
             return parity ? o.odd : o.even;
+    }
     return -1;
 }
 
@@ -658,7 +679,7 @@ Layout make_layout(const lbm_params* p, bool solids, int64_t n_links)
     const size_t es = (size_t)p->dtype;
     const size_t fb = align_up((size_t)ef * es);
     const size_t gb = p->thermal ? align_up((size_t)eg * es) : 0;
-    const bool ab = p->streaming == LBM_STREAM_AB;
+    const bool ab = p->streaming == LBM_STREAM_AB || p->streaming == LBM_STREAM_AB_PUSH;
     size_t off = 0;
     L.f = off; off += fb;
     L.g = off; off += gb;
@@ -764,8 +785,13 @@ lbm_status enqueue_step(lbm_ctx* c, hipStream_t stream, bool last)
         s.g = (R*)ga;
         s.f2 = (R*)fb;
         s.g2 = (R*)gb;
-        LBM_HIP(c, (launch_ab_collide<L, R>(s, c->thermal, c->lds[0], stream)), "A-B collide kernel");
-        LBM_HIP(c, (launch_ab_pull<L, R>(s, c->thermal, c->lds[1], stream)), "A-B pull kernel");
+        if (c->push) {
+            // one pass: collide, push and the boundary rules (links are always in the kernel)
+            LBM_HIP(c, (launch_ab_push<L, R>(s, c->thermal, c->lds[parity], stream)), "A-B push kernel");
+        } else {
+            LBM_HIP(c, (launch_ab_collide<L, R>(s, c->thermal, c->lds[0], stream)), "A-B collide kernel");
+            LBM_HIP(c, (launch_ab_pull<L, R>(s, c->thermal, c->lds[1], stream)), "A-B pull kernel");
+        }
         la = link_args<R>(c, LINK_AB, fa, fb, ga, gb);
         if (passes) {
             // sources in one buffer, destinations in the other: one pass
@@ -912,7 +938,8 @@ lbm_status lbm_create(const lbm_params* p, const uint8_t* solid_labels, void* de
         c->p = *p;
         c->es = p->dtype;
         c->thermal = p->thermal != 0;
-        c->ab = p->streaming == LBM_STREAM_AB;
+        c->ab = p->streaming == LBM_STREAM_AB || p->streaming == LBM_STREAM_AB_PUSH;
+        c->push = p->streaming == LBM_STREAM_AB_PUSH;
         c->two_d = p->lattice == LBM_LATTICE_2D;
         c->stream = (hipStream_t)hip_stream;
         const bool solids = any_solid(p, solid_labels);
@@ -976,7 +1003,8 @@ lbm_status lbm_create(const lbm_params* p, const uint8_t* solid_labels, void* de
                 lds_cu = 0;
             const int rules = boundary_rules(make_bounce<float>(p, c->in_kernel, nullptr));
             for (int k = 0; k < 2; ++k) {
-                const int blocks = p->occupancy[k] ? p->occupancy[k] : automatic_occupancy(p, c->ab, rules, k);
+                const int blocks =
+                    p->occupancy[k] ? p->occupancy[k] : automatic_occupancy(p, c->ab, c->push, rules, k);
                 c->lds[k] = occupancy_lds(blocks, lds_cu);
             }
         }

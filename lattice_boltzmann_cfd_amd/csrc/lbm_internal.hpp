@@ -180,6 +180,8 @@ template <class L, typename R>
 hipError_t launch_ab_collide(const StepArgs<R>& a, bool thermal, size_t lds, hipStream_t s);
 template <class L, typename R>
 hipError_t launch_ab_pull(const StepArgs<R>& a, bool thermal, size_t lds, hipStream_t s);
+template <class L, typename R>
+hipError_t launch_ab_push(const StepArgs<R>& a, bool thermal, size_t lds, hipStream_t s);
 template <typename R> hipError_t launch_link_gather(const LinkArgs<R>& a, hipStream_t s);
 template <typename R> hipError_t launch_link_scatter(const LinkArgs<R>& a, hipStream_t s);
 template <typename R> hipError_t launch_link_direct(const LinkArgs<R>& a, hipStream_t s);

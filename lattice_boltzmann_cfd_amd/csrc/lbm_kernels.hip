@@ -548,6 +548,68 @@ __global__ void __launch_bounds__(BLOCK) k_ab_pull(StepArgs<R> a)
     }
 }
 
+// Two buffers in one pass: every cell loads its populations from A where
+// they sit at time t (its own slots), collides, and pushes f_q^+ to
+// B(q, x + c_q).  A blocked direction (a face or a solid cell at x + c_q) is
+// stored by the link's rule where the cell itself reads it next, exactly as
+// the in-place odd step stores it (blocked_outflow); a solid cell leaves out
+// the slots that a fluid neighbour fills that way (its mask bits), and no
+// cell stores across a no-slip face.  B then holds every population at time
+// t + 1 in its own slot, as after a pull.
+template <class L, typename R, bool TH, int BND>
+__global__ void __launch_bounds__(BLOCK) k_ab_push(StepArgs<R> a)
+{
+    const Geometry& G = a.geo;
+    const int32_t cell = (int32_t)(blockIdx.x * BLOCK + threadIdx.x);
+    if (cell >= G.ncell) return;
+    R* __restrict__ fb = a.f2;
+    R* __restrict__ gb = a.g2;
+    R h[L::Q];
+    R g[L::QT];
+#pragma unroll
+    for (int q = 0; q < L::Q; ++q) h[q] = ld(a.f, posf(G, q, cell));
+    if (TH) {
+#pragma unroll
+        for (int k = 0; k < L::QT; ++k) g[k] = ld(a.g, posg(G, k, cell));
+    }
+    const Nbr<L::DIMS> nb(G, cell);
+    Blocked b{0u, 0u, 0u, false};
+    if (BND) b = blocked_dirs<L>(a.bb, a.mask, cell, nb.faces);
+    const uint32_t blk = b.wall | b.solid;           // a fluid cell's blocked directions
+    const uint32_t skip = b.wall | b.claim;          // usual stores to leave out
+    const bool near = BND && !b.is_solid && blk != 0;
+    FaceRules fr{};
+    if (BND == 2 && near) fr = face_rules<L>(a.bb, nb.faces);
+    R ux = R(0), uy = R(0), uz = R(0);
+    if (BND == 2 && fr.pres) {
+        const Macro<R> m = macros<R, TH>(h, g, a.col);
+        ux = m.ux;
+        uy = m.uy;
+        uz = m.uz;
+        keep_face_velocity(a.bb, G, nb, ux, uy, uz);
+    }
+    collide<R, TH>(h, g, a.col);
+#pragma unroll
+    for (int q = 0; q < L::Q; ++q)
+        if (!BND || !((skip >> q) & 1u)) st(fb, posf(G, q, cell + nb.at(L::cx(q), L::cy(q), L::cz(q))), h[q]);
+    if (TH) {
+#pragma unroll
+        for (int k = 0; k < L::QT; ++k)
+            if (!BND || !((skip >> k) & 1u))
+                st(gb, posg(G, k, cell + nb.at(L::cxT(k), L::cyT(k), L::czT(k))), g[k]);
+    }
+    if (near) {
+#pragma unroll
+        for (int p = 1; p < L::Q; ++p)
+            if ((blk >> p) & 1u) blocked_outflow<L, R, BND>(fb, G, cell, nb, fr, a.bb, p, h[p], ux, uy, uz);
+        if (TH) {
+#pragma unroll
+            for (int k = 1; k < L::QT; ++k)
+                if ((blk >> k) & 1u) st(gb, posg(G, opp(k), cell), bounce7(a.bb, b, k, g[k]));
+        }
+    }
+}
+
 // ------------------------------------------------------------ links
 
 __device__ __forceinline__ double wave_sum(double v)
@@ -1011,6 +1073,12 @@ hipError_t launch_ab_pull(const StepArgs<R>& a, bool thermal, size_t lds, hipStr
     LBM_CELL_LAUNCH(k_ab_pull, a, thermal, lds, s);
 }
 
+template <class L, typename R>
+hipError_t launch_ab_push(const StepArgs<R>& a, bool thermal, size_t lds, hipStream_t s)
+{
+    LBM_CELL_LAUNCH(k_ab_push, a, thermal, lds, s);
+}
+
 template <typename R>
 hipError_t launch_link_gather(const LinkArgs<R>& a, hipStream_t s)
 {
@@ -1080,6 +1148,7 @@ hipError_t launch_zero_f64(double* p, int64_t n, hipStream_t s)
     template hipError_t launch_aa_step<L, R>(const StepArgs<R>&, bool, size_t, hipStream_t);    \
     template hipError_t launch_ab_collide<L, R>(const StepArgs<R>&, bool, size_t, hipStream_t); \
     template hipError_t launch_ab_pull<L, R>(const StepArgs<R>&, bool, size_t, hipStream_t);    \
+    template hipError_t launch_ab_push<L, R>(const StepArgs<R>&, bool, size_t, hipStream_t);    \
     template hipError_t launch_link_force<L, R>(const LinkArgs<R>&, hipStream_t);          \
     template hipError_t launch_init<L, R>(const FieldArgs<R>&, bool, hipStream_t);         \
     template hipError_t launch_read<L, R>(const FieldArgs<R>&, bool, hipStream_t);         \

@@ -105,6 +105,20 @@ def test_bad_dtype_and_streaming(lib):
     assert e.value.status == binding.LBM_E_INVALID
 
 
+def test_push_streaming_needs_links_in_the_kernel(lib):
+    """The one-pass two-buffer mode needs the two-pass mode's buffers and
+    applies the boundary rules itself: link passes are rejected with it."""
+    p = periodic(8, face_kind=[0, 0, 1, 1, 0, 0])
+    push = binding.lbm_required_bytes(p, streaming=binding.LBM_STREAM_AB_PUSH)
+    assert push == binding.lbm_required_bytes(p, streaming=binding.LBM_STREAM_AB) > 0
+    q = dict(p, links=binding.LBM_LINKS_PASSES)
+    assert binding.lbm_required_bytes(q, streaming=binding.LBM_STREAM_AB) > 0
+    assert binding.lbm_required_bytes(q, streaming=binding.LBM_STREAM_AB_PUSH) == 0
+    with pytest.raises(binding.LbmError) as e:
+        binding.lbm_create(q, None, 256, 1 << 30, streaming=binding.LBM_STREAM_AB_PUSH)
+    assert e.value.status == binding.LBM_E_INVALID
+
+
 def test_too_small_buffer_is_nomem(lib):
     p = periodic()
     need = binding.lbm_required_bytes(p)

@@ -100,10 +100,11 @@ def test_2d_two_buffer_equals_in_place_bitwise(case, dtype):
     w = CASES[case]()
     for steps in (1, 2, 7, 12):
         a = gpu_run(w, [steps], dtype=dtype, streaming=binding.LBM_STREAM_AA)
-        b = gpu_run(w, [steps], dtype=dtype, streaming=binding.LBM_STREAM_AB)
-        for k in ("rho", "u", "T"):
-            assert np.array_equal(a[k], b[k], equal_nan=True), (case, steps, k)
-        check_forces(b["forces"][-1], a["forces"][-1], dtype, n_links(a), f"{case} A-B vs AA")
+        for streaming in (binding.LBM_STREAM_AB, binding.LBM_STREAM_AB_PUSH):
+            b = gpu_run(w, [steps], dtype=dtype, streaming=streaming)
+            for k in ("rho", "u", "T"):
+                assert np.array_equal(a[k], b[k], equal_nan=True), (case, steps, streaming, k)
+            check_forces(b["forces"][-1], a["forces"][-1], dtype, n_links(a), f"{case} streaming {streaming} vs AA")
 
 
 @pytest.mark.parametrize("dtype", [4, 8])

@@ -76,7 +76,8 @@ def test_degenerate_box_layouts_and_launches_bitwise(name):
     w = workload(name)
     ref = gpu_run(w, [7, 24])
     fl = fluid_mask(w)
-    variants = [("two buffers", {}, binding.LBM_STREAM_AB), ("tiles of 64 cells", {"tile_log2": 6}, None),
+    variants = [("two buffers", {}, binding.LBM_STREAM_AB), ("two buffers in one pass", {}, binding.LBM_STREAM_AB_PUSH),
+                ("tiles of 64 cells", {"tile_log2": 6}, None),
                 ("occupancy 1/2", {"occupancy": [1, 2]}, None)]
     if name not in OPEN_FACES:
         variants.append(("link passes", {"links": binding.LBM_LINKS_PASSES}, None))

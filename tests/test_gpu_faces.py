@@ -74,18 +74,19 @@ def test_face_rules_parity(case, steps, dtype):
 
 @pytest.mark.parametrize("case", ["mixed", "channel_thermal", "slip_channel"])
 def test_face_rules_two_buffer_equals_in_place_bitwise(case):
-    say(f"CASE faces AA vs A-B {case}")
+    say(f"CASE faces AA vs both two-buffer modes {case}")
     w = CASES[case]()
     for steps in (1, 2, 7, 12):
         a = gpu_run(w, [steps], streaming=binding.LBM_STREAM_AA)
-        b = gpu_run(w, [steps], streaming=binding.LBM_STREAM_AB)
-        for k in ("rho", "u", "T"):
-            if a[k] is not None:
-                assert np.array_equal(a[k], b[k], equal_nan=True), (case, steps, k)
-        # forces: a VELOCITY link's leaving value is rebuilt from the stored
-        # returning one in one layout and read directly in the other, so the
-        # sums agree to rounding, not bit for bit
-        check_forces(b["forces"][-1], a["forces"][-1], 4, n_links(a), f"{case} A-B vs AA")
+        for streaming in (binding.LBM_STREAM_AB, binding.LBM_STREAM_AB_PUSH):
+            b = gpu_run(w, [steps], streaming=streaming)
+            for k in ("rho", "u", "T"):
+                if a[k] is not None:
+                    assert np.array_equal(a[k], b[k], equal_nan=True), (case, steps, streaming, k)
+            # forces: a VELOCITY link's leaving value is rebuilt from the stored
+            # returning one in one layout and read directly in the other, so the
+            # sums agree to rounding, not bit for bit
+            check_forces(b["forces"][-1], a["forces"][-1], 4, n_links(a), f"{case} streaming {streaming} vs AA")
 
 
 def test_face_rules_split_submissions_and_replays():

@@ -73,11 +73,12 @@ def test_sol256_conservation_100_steps(sol256):
 
 
 def test_sol128_in_place_equals_two_buffer_bitwise():
-    say("CASE sol128 full size, AA vs A-B, 100 steps")
+    say("CASE sol128 full size, AA vs both two-buffer modes, 100 steps")
     w = inputs.make("sol128")
     a = gpu_run(w, [100], streaming=binding.LBM_STREAM_AA, want_forces=False)
-    b = gpu_run(w, [100], streaming=binding.LBM_STREAM_AB, want_forces=False)
-    assert np.array_equal(a["rho"], b["rho"]) and np.array_equal(a["u"], b["u"])
+    for streaming in (binding.LBM_STREAM_AB, binding.LBM_STREAM_AB_PUSH):
+        b = gpu_run(w, [100], streaming=streaming, want_forces=False)
+        assert np.array_equal(a["rho"], b["rho"]) and np.array_equal(a["u"], b["u"]), streaming
 
 
 def test_sphere128_windows_and_momentum_budget():
@@ -184,5 +185,6 @@ def test_sol128_in_place_equals_two_buffer_bitwise_fp64():
     say("CASE sol128 full size fp64, AA vs A-B, 100 steps")
     w = inputs.make("sol128")
     a = gpu_run(w, [100], dtype=8, streaming=binding.LBM_STREAM_AA, want_forces=False)
-    b = gpu_run(w, [100], dtype=8, streaming=binding.LBM_STREAM_AB, want_forces=False)
-    assert np.array_equal(a["rho"], b["rho"]) and np.array_equal(a["u"], b["u"])
+    for streaming in (binding.LBM_STREAM_AB, binding.LBM_STREAM_AB_PUSH):
+        b = gpu_run(w, [100], dtype=8, streaming=streaming, want_forces=False)
+        assert np.array_equal(a["rho"], b["rho"]) and np.array_equal(a["u"], b["u"]), streaming

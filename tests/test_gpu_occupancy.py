@@ -33,12 +33,13 @@ def test_bounded_occupancy_equals_unbounded_bitwise(case, dtype, occ):
         assert np.allclose(f_got, f_ref, rtol=1e-9 if dtype == 8 else 1e-5, atol=1e-12)
 
 
+@pytest.mark.parametrize("streaming", [binding.LBM_STREAM_AB, binding.LBM_STREAM_AB_PUSH])
 @pytest.mark.parametrize("case", ["spheres", "disks2d"])
-def test_bounded_occupancy_two_buffers(case):
-    say(f"CASE occupancy two buffers {case}")
+def test_bounded_occupancy_two_buffers(case, streaming):
+    say(f"CASE occupancy two buffers {case} streaming={streaming}")
     w = CASES[case]()
     w.params["occupancy"] = [-1, -1]
-    ref = gpu_run(w, [7, 93], streaming=binding.LBM_STREAM_AB)
+    ref = gpu_run(w, [7, 93], streaming=streaming)
     w.params["occupancy"] = [2, 1]
-    got = gpu_run(w, [7, 93], streaming=binding.LBM_STREAM_AB)
-    same_fields(got, ref, w, f"{case} two buffers")
+    got = gpu_run(w, [7, 93], streaming=streaming)
+    same_fields(got, ref, w, f"{case} two buffers, streaming {streaming}")

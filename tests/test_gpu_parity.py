@@ -113,30 +113,34 @@ def test_dirichlet_spheres(dtype):
     check_forces(g["forces"][-1], o["diag"][-1], dtype, g["links19"] + g["links7"], "dirichlet-spheres")
 
 
+@pytest.mark.parametrize("streaming", [binding.LBM_STREAM_AB, binding.LBM_STREAM_AB_PUSH])
 @pytest.mark.parametrize("dtype", [4, 8])
-def test_two_buffer_matches_in_place_bitwise(dtype):
-    say(f"CASE AA vs A-B dtype={dtype}")
+def test_two_buffer_matches_in_place_bitwise(dtype, streaming):
+    say(f"CASE AA vs A-B dtype={dtype} streaming={streaming}")
     w = dirichlet_spheres_case()
     for steps in (1, 2, 7, 12):
         a = gpu_run(w, [steps], dtype=dtype, streaming=binding.LBM_STREAM_AA)
-        b = gpu_run(w, [steps], dtype=dtype, streaming=binding.LBM_STREAM_AB)
+        b = gpu_run(w, [steps], dtype=dtype, streaming=streaming)
         fl = fluid_mask(w)
         for k in ("rho", "u", "T"):
             x, y = a[k][..., fl], b[k][..., fl]
             assert np.array_equal(x, y), f"{k} differs after {steps} steps: {np.abs(x - y).max():.3e}"
+        # the same bounced values, read from each layout's slots and summed in another order
+        assert np.allclose(a["forces"][-1], b["forces"][-1], rtol=1e-9 if dtype == 8 else 1e-5, atol=1e-12)
 
 
+@pytest.mark.parametrize("streaming", [binding.LBM_STREAM_AB, binding.LBM_STREAM_AB_PUSH])
 @pytest.mark.parametrize("dtype", [4, 8])
-def test_two_buffer_parity(dtype):
-    say(f"CASE A-B vs oracle dtype={dtype}")
+def test_two_buffer_parity(dtype, streaming):
+    say(f"CASE A-B vs oracle dtype={dtype} streaming={streaming}")
     w = inputs.cavity256(shape=(30, 26, 22))
-    g = gpu_run(w, [100], dtype=dtype, streaming=binding.LBM_STREAM_AB)
+    g = gpu_run(w, [100], dtype=dtype, streaming=streaming)
     o = oracle_run(w, 100, want_diag=True)
     check_fields(g, o, w, dtype, "ab-cavity")
     check_forces(g["forces"][-1], o["diag"][-1], dtype, g["links19"] + g["links7"], "ab-cavity")
 
 
-@pytest.mark.parametrize("streaming", [binding.LBM_STREAM_AA, binding.LBM_STREAM_AB])
+@pytest.mark.parametrize("streaming", [binding.LBM_STREAM_AA, binding.LBM_STREAM_AB, binding.LBM_STREAM_AB_PUSH])
 def test_submissions_split_bitwise(streaming):
     say(f"CASE submissions split streaming={streaming}")
     w = dirichlet_spheres_case()
@@ -226,8 +230,11 @@ def test_in_kernel_equals_link_passes_bitwise(dtype, streaming):
             assert np.allclose(a["forces"][-1], b["forces"][-1], rtol=1e-6, atol=1e-9)
 
 
-@pytest.mark.parametrize("links", [binding.LBM_LINKS_IN_KERNEL, binding.LBM_LINKS_PASSES])
-@pytest.mark.parametrize("streaming", [binding.LBM_STREAM_AA, binding.LBM_STREAM_AB])
+@pytest.mark.parametrize("streaming,links", [(binding.LBM_STREAM_AA, binding.LBM_LINKS_IN_KERNEL),
+                                             (binding.LBM_STREAM_AA, binding.LBM_LINKS_PASSES),
+                                             (binding.LBM_STREAM_AB, binding.LBM_LINKS_IN_KERNEL),
+                                             (binding.LBM_STREAM_AB, binding.LBM_LINKS_PASSES),
+                                             (binding.LBM_STREAM_AB_PUSH, binding.LBM_LINKS_IN_KERNEL)])
 def test_graph_replays_match_eager_steps(streaming, links):
     """Submissions of >= 6 steps replay a captured even+odd graph; every
     replayed state must equal one-step-at-a-time launches bit for bit, with

@@ -67,7 +67,8 @@ def test_tiled_equals_untiled_bitwise(case, tile, dtype):
 
 @pytest.mark.parametrize("streaming,links", [(binding.LBM_STREAM_AB, binding.LBM_LINKS_IN_KERNEL),
                                              (binding.LBM_STREAM_AA, binding.LBM_LINKS_PASSES),
-                                             (binding.LBM_STREAM_AB, binding.LBM_LINKS_PASSES)])
+                                             (binding.LBM_STREAM_AB, binding.LBM_LINKS_PASSES),
+                                             (binding.LBM_STREAM_AB_PUSH, binding.LBM_LINKS_IN_KERNEL)])
 @pytest.mark.parametrize("case", ["spheres", "cavity", "disks2d"])
 def test_tiled_two_buffer_and_link_passes(case, streaming, links):
     say(f"CASE tiles {case} streaming={streaming} links={links}")
