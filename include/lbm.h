@@ -207,7 +207,7 @@ size_t lbm_required_bytes(const lbm_params* p, const uint8_t* solid_labels);
  * or a solid cell), carve device_buf and upload the links.
  * device_buf: device memory of device_bytes bytes, BORROWED: the caller owns
  * it and keeps it alive until lbm_destroy(); the populations live in it, so
- * saving its bytes and lbm_time() checkpoints the state.
+ * saving its bytes and lbm_time() checkpoints the state (lbm_resume).
  * hip_stream: a hipStream_t (NULL = the null stream), BORROWED.
  * Host arrays are copied before the call returns.  On failure nothing is kept
  * and *out is NULL.  Errors: LBM_E_INVALID (bad sizes, a rate outside [0, 2),
@@ -288,6 +288,16 @@ lbm_status lbm_diagnostics(lbm_ctx* ctx, double* out, int32_t n);
 
 /* Current time step count (number of steps since lbm_init_fields). */
 int64_t lbm_time(const lbm_ctx* ctx);
+
+/* Continue from a checkpoint.  A checkpoint is the device_bytes bytes of a
+ * context's buffer, copied after its stream has finished a call, with that
+ * context's lbm_time() t.  To resume: create a context with the same
+ * parameters, labels, dtype and streaming mode, copy the saved bytes into its
+ * buffer (on or ordered before its stream), then call lbm_resume(ctx, t) in
+ * place of lbm_init_fields; the next lbm_step continues at step t exactly as
+ * the saved context would have.  No device work.  Errors: LBM_E_INVALID for a
+ * NULL context or t < 0. */
+lbm_status lbm_resume(lbm_ctx* ctx, int64_t t);
 
 /* Number of links of the flow lattice's list (lattice = 19 for D3Q19 or 9
  * for D2Q9) or of the temperature lattice's (7 for D3Q7, 5 for D2Q5); -1

@@ -31,7 +31,8 @@ MAX_GROUPS = 261
 # every function the header declares
 ABI_FUNCTIONS = (
     "lbm_required_bytes", "lbm_create", "lbm_init_fields", "lbm_step", "lbm_read_macros",
-    "lbm_wall_force", "lbm_diagnostics", "lbm_time", "lbm_num_links", "lbm_count_links", "lbm_last_error", "lbm_destroy",
+    "lbm_wall_force", "lbm_diagnostics", "lbm_time", "lbm_resume", "lbm_num_links", "lbm_count_links", "lbm_last_error",
+    "lbm_destroy",
 )
 
 
@@ -90,6 +91,8 @@ def library():
         lib.lbm_diagnostics.restype = ctypes.c_int
         lib.lbm_time.argtypes = [vp]
         lib.lbm_time.restype = ctypes.c_int64
+        lib.lbm_resume.argtypes = [vp, ctypes.c_int64]
+        lib.lbm_resume.restype = ctypes.c_int
         lib.lbm_num_links.argtypes = [vp, ctypes.c_int32]
         lib.lbm_num_links.restype = ctypes.c_int64
         lib.lbm_count_links.argtypes = [P, ctypes.POINTER(ctypes.c_uint8), ctypes.c_int32]
@@ -206,6 +209,10 @@ def lbm_time(ctx) -> int:
     return int(library().lbm_time(ctypes.c_void_p(ctx)))
 
 
+def lbm_resume(ctx, t: int):
+    _check(ctx, library().lbm_resume(ctypes.c_void_p(ctx), int(t)))
+
+
 def lbm_num_links(ctx, lattice: int) -> int:
     return int(library().lbm_num_links(ctypes.c_void_p(ctx), int(lattice)))
 
@@ -293,6 +300,24 @@ class Solver:
 
     def num_links(self, lattice: int) -> int:
         return lbm_num_links(self.ctx, lattice)
+
+    def checkpoint(self):
+        """A checkpoint: a copy of the buffer's bytes (device tensor), taken on
+        the solver's stream after the work queued so far, and the time."""
+        with self.torch.cuda.stream(self.stream):
+            saved = self.buf.clone()
+        self.stream.synchronize()
+        return saved, self.time
+
+    def resume(self, saved, t: int):
+        """Continue from a checkpoint of a solver with the same parameters,
+        labels, dtype and streaming mode (in place of init)."""
+        if saved.numel() != self.buf.numel():
+            raise LbmError(LBM_E_INVALID, "checkpoint size differs from this solver's buffer")
+        with self.torch.cuda.stream(self.stream):
+            self.buf.copy_(saved, non_blocking=True)
+            self._keep = saved  # read by the copy on the stream
+        lbm_resume(self.ctx, t)
 
     def close(self):
         if self.ctx:

@@ -1186,6 +1186,19 @@ lbm_status lbm_diagnostics(lbm_ctx* c, double* out, int32_t n)
 
 int64_t lbm_time(const lbm_ctx* c) { return c ? c->t : -1; }
 
+lbm_status lbm_resume(lbm_ctx* c, int64_t t)
+{
+    if (!c) return LBM_E_INVALID;
+    if (t < 0) {
+        c->err = "t must be >= 0";
+        return LBM_E_INVALID;
+    }
+    // the buffer holds the state at time t in the layout of parity t & 1
+    c->t = t;
+    c->initialised = true;
+    return LBM_OK;
+}
+
 int64_t lbm_count_links(const lbm_params* p, const uint8_t* solid_labels, int32_t lattice)
 {
     try {

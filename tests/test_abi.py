@@ -135,6 +135,7 @@ def test_null_context_calls_are_invalid(lib):
     assert lib.lbm_wall_force(None, out, 4) == binding.LBM_E_INVALID
     assert lib.lbm_diagnostics(None, out, binding.LBM_DIAG_COUNT) == binding.LBM_E_INVALID
     assert lib.lbm_time(None) == -1
+    assert lib.lbm_resume(None, 5) == binding.LBM_E_INVALID
     assert lib.lbm_num_links(None, 19) == -1
 
 

@@ -1,0 +1,65 @@
+"""Checkpoint and resume through the C ABI (lbm_resume).
+
+A run saved after some steps (the buffer's bytes and lbm_time), restored into
+a new context with the same parameters and continued must give the state of
+the uninterrupted run bit for bit: fields and the force and heat sums of the
+last step.  Saves at odd and even times (the in-place layout depends on the
+parity), in all three streaming modes, with walls, Dirichlet solids, open
+faces and the 2D lattice; one checkpoint goes through host memory."""
+import numpy as np
+import pytest
+
+from harness import say
+from lattice_boltzmann_cfd_amd import binding
+from test_gpu_2d import disks as disks2d
+from test_gpu_faces import mixed_box
+from test_gpu_parity import dirichlet_spheres_case
+
+pytestmark = pytest.mark.gpu
+
+CASES = {"spheres": dirichlet_spheres_case, "mixed_faces": mixed_box, "disks2d": disks2d}
+
+
+def fields(s):
+    import torch
+
+    rho, u, T = s.macros()
+    torch.cuda.synchronize()
+    out = [rho.cpu().numpy(), u.cpu().numpy()]
+    if T is not None:
+        out.append(T.cpu().numpy())
+    return out
+
+
+@pytest.mark.parametrize("save_at", [37, 40])
+@pytest.mark.parametrize("streaming", [binding.LBM_STREAM_AA, binding.LBM_STREAM_AB, binding.LBM_STREAM_AB_PUSH])
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_resume_equals_uninterrupted_run(case, streaming, save_at):
+    say(f"CASE checkpoint {case} streaming={streaming} save at {save_at}")
+    w = CASES[case]()
+    total = 100
+    a = binding.Solver(w.params, w.labels, streaming=streaming)
+    b = binding.Solver(w.params, w.labels, streaming=streaming)
+    try:
+        a.init(w.rho, w.u, w.T if w.params.get("thermal") else None)
+        a.step(save_at)
+        saved, t = a.checkpoint()
+        if case == "spheres" and streaming == binding.LBM_STREAM_AA:
+            saved = saved.cpu().cuda()  # through host memory, as a file would
+        a.step(total - save_at)
+        ref_f = a.wall_force()
+        ref = fields(a)
+        assert t == save_at
+        b.resume(saved, t)
+        assert b.time == save_at
+        b.step(total - save_at)
+        got_f = b.wall_force()
+        got = fields(b)
+        assert b.time == a.time == total
+        for x, y in zip(got, ref):
+            assert np.array_equal(x, y, equal_nan=True)
+        # the same link sums, accumulated by atomics in no fixed order
+        assert np.allclose(got_f, ref_f, rtol=1e-5, atol=1e-12)
+    finally:
+        a.close()
+        b.close()
