@@ -336,3 +336,15 @@ def test_solid_link_destinations_are_never_link_sources(name):
             wall_dst = {link_dst(lk, opp, odd) for lk in links if lk[3] < 6}
             if name == "walls_solids":
                 assert wall_dst & sources
+
+
+@pytest.mark.parametrize("name", ["walls_solids", "cavity_thermal", "rb_spheres", "dirichlet_solid"] + DEGENERATE)
+def test_link_destinations_are_unique(name):
+    """No two links write the same slot, in either parity and on either
+    lattice: the link passes may then scatter in any order."""
+    p, lab, rho, u, T = case(name)
+    for cset, opp in ((C19, OPP19), (C7, OPP7)):
+        links = build_links(p, lab, cset)
+        for odd in (0, 1):
+            dst = [link_dst(lk, opp, odd) for lk in links]
+            assert len(dst) == len(set(dst)), (name, odd, len(dst) - len(set(dst)))

@@ -159,6 +159,18 @@ def test_submissions_split_bitwise(streaming):
     check_forces(three["forces"][1], o["diag"][50], 4, three["links19"] + three["links7"], "after 51")
 
 
+@pytest.mark.parametrize("streaming", [binding.LBM_STREAM_AA, binding.LBM_STREAM_AB, binding.LBM_STREAM_AB_PUSH])
+def test_repeatable_bitwise(streaming):
+    """The same run twice gives the same fields bit for bit: no cell's result
+    depends on the order in which blocks run (a race would show here)."""
+    say(f"CASE repeatability streaming={streaming}")
+    w = dirichlet_spheres_case()
+    a = gpu_run(w, [7, 93], streaming=streaming)
+    b = gpu_run(w, [7, 93], streaming=streaming)
+    for k in ("rho", "u", "T"):
+        assert np.array_equal(a[k], b[k], equal_nan=True), k
+
+
 @pytest.mark.parametrize("dtype", [4, 8])
 def test_rest_state_stays_at_rest(dtype):
     say(f"CASE rest dtype={dtype}")
