@@ -152,7 +152,7 @@ def main(argv=None):
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+        print(f"bench.py: the library runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
               "the multi-GPU slab decomposition is a design, not code", file=sys.stderr)
         return 2
 
