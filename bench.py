@@ -145,7 +145,8 @@ def main(argv=None):
     ap.add_argument("--dtype", type=int, default=4, choices=(4, 8))
     ap.add_argument("--streaming", type=int, default=1, choices=(1, 2, 3),
                     help="1 in place (AA), 2 two buffers in two passes, 3 two buffers in one pass")
-    ap.add_argument("--cpu-steps", type=int, default=6, help="oracle steps for the CPU baseline (0: skip)")
+    ap.add_argument("--cpu-steps", type=int, default=16,
+                    help="oracle steps for the CPU baseline, about 15 s on 16 host threads at 256^3 (0: skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run torch's device copy of 1 GiB 10 times (reference kernel for HBM counters)")
     args = ap.parse_args(argv)
