@@ -188,3 +188,17 @@ def test_sol128_in_place_equals_two_buffer_bitwise_fp64():
     for streaming in (binding.LBM_STREAM_AB, binding.LBM_STREAM_AB_PUSH):
         b = gpu_run(w, [100], dtype=8, streaming=streaming, want_forces=False)
         assert np.array_equal(a["rho"], b["rho"]) and np.array_equal(a["u"], b["u"]), streaming
+
+
+@pytest.mark.parametrize("name,dtype,steps", [("sol256", 4, 41), ("cavity256", 4, 41), ("cavity2d", 8, 21)])
+def test_push_equals_in_place_at_full_size(name, dtype, steps, sol256, cavity256):
+    """The one-pass two-buffer step against the in-place step, bit for bit, at
+    the workloads' full sizes with each mode's automatic layout and occupancy
+    bounds (an odd step count ends on the in-place odd step)."""
+    say(f"CASE {name} full size dtype={dtype}: AA vs one-pass two buffers, {steps} steps")
+    w = {"sol256": sol256, "cavity256": cavity256}.get(name) or inputs.make(name)
+    a = gpu_run(w, [steps], dtype=dtype, streaming=binding.LBM_STREAM_AA, want_forces=False)
+    b = gpu_run(w, [steps], dtype=dtype, streaming=binding.LBM_STREAM_AB_PUSH, want_forces=False)
+    for k in ("rho", "u", "T"):
+        if a[k] is not None:
+            assert np.array_equal(a[k], b[k]), k
