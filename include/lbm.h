@@ -52,9 +52,10 @@
  *  - Momentum exchange on a wall link: the wall receives 2 c_p f_p^+; heat into
  *    the fluid through a Dirichlet link: w T_w - 2 g_p^+.
  *  - Walls sit half-way between the last fluid cell and the box face; a box
- *    face is either periodic or a no-slip wall, the same on both ends of an
- *    axis.  A link crossing two faces belongs to the first crossed axis in
- *    x, y, z order.
+ *    face is periodic or one of the half-way kinds listed under the face
+ *    kinds below, and an axis is periodic on both faces or on neither.  A
+ *    link crossing two faces belongs to the first crossed axis in x, y, z
+ *    order.
  */
 #ifndef LBM_H
 #define LBM_H
@@ -174,7 +175,7 @@ typedef struct lbm_params {
     int32_t face_thermal[6]; /* LBM_ADIABATIC or LBM_DIRICHLET (wall faces) */
     double face_T[6];        /* Dirichlet wall temperature per face */
     int32_t solid_thermal;   /* thermal rule of every solid cell */
-    int32_t links;           /* LBM_LINKS_IN_KERNEL (0) or LBM_LINKS_PASSES (1), see below */
+    int32_t links;           /* LBM_LINKS_IN_KERNEL (0) or LBM_LINKS_PASSES (1), see above */
     double solid_T;          /* Dirichlet temperature of the solids */
     double s19[19];          /* D3Q19 relaxation rates, row order above, each in [0, 2) */
     double s7[7];            /* D3Q7 relaxation rates, row order above, each in [0, 2) */
@@ -184,13 +185,13 @@ typedef struct lbm_params {
     double T0;               /* reference temperature of the buoyancy term */
     double face_u[6][3];     /* wall velocity u_w of each VELOCITY face */
     double face_rho[6];      /* wall density rho_w of each VELOCITY and PRESSURE face, > 0 */
-    int32_t lattice;         /* LBM_LATTICE_3D (0) or LBM_LATTICE_2D (1), see below */
+    int32_t lattice;         /* LBM_LATTICE_3D (0) or LBM_LATTICE_2D (1), see above */
     int32_t pad1;
-    double s9[9];            /* D2Q9 relaxation rates (LBM_LATTICE_2D), row order below, each in [0, 2) */
-    double s5[5];            /* D2Q5 relaxation rates (LBM_LATTICE_2D), row order below, each in [0, 2) */
-    int32_t tile_log2;       /* population layout, see below: 0 automatic, 6..20 tiles of 2^k cells, 31 none */
+    double s9[9];            /* D2Q9 relaxation rates (LBM_LATTICE_2D), row order above, each in [0, 2) */
+    double s5[5];            /* D2Q5 relaxation rates (LBM_LATTICE_2D), row order above, each in [0, 2) */
+    int32_t tile_log2;       /* population layout, see above: 0 automatic, 6..20 tiles of 2^k cells, 31 none */
     int32_t pad2;
-    int32_t occupancy[2];    /* resident blocks per compute unit, even / odd steps, see below: 0 automatic */
+    int32_t occupancy[2];    /* resident blocks per compute unit, even / odd steps, see above: 0 automatic */
 } lbm_params;
 
 typedef struct lbm_ctx lbm_ctx;
@@ -240,7 +241,8 @@ lbm_status lbm_step(lbm_ctx* ctx, int64_t n);
  * three planes, T (may be NULL; ignored unless thermal).  Device pointers in
  * the context's dtype, written by a kernel on the stream.  Solid cells get
  * NaN.  If a fluid cell's rho or T is not finite, a sticky LBM_E_UNSTABLE is
- * recorded and returned by the next lbm_wall_force().  Asynchronous. */
+ * recorded and returned by the next lbm_wall_force() or lbm_diagnostics().
+ * Asynchronous. */
 lbm_status lbm_read_macros(lbm_ctx* ctx, void* rho, void* u, void* T);
 
 /* Copy the latched per-group sums of the last step of the last submission to
