@@ -147,6 +147,9 @@ def main(argv=None):
                     help="1 in place (AA), 2 two buffers in two passes, 3 two buffers in one pass")
     ap.add_argument("--cpu-steps", type=int, default=16,
                     help="oracle steps for the CPU baseline, about 15 s on 16 host threads at 256^3 (0: skip)")
+    ap.add_argument("--profile-steps", type=int, default=0,
+                    help="after the timed region, this many more steps with per-kernel timing (lbm_profile); "
+                         "adds the mean milliseconds per launch of each kernel kind to the line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run torch's device copy of 1 GiB 10 times (reference kernel for HBM counters)")
     args = ap.parse_args(argv)
@@ -219,6 +222,12 @@ def main(argv=None):
                    "hbm_TBps_algorithmic": round(bpc * w.cells * args.steps / (ms / 1e3) / 1e12, 3)},
         "roofline": roofline,
     }
+    if args.profile_steps > 0:
+        # per-kernel breakdown, outside the timed region (each kernel launched on its own between events)
+        solver.profile(True)
+        solver.step(args.profile_steps)
+        line["kernel_ms"] = {k: round(ms / n, 5) for k, (ms, n) in solver.kernel_times().items()}
+        solver.profile(False)
     if w.labels is not None:
         # solid cells are updated too (on NaN); the throughput over fluid cells only
         fluid = int((w.labels == 0).sum())

@@ -5,7 +5,8 @@
  * Every call takes plain pointers and sizes; no C++ or framework types cross
  * this boundary.  All compute runs in the library's kernels on the caller's
  * HIP stream; calls are stream-ordered and asynchronous except
- * lbm_wall_force() and lbm_diagnostics(), which synchronise the stream.
+ * lbm_wall_force(), lbm_diagnostics() and lbm_profile_read(), which
+ * synchronise the stream (and lbm_step() while profiling, see lbm_profile()).
  *
  * What the library computes (the pages it follows):
  *  - "Multi-GPU thermal lattice Boltzmann simulations using OpenACC and MPI",
@@ -287,6 +288,37 @@ enum {
  * Synchronises the stream; returns LBM_E_UNSTABLE if a fluid value was not
  * finite (then the sums are not finite either). */
 lbm_status lbm_diagnostics(lbm_ctx* ctx, double* out, int32_t n);
+
+/* Kernel kinds of per-kernel timing (lbm_profile_read). */
+enum {
+    LBM_KERNEL_STEP_EVEN = 0,    /* the step kernel at even t: in place (AA) or one-pass two buffers (AB_PUSH) */
+    LBM_KERNEL_STEP_ODD = 1,     /* the same at odd t */
+    LBM_KERNEL_AB_COLLIDE = 2,   /* two buffers in two passes (AB): collide in place */
+    LBM_KERNEL_AB_PULL = 3,      /* ... then pull into the other buffer */
+    LBM_KERNEL_LINK_GATHER = 4,  /* link passes (LBM_LINKS_PASSES), in place: gather */
+    LBM_KERNEL_LINK_SCATTER = 5, /* ... then scatter */
+    LBM_KERNEL_LINK_DIRECT = 6,  /* link passes with two buffers: one pass */
+    LBM_KERNEL_FORCE = 7,        /* a submission's last step: clearing the sums and the force / heat pass */
+    LBM_KERNEL_KINDS = 8
+};
+
+/* Per-kernel timing, the profile mode of "GPU lattice Boltzmann: streaming
+ * layout and performance", which times each kernel with GPU timestamps and
+ * warns that throughput is then not representative.  on = 1: the sums start
+ * again at zero and, from the next lbm_step on, every kernel of a step is
+ * launched on its own (no graph replays) between two HIP events recorded on
+ * the stream; every 1024 timed launches lbm_step synchronises the stream to
+ * add them up.  on = 0: back to normal launches; the sums stay readable.
+ * Fields, forces and heat are the same bit for bit either way.  No device
+ * work.  Errors: LBM_E_INVALID for a NULL context or on not 0 or 1. */
+lbm_status lbm_profile(lbm_ctx* ctx, int32_t on);
+
+/* Milliseconds and launch counts per kernel kind (LBM_KERNEL_*) timed since
+ * profiling was last switched on: ms[k] and launches[k] for k < n (host
+ * arrays, either may be NULL; kinds from LBM_KERNEL_KINDS on read 0).
+ * Synchronises the stream.  Errors: LBM_E_INVALID (NULL context, n < 0),
+ * LBM_E_DEVICE. */
+lbm_status lbm_profile_read(lbm_ctx* ctx, double* ms, int64_t* launches, int32_t n);
 
 /* Current time step count (number of steps since lbm_init_fields). */
 int64_t lbm_time(const lbm_ctx* ctx);

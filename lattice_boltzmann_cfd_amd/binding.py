@@ -27,12 +27,16 @@ LBM_FACE_PERIODIC, LBM_FACE_WALL, LBM_FACE_SLIP, LBM_FACE_VELOCITY, LBM_FACE_PRE
 MAX_GROUPS = 261
 (LBM_DIAG_FLUID_CELLS, LBM_DIAG_MASS, LBM_DIAG_MOM_X, LBM_DIAG_MOM_Y, LBM_DIAG_MOM_Z, LBM_DIAG_KINETIC,
  LBM_DIAG_UMAX, LBM_DIAG_HEAT, LBM_DIAG_CONV_X, LBM_DIAG_CONV_Y, LBM_DIAG_CONV_Z, LBM_DIAG_COUNT) = range(12)
+(LBM_KERNEL_STEP_EVEN, LBM_KERNEL_STEP_ODD, LBM_KERNEL_AB_COLLIDE, LBM_KERNEL_AB_PULL, LBM_KERNEL_LINK_GATHER,
+ LBM_KERNEL_LINK_SCATTER, LBM_KERNEL_LINK_DIRECT, LBM_KERNEL_FORCE, LBM_KERNEL_KINDS) = range(9)
+KERNEL_NAMES = ("step_even", "step_odd", "ab_collide", "ab_pull", "link_gather", "link_scatter", "link_direct",
+                "force")
 
 # every function the header declares
 ABI_FUNCTIONS = (
     "lbm_required_bytes", "lbm_create", "lbm_init_fields", "lbm_step", "lbm_read_macros",
     "lbm_wall_force", "lbm_diagnostics", "lbm_time", "lbm_resume", "lbm_num_links", "lbm_count_links", "lbm_last_error",
-    "lbm_destroy",
+    "lbm_destroy", "lbm_profile", "lbm_profile_read",
 )
 
 
@@ -101,6 +105,11 @@ def library():
         lib.lbm_last_error.restype = ctypes.c_char_p
         lib.lbm_destroy.argtypes = [vp]
         lib.lbm_destroy.restype = None
+        lib.lbm_profile.argtypes = [vp, ctypes.c_int32]
+        lib.lbm_profile.restype = ctypes.c_int
+        lib.lbm_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64),
+                                         ctypes.c_int32]
+        lib.lbm_profile_read.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -233,6 +242,20 @@ def lbm_destroy(ctx):
         library().lbm_destroy(ctypes.c_void_p(ctx))
 
 
+def lbm_profile(ctx, on: bool):
+    _check(ctx, library().lbm_profile(ctypes.c_void_p(ctx), 1 if on else 0))
+
+
+def lbm_profile_read(ctx, n: int = LBM_KERNEL_KINDS):
+    """(milliseconds, launch counts) per kernel kind, numpy arrays of n."""
+    ms = np.zeros(n, np.float64)
+    launches = np.zeros(n, np.int64)
+    st = library().lbm_profile_read(ctypes.c_void_p(ctx), ms.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                                    launches.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), int(n))
+    _check(ctx, st)
+    return ms, launches
+
+
 class Solver:
     """A context plus the torch-allocated device buffer it borrows.
 
@@ -300,6 +323,16 @@ class Solver:
 
     def num_links(self, lattice: int) -> int:
         return lbm_num_links(self.ctx, lattice)
+
+    def profile(self, on: bool = True):
+        """Switch per-kernel timing on (sums restart at zero) or off."""
+        lbm_profile(self.ctx, on)
+
+    def kernel_times(self) -> dict:
+        """{kernel kind: (milliseconds, launches)} for the kinds launched since
+        profiling was switched on."""
+        ms, launches = lbm_profile_read(self.ctx)
+        return {KERNEL_NAMES[k]: (float(ms[k]), int(launches[k])) for k in range(LBM_KERNEL_KINDS) if launches[k]}
 
     def checkpoint(self):
         """A checkpoint: a copy of the buffer's bytes (device tensor), taken on

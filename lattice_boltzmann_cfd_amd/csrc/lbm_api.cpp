@@ -52,10 +52,26 @@ struct lbm_ctx {
     hipGraphExec_t pair = nullptr;
     int pair_steps = 0;  // steps per replay (an even number)
     bool pair_failed = false;
+    // per-kernel timing (lbm_profile): an event pair recorded around each
+    // launch on the caller's stream, added up at a synchronisation
+    struct Timed {
+        int kind;
+        hipEvent_t start, stop;
+    };
+    bool profile = false;
+    std::vector<Timed> timed;               // recorded, not yet added up
+    std::vector<hipEvent_t> spare_events;   // created, free for the next launch
+    double prof_ms[LBM_KERNEL_KINDS] = {};
+    int64_t prof_launches[LBM_KERNEL_KINDS] = {};
     ~lbm_ctx()
     {
         if (pair) (void)hipGraphExecDestroy(pair);
         if (capture_stream) (void)hipStreamDestroy(capture_stream);
+        for (const Timed& t : timed) {
+            (void)hipEventDestroy(t.start);
+            (void)hipEventDestroy(t.stop);
+        }
+        for (hipEvent_t e : spare_events) (void)hipEventDestroy(e);
     }
     std::string err;
     Collision<float> colf{};
@@ -717,6 +733,65 @@ lbm_status device_error(lbm_ctx* ctx, hipError_t e, const char* what)
         if (e_ != hipSuccess) return device_error(ctx, e_, what); \
     } while (0)
 
+// ------------------------------------------------------- kernel timing
+
+hipError_t take_event(lbm_ctx* c, hipEvent_t* ev)
+{
+    if (!c->spare_events.empty()) {
+        *ev = c->spare_events.back();
+        c->spare_events.pop_back();
+        return hipSuccess;
+    }
+    return hipEventCreate(ev);
+}
+
+// Record the start of a timed launch of `kind` on `stream`.
+hipError_t timed_begin(lbm_ctx* c, hipStream_t stream, int kind)
+{
+    lbm_ctx::Timed t{kind, nullptr, nullptr};
+    hipError_t e = take_event(c, &t.start);
+    if (e != hipSuccess) return e;
+    e = take_event(c, &t.stop);
+    if (e != hipSuccess) {
+        c->spare_events.push_back(t.start);
+        return e;
+    }
+    c->timed.push_back(t);
+    return hipEventRecord(t.start, stream);
+}
+
+hipError_t timed_end(lbm_ctx* c, hipStream_t stream) { return hipEventRecord(c->timed.back().stop, stream); }
+
+// Add the recorded launches to the sums (synchronises the stream) and keep
+// their events for reuse.
+hipError_t add_up_timed(lbm_ctx* c)
+{
+    if (c->timed.empty()) return hipSuccess;
+    hipError_t e = hipStreamSynchronize(c->stream);
+    for (const lbm_ctx::Timed& t : c->timed) {
+        if (e == hipSuccess) {
+            float ms = 0.0f;
+            e = hipEventElapsedTime(&ms, t.start, t.stop);
+            c->prof_ms[t.kind] += ms;
+            c->prof_launches[t.kind] += 1;
+        }
+        c->spare_events.push_back(t.start);
+        c->spare_events.push_back(t.stop);
+    }
+    c->timed.clear();
+    return e;
+}
+
+// A launch, timed when profiling and launched on the caller's stream (graph
+// captures run on a private stream and are never timed).
+#define LBM_TIMED(ctx, stream, kind, call, what)                                       \
+    do {                                                                               \
+        const bool timed_ = (ctx)->profile && (stream) == (ctx)->stream;               \
+        if (timed_) LBM_HIP(ctx, timed_begin(ctx, stream, kind), "profile event");     \
+        LBM_HIP(ctx, call, what);                                                      \
+        if (timed_) LBM_HIP(ctx, timed_end(ctx, stream), "profile event");             \
+    } while (0)
+
 template <typename R>
 LinkArgs<R> link_args(lbm_ctx* c, int mode, char* fsrc, char* fdst, char* gsrc, char* gdst)
 {
@@ -767,14 +842,15 @@ lbm_status enqueue_step(lbm_ctx* c, hipStream_t stream, bool last)
         s.f = (R*)c->f;
         s.g = (R*)c->g;
         s.parity = parity;
-        LBM_HIP(c, (launch_aa_step<L, R>(s, c->thermal, c->lds[parity], stream)), "AA step kernel");
+        LBM_TIMED(c, stream, parity ? LBM_KERNEL_STEP_ODD : LBM_KERNEL_STEP_EVEN,
+                  (launch_aa_step<L, R>(s, c->thermal, c->lds[parity], stream)), "AA step kernel");
         la = link_args<R>(c, parity == 0 ? LINK_AA_AFTER_EVEN : LINK_AA_AFTER_ODD, c->f, c->f, c->g, c->g);
         if (passes) {
             // link passes: gather every source, then scatter
             la.begin = 0;
             la.end = n_links;
-            LBM_HIP(c, launch_link_gather<R>(la, stream), "link gather kernel");
-            LBM_HIP(c, launch_link_scatter<R>(la, stream), "link scatter kernel");
+            LBM_TIMED(c, stream, LBM_KERNEL_LINK_GATHER, launch_link_gather<R>(la, stream), "link gather kernel");
+            LBM_TIMED(c, stream, LBM_KERNEL_LINK_SCATTER, launch_link_scatter<R>(la, stream), "link scatter kernel");
         }
     } else {
         char* fa = parity ? c->f2 : c->f;
@@ -787,26 +863,32 @@ lbm_status enqueue_step(lbm_ctx* c, hipStream_t stream, bool last)
         s.g2 = (R*)gb;
         if (c->push) {
             // one pass: collide, push and the boundary rules (links are always in the kernel)
-            LBM_HIP(c, (launch_ab_push<L, R>(s, c->thermal, c->lds[parity], stream)), "A-B push kernel");
+            LBM_TIMED(c, stream, parity ? LBM_KERNEL_STEP_ODD : LBM_KERNEL_STEP_EVEN,
+                      (launch_ab_push<L, R>(s, c->thermal, c->lds[parity], stream)), "A-B push kernel");
         } else {
-            LBM_HIP(c, (launch_ab_collide<L, R>(s, c->thermal, c->lds[0], stream)), "A-B collide kernel");
-            LBM_HIP(c, (launch_ab_pull<L, R>(s, c->thermal, c->lds[1], stream)), "A-B pull kernel");
+            LBM_TIMED(c, stream, LBM_KERNEL_AB_COLLIDE, (launch_ab_collide<L, R>(s, c->thermal, c->lds[0], stream)),
+                      "A-B collide kernel");
+            LBM_TIMED(c, stream, LBM_KERNEL_AB_PULL, (launch_ab_pull<L, R>(s, c->thermal, c->lds[1], stream)),
+                      "A-B pull kernel");
         }
         la = link_args<R>(c, LINK_AB, fa, fb, ga, gb);
         if (passes) {
             // sources in one buffer, destinations in the other: one pass
             la.begin = 0;
             la.end = n_links;
-            LBM_HIP(c, launch_link_direct<R>(la, stream), "link kernel");
+            LBM_TIMED(c, stream, LBM_KERNEL_LINK_DIRECT, launch_link_direct<R>(la, stream), "link kernel");
         }
     }
     if (last) {
         // forces and heat of the submission's last step, read where each
         // link's bounced population was left
+        const bool timed = c->profile && stream == c->stream;
+        if (timed) LBM_HIP(c, timed_begin(c, stream, LBM_KERNEL_FORCE), "profile event");
         LBM_HIP(c, launch_zero_f64(c->accum, 4 * LBM_MAX_GROUPS, stream), "zero accumulators");
         la.begin = 0;
         la.end = n_links;
         LBM_HIP(c, (launch_link_force<L, R>(la, stream)), "force kernel");
+        if (timed) LBM_HIP(c, timed_end(c, stream), "profile event");
     }
     c->t += 1;
     return LBM_OK;
@@ -856,6 +938,14 @@ template <class L, typename R>
 lbm_status step_impl(lbm_ctx* c, int64_t n)
 {
     int64_t left = n;
+    if (c->profile) {
+        // every kernel launched and timed on its own
+        for (; left > 0; --left) {
+            if (lbm_status st = enqueue_step<L, R>(c, c->stream, left == 1)) return st;
+            if (c->timed.size() >= 1024) LBM_HIP(c, add_up_timed(c), "profile timing");
+        }
+        return LBM_OK;
+    }
     if (left >= 6) capture_pair<L, R>(c);
     if (c->pair && left > c->pair_steps + 1) {
         if (c->t & 1) {
@@ -1219,6 +1309,45 @@ int64_t lbm_num_links(const lbm_ctx* c, int32_t lattice)
     if (lattice == (c->two_d ? 9 : 19)) return c->n_f;
     if (lattice == (c->two_d ? 5 : 7)) return c->n_g;
     return -1;
+}
+
+lbm_status lbm_profile(lbm_ctx* c, int32_t on)
+{
+    if (!c) return LBM_E_INVALID;
+    if (on != 0 && on != 1) {
+        c->err = "on must be 0 or 1";
+        return LBM_E_INVALID;
+    }
+    if (on) {
+        // start the sums again; launches recorded before are dropped (their
+        // events are re-recorded before they are read again)
+        for (const lbm_ctx::Timed& t : c->timed) {
+            c->spare_events.push_back(t.start);
+            c->spare_events.push_back(t.stop);
+        }
+        c->timed.clear();
+        for (int k = 0; k < LBM_KERNEL_KINDS; ++k) {
+            c->prof_ms[k] = 0.0;
+            c->prof_launches[k] = 0;
+        }
+    }
+    c->profile = on != 0;
+    return LBM_OK;
+}
+
+lbm_status lbm_profile_read(lbm_ctx* c, double* ms, int64_t* launches, int32_t n)
+{
+    if (!c) return LBM_E_INVALID;
+    if (n < 0) {
+        c->err = "n must be >= 0";
+        return LBM_E_INVALID;
+    }
+    LBM_HIP(c, add_up_timed(c), "profile timing");
+    for (int32_t k = 0; k < n; ++k) {
+        if (ms) ms[k] = k < LBM_KERNEL_KINDS ? c->prof_ms[k] : 0.0;
+        if (launches) launches[k] = k < LBM_KERNEL_KINDS ? c->prof_launches[k] : 0;
+    }
+    return LBM_OK;
 }
 
 const char* lbm_last_error(const lbm_ctx* c) { return c ? c->err.c_str() : g_create_error.c_str(); }

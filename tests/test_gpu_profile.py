@@ -1,0 +1,117 @@
+"""Per-kernel timing through the C ABI (lbm_profile / lbm_profile_read).
+
+Timing launches every kernel on its own between two HIP events, instead of
+replaying captured step graphs.  The populations, fields and link sums must
+not change: the same run with and without timing gives the same fields bit
+for bit, in every streaming mode and in both link modes, with timing switched
+on and off between submissions.  The launch counts follow from the step
+sequence (even and odd steps, link passes per step, one force pass per
+submission), and the times are positive and add up to no more than the timed
+region."""
+import numpy as np
+import pytest
+
+from harness import say
+from lattice_boltzmann_cfd_amd import binding
+from test_gpu_parity import dirichlet_spheres_case
+
+pytestmark = pytest.mark.gpu
+
+K = binding
+
+
+def fields(s):
+    import torch
+
+    rho, u, T = s.macros()
+    torch.cuda.synchronize()
+    return [rho.cpu().numpy(), u.cpu().numpy(), T.cpu().numpy()]
+
+
+def expected_launches(streaming, links, t0, n):
+    """Launches of one submission of n steps starting at time t0."""
+    even = sum(1 for t in range(t0, t0 + n) if t % 2 == 0)
+    odd = n - even
+    c = {}
+    if streaming in (K.LBM_STREAM_AA, K.LBM_STREAM_AB_PUSH):
+        c["step_even"], c["step_odd"] = even, odd
+    else:
+        c["ab_collide"] = c["ab_pull"] = n
+    if links == K.LBM_LINKS_PASSES:
+        if streaming == K.LBM_STREAM_AA:
+            c["link_gather"] = c["link_scatter"] = n
+        else:
+            c["link_direct"] = n
+    c["force"] = 1
+    return c
+
+
+CONFIGS = [(K.LBM_STREAM_AA, K.LBM_LINKS_IN_KERNEL), (K.LBM_STREAM_AA, K.LBM_LINKS_PASSES),
+           (K.LBM_STREAM_AB, K.LBM_LINKS_IN_KERNEL), (K.LBM_STREAM_AB, K.LBM_LINKS_PASSES),
+           (K.LBM_STREAM_AB_PUSH, K.LBM_LINKS_IN_KERNEL)]
+
+
+@pytest.mark.parametrize("streaming,links", CONFIGS)
+def test_timed_run_equals_untimed_run_bitwise(streaming, links):
+    say(f"CASE profile streaming={streaming} links={links}")
+    w = dirichlet_spheres_case()
+    w.params["links"] = links
+    subs = [37, 40, 23]  # odd and even starts; long enough for graph replays when untimed
+    a = binding.Solver(w.params, w.labels, streaming=streaming)
+    b = binding.Solver(w.params, w.labels, streaming=streaming)
+    try:
+        a.init(w.rho, w.u, w.T)
+        b.init(w.rho, w.u, w.T)
+        ref_forces, got_forces = [], []
+        for n in subs:
+            a.step(n)
+            ref_forces.append(a.wall_force())
+        t = 0
+        for i, n in enumerate(subs):
+            b.profile(i != 1)  # timed, untimed, timed again (the sums restart)
+            b.step(n)
+            got_forces.append(b.wall_force())
+            times = b.kernel_times()
+            if i != 1:
+                assert times.keys() == expected_launches(streaming, links, t, n).keys(), times
+                for name, (ms, launches) in times.items():
+                    assert launches == expected_launches(streaming, links, t, n)[name], (name, times)
+                    assert np.isfinite(ms) and ms > 0.0, (name, times)
+            t += n
+        assert a.time == b.time == sum(subs)
+        for x, y in zip(fields(a), fields(b)):
+            assert np.array_equal(x, y, equal_nan=True)
+        for f, g in zip(ref_forces, got_forces):
+            assert np.allclose(f, g, rtol=1e-5, atol=1e-12)  # atomics add in no fixed order
+    finally:
+        a.close()
+        b.close()
+
+
+def test_kernel_times_within_the_timed_region():
+    import torch
+
+    say("CASE profile times within the region")
+    w = dirichlet_spheres_case()
+    s = binding.Solver(w.params, w.labels)
+    try:
+        s.init(w.rho, w.u, w.T)
+        s.step(4)
+        s.profile(True)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(s.stream)
+        s.step(1500)  # more than 1024 timed launches: the sums are folded inside lbm_step too
+        end.record(s.stream)
+        times = s.kernel_times()
+        region = start.elapsed_time(end)
+        total = sum(ms for ms, _ in times.values())
+        say(f"kernel times {times}, region {region:.3f} ms")
+        assert times["step_even"][1] == times["step_odd"][1] == 750
+        assert times["force"][1] == 1
+        assert 0.0 < total <= region * 1.001
+        s.profile(False)
+        s.step(10)
+        assert s.kernel_times() == times  # timing off: the sums stay as they were
+    finally:
+        s.close()
