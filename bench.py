@@ -114,14 +114,11 @@ def device_ceilings(nbytes: int = 19 * (1 << 24) * 4, reps: int = 10):
     return out
 
 
-def cpu_baseline(w, steps: int):
-    """The oracle as it stands on the host cores: one run of `steps` steps and
-    one of 0 steps on the same box; the difference is the stepping time (the
-    0-step run holds the oracle's serial set-up and read-out)."""
+def oracle_stepping_seconds(w, steps: int, threads: int):
+    """Wall seconds of `steps` oracle steps on `threads` host threads, less a
+    0-step run of the same box (the oracle's serial set-up and read-out)."""
     import oracle
 
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    oracle.build(force=False)
     T = w.T if w.params.get("thermal") else None
     t0 = time.perf_counter()
     oracle.run(w.params, 0, w.rho, w.u, T, labels=w.labels, nthreads=threads)
@@ -129,11 +126,27 @@ def cpu_baseline(w, steps: int):
     t0 = time.perf_counter()
     oracle.run(w.params, steps, w.rho, w.u, T, labels=w.labels, nthreads=threads)
     dt = time.perf_counter() - t0
-    stepping = max(dt - t_setup, 1e-9)
-    return {"value": w.cells * steps / stepping / 1e6, "unit": "MLUPS", "cores": threads, "kind": "oracle",
-            "sample": f"{steps} steps of the full {w.shape[0]}x{w.shape[1]}x{w.shape[2]} box "
-                      f"(fp64 two-buffer collide-then-pull, OpenMP over cells): {dt:.1f} s, less {t_setup:.1f} s "
-                      f"of set-up and read-out timed by a 0-step run"}
+    return max(dt - t_setup, 1e-9), dt, t_setup
+
+
+def cpu_baseline(w, steps: int, steps_one_thread: int):
+    """The oracle as it stands on the host cores: `steps` steps on all of
+    them and, if asked, `steps_one_thread` steps on one thread."""
+    import oracle
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    oracle.build(force=False)
+    stepping, dt, t_setup = oracle_stepping_seconds(w, steps, threads)
+    out = {"value": w.cells * steps / stepping / 1e6, "unit": "MLUPS", "cores": threads, "kind": "oracle",
+           "sample": f"{steps} steps of the full {w.shape[0]}x{w.shape[1]}x{w.shape[2]} box "
+                     f"(fp64 two-buffer collide-then-pull, OpenMP over cells): {dt:.1f} s, less {t_setup:.1f} s "
+                     f"of set-up and read-out timed by a 0-step run"}
+    if steps_one_thread > 0:
+        stepping1, dt1, t_setup1 = oracle_stepping_seconds(w, steps_one_thread, 1)
+        out["one_thread"] = {"value": w.cells * steps_one_thread / stepping1 / 1e6, "unit": "MLUPS", "cores": 1,
+                             "sample": f"{steps_one_thread} step(s) of the same box on one thread: {dt1:.1f} s, "
+                                       f"less {t_setup1:.1f} s of set-up and read-out"}
+    return out
 
 
 def main(argv=None):
@@ -147,6 +160,9 @@ def main(argv=None):
                     help="1 in place (AA), 2 two buffers in two passes, 3 two buffers in one pass")
     ap.add_argument("--cpu-steps", type=int, default=16,
                     help="oracle steps for the CPU baseline, about 15 s on 16 host threads at 256^3 (0: skip)")
+    ap.add_argument("--cpu-steps-one-thread", type=int, default=1,
+                    help="oracle steps on one host thread for the same baseline, about 14 s per step at 256^3 "
+                         "(0: skip)")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="after the timed region, this many more steps with per-kernel timing (lbm_profile); "
                          "adds the mean milliseconds per launch of each kernel kind to the line")
@@ -238,7 +254,7 @@ def main(argv=None):
     torch.cuda.empty_cache()
     roofline["practical"] = device_ceilings()
     if args.cpu_steps > 0:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_steps)
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_steps, args.cpu_steps_one_thread)
     print(json.dumps(line), flush=True)
     return 0
 
