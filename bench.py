@@ -36,6 +36,16 @@ def bytes_per_cell(thermal: bool, dtype: int, streaming: int, two_d: bool = Fals
     return 2 * q * dtype * passes
 
 
+def hbm_gbps(mlups: float, bytes_per_update: float) -> float:
+    """Algorithmic HBM GB/s of a throughput in MLUPS."""
+    return mlups * 1e6 * bytes_per_update / 1e9
+
+
+def mlups_at(gbps: float, bytes_per_update: float) -> float:
+    """MLUPS that a bandwidth of gbps GB/s allows at bytes_per_update."""
+    return gbps * 1e9 / bytes_per_update / 1e6
+
+
 WORKLOAD_INFO = {
     "sol256": "D3Q19 MRT isothermal, 256^3 periodic, tau=0.55, seeded random solenoidal velocity "
               "(|u|<=0.05) on rho=1 (the 128^3 in-place/two-buffer recipe at 256^3)",
@@ -235,7 +245,7 @@ def main(argv=None):
         "config": {"workload": args.workload, "description": WORKLOAD_INFO[args.workload],
                    "shape": list(w.shape), "cells": w.cells,
                    "streaming": STREAMING[args.streaming][2],
-                   "hbm_TBps_algorithmic": round(bpc * w.cells * args.steps / (ms / 1e3) / 1e12, 3)},
+                   "hbm_TBps_algorithmic": round(hbm_gbps(mlups, bpc) / 1e3, 3)},
         "roofline": roofline,
     }
     if args.profile_steps > 0:
