@@ -173,6 +173,9 @@ def main(argv=None):
     ap.add_argument("--cpu-steps-one-thread", type=int, default=1,
                     help="oracle steps on one host thread for the same baseline, about 14 s per step at 256^3 "
                          "(0: skip)")
+    ap.add_argument("--repeats", type=int, default=3,
+                    help="timed regions of K steps in all: the first gives the line's value; all of them, their "
+                         "mean and minimum are reported as repeat_MLUPS (the pages quote means of three runs)")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="after the timed region, this many more steps with per-kernel timing (lbm_profile); "
                          "adds the mean milliseconds per launch of each kernel kind to the line")
@@ -222,6 +225,15 @@ def main(argv=None):
     solver.wall_force(0)
     ms_per_step = ms / args.steps
     mlups = w.cells * args.steps / (ms / 1e3) / 1e6
+    runs = [mlups]
+    for _ in range(args.repeats - 1):
+        # the same timed region again, after the read-back above
+        torch.cuda.synchronize()
+        start.record(stream)
+        solver.step(args.steps)
+        end.record(stream)
+        torch.cuda.synchronize()
+        runs.append(w.cells * args.steps / (start.elapsed_time(end) / 1e3) / 1e6)
 
     two_d = int(w.params.get("lattice", 0)) == 1
     bpc = bytes_per_cell(thermal, args.dtype, args.streaming, two_d)
@@ -248,6 +260,9 @@ def main(argv=None):
                    "hbm_TBps_algorithmic": round(hbm_gbps(mlups, bpc) / 1e3, 3)},
         "roofline": roofline,
     }
+    if len(runs) > 1:
+        line["repeat_MLUPS"] = {"runs": [round(v, 1) for v in runs], "mean": round(sum(runs) / len(runs), 1),
+                                "min": round(min(runs), 1)}
     if args.profile_steps > 0:
         # per-kernel breakdown, outside the timed region (each kernel launched on its own between events)
         solver.profile(True)
