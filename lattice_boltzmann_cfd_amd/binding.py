@@ -154,10 +154,19 @@ def to_params(d: dict, dtype: int = 4, streaming: int = LBM_STREAM_AUTO) -> LbmP
     return p
 
 
-def _labels_ptr(labels):
+def _labels_ptr(labels, params: dict):
+    """Pointer to the labels as nx*ny*nz contiguous bytes (the library reads
+    exactly that many); a label array of another size or with values outside
+    0..255 is rejected here."""
     if labels is None:
         return ctypes.POINTER(ctypes.c_uint8)(), None
-    arr = np.ascontiguousarray(labels, dtype=np.uint8).reshape(-1)
+    src = np.asarray(labels)
+    cells = int(params["nx"]) * int(params["ny"]) * int(params["nz"])
+    if src.size != cells:
+        raise LbmError(LBM_E_INVALID, f"solid labels hold {src.size} values, the box has {cells} cells")
+    if src.dtype != np.uint8 and src.size and (src.min() < 0 or src.max() > 255):
+        raise LbmError(LBM_E_INVALID, "solid labels must lie in 0..255")
+    arr = np.ascontiguousarray(src, dtype=np.uint8).reshape(-1)
     return arr.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), arr
 
 
@@ -168,7 +177,7 @@ def _check(ctx, status):
 
 def lbm_required_bytes(params: dict, labels=None, dtype=4, streaming=LBM_STREAM_AUTO) -> int:
     p = to_params(params, dtype, streaming)
-    lp, _keep = _labels_ptr(labels)
+    lp, _keep = _labels_ptr(labels, params)
     return int(library().lbm_required_bytes(ctypes.byref(p), lp))
 
 
@@ -176,7 +185,7 @@ def lbm_create(params: dict, labels, device_buf: int, device_bytes: int, stream:
                streaming=LBM_STREAM_AUTO):
     """Returns the context handle (an integer)."""
     p = to_params(params, dtype, streaming)
-    lp, _keep = _labels_ptr(labels)
+    lp, _keep = _labels_ptr(labels, params)
     out = ctypes.c_void_p()
     st = library().lbm_create(ctypes.byref(p), lp, ctypes.c_void_p(device_buf), device_bytes,
                               ctypes.c_void_p(stream), ctypes.byref(out))
@@ -228,7 +237,7 @@ def lbm_num_links(ctx, lattice: int) -> int:
 
 def lbm_count_links(params: dict, labels, lattice: int) -> int:
     p = to_params(params)
-    lp, _keep = _labels_ptr(labels)
+    lp, _keep = _labels_ptr(labels, params)
     return int(library().lbm_count_links(ctypes.byref(p), lp, int(lattice)))
 
 

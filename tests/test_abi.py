@@ -331,3 +331,26 @@ def test_tile_layout_buffer_sizes(lib):
             sizes[tile, d] = binding.lbm_required_bytes(w.params, None, dtype=d)
         for tile in (13, 9, 6, 0):
             assert abs((sizes[31, d] - sizes[tile, d]) - 26 * 1024 * d) <= 2 * 256, (tile, d)
+
+
+@pytest.mark.parametrize("bad", ["short", "long", "negative", "too_large"])
+def test_label_arrays_checked_by_the_binding(lib, bad):
+    """The library reads nx*ny*nz label bytes; the binding refuses arrays of
+    another size or values outside 0..255 before any call."""
+    w = inputs.sphere128(shape=(12, 10, 8), R=3.0)
+    lab = w.labels.astype(np.int64)
+    if bad == "short":
+        lab = lab[:-1]
+    elif bad == "long":
+        lab = np.concatenate([lab, [0]])
+    elif bad == "negative":
+        lab[5] = -1
+    else:
+        lab[5] = 256
+    with pytest.raises(binding.LbmError) as e:
+        binding.lbm_required_bytes(w.params, lab)
+    assert e.value.status == binding.LBM_E_INVALID
+    with pytest.raises(binding.LbmError):
+        binding.lbm_count_links(w.params, lab, 19)
+    # the same labels in range and of the right size are accepted, whatever their integer type
+    assert binding.lbm_required_bytes(w.params, w.labels.astype(np.int32)) == binding.lbm_required_bytes(w.params, w.labels)
