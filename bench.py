@@ -50,6 +50,8 @@ WORKLOAD_INFO = {
     "sol256": "D3Q19 MRT isothermal, 256^3 periodic, tau=0.55, seeded random solenoidal velocity "
               "(|u|<=0.05) on rho=1 (the 128^3 in-place/two-buffer recipe at 256^3)",
     "sol128": "D3Q19 MRT isothermal, 128^3 periodic, tau=0.55, seeded random solenoidal velocity (|u|<=0.05)",
+    "sol512": "D3Q19 MRT isothermal, 512^3 periodic, tau=0.55, seeded random solenoidal velocity (|u|<=0.05) on "
+              "rho=1 (the 128^3 recipe at 512^3)",
     "sphere128": "D3Q19 MRT, 128^3 periodic, centred solid sphere R=16, bounce-back links, gx=1e-6",
     "cavity256": "thermal D3Q19+D3Q7 MRT, 256^3 cavity, x- hot/x+ cold, adiabatic others, Ra=1e7, Pr=0.71",
     "rb512": "thermal D3Q19+D3Q7 MRT, 512^3, periodic x/y, z- hot/z+ cold, random spheres R 4..12 (10%), "

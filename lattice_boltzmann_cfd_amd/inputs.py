@@ -23,6 +23,7 @@ Workloads (the pages give no input data; every one is synthetic):
                     (-0.5), seeded random non-overlapping spheres of radius
                     4..12 up to 10 % solid fraction, Ra = 1e8, Pr = 0.71.
   * ``sol256``   -- the ``sol128`` recipe at 256^3 (the throughput point).
+  * ``sol512``   -- the same recipe at 512^3 (the largest isothermal box).
   * ``channel256``-- flow past a sphere in an open channel, 256x128x128: x-
                     a velocity inlet at U = 0.05, x+ a pressure outlet at
                     rho_w = 1, y and z free-slip faces, a solid sphere R = 16
@@ -333,6 +334,12 @@ def sol256(shape=(256, 256, 256), seed=2) -> Workload:
     return w
 
 
+def sol512(shape=(512, 512, 512), seed=2) -> Workload:
+    w = sol128(shape, seed=seed)
+    w.name = "sol512"
+    return w
+
+
 def sphere128(shape=(128, 128, 128), R=16.0, gx=1e-6, tau=0.6) -> Workload:
     nx, ny, nz = shape
     rho, u, _ = rest(nx, ny, nz)
@@ -422,7 +429,8 @@ def tg2d(shape=(256, 256), u0=0.05, seed=1, tau=0.6) -> Workload:
     return Workload("tg2d", p, rho, u, None, None, 1000)
 
 
-WORKLOADS = dict(tg32=tg32, sol128=sol128, sol256=sol256, sphere128=sphere128, cavity256=cavity256, rb512=rb512,
+WORKLOADS = dict(tg32=tg32, sol128=sol128, sol256=sol256, sol512=sol512, sphere128=sphere128, cavity256=cavity256,
+                 rb512=rb512,
                  channel256=channel256, cavity2d=cavity2d, tg2d=tg2d)
 
 
