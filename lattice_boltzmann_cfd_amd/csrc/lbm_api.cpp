@@ -9,6 +9,7 @@
 #include <exception>
 #include <iterator>
 #include <new>
+#include <stdexcept>
 #include <string>
 #include <thread>
 #include <vector>
@@ -39,6 +40,10 @@ struct lbm_ctx {
     char* face_vel = nullptr;  // PRESSURE faces: velocity planes
     double* wall_T = nullptr;
     double* accum = nullptr;
+    int64_t* seg_begin = nullptr;  // force-pass segments (see LinkArgs)
+    int32_t* group_seg = nullptr;
+    double* seg_sum = nullptr;
+    int64_t n_seg = 0;
     double* diag = nullptr;
     int32_t* unstable = nullptr;
     int64_t n_f = 0, n_g = 0, n_wall = 0;
@@ -682,9 +687,34 @@ std::vector<uint32_t> build_mask(const lbm_params* p, const uint8_t* labels)
 }
 
 struct Layout {
-    size_t f, g, f2, g2, mask, lcell, lcellw, lmeta, scratch, face_vel, wall_T, accum, diag, unstable, total;
+    size_t f, g, f2, g2, mask, lcell, lcellw, lmeta, scratch, face_vel, wall_T, accum, seg_begin, group_seg, seg_sum,
+        diag, unstable, total;
     Geometry tiles;  // the tile fields of the kernels' Geometry
 };
+
+// Force-pass segments: each group's links (contiguous after order_links) cut
+// into runs of at most LINK_SEGMENT links.  A group of n links gives
+// ceil(n / LINK_SEGMENT) segments, so all groups together give at most
+// n_links / LINK_SEGMENT + 1 + LBM_MAX_GROUPS.
+size_t max_segments(int64_t n_links) { return (size_t)(n_links / LINK_SEGMENT) + 1 + LBM_MAX_GROUPS; }
+
+void build_segments(const std::vector<uint32_t>& meta, std::vector<int64_t>* seg_begin, std::vector<int32_t>* group_seg)
+{
+    const int64_t n = (int64_t)meta.size();
+    seg_begin->clear();
+    group_seg->assign(LBM_MAX_GROUPS + 1, 0);
+    int64_t l = 0;
+    for (int g = 0; g < LBM_MAX_GROUPS; ++g) {
+        (*group_seg)[g] = (int32_t)seg_begin->size();
+        int64_t e = l;
+        while (e < n && (int)((meta[e] >> LINK_GROUP_SHIFT) & LINK_GROUP_MASK) == g) ++e;
+        for (int64_t b = l; b < e; b += LINK_SEGMENT) seg_begin->push_back(b);
+        l = e;
+    }
+    (*group_seg)[LBM_MAX_GROUPS] = (int32_t)seg_begin->size();
+    if (l != n) throw std::runtime_error("internal: links are not ordered by group");
+    seg_begin->push_back(n);
+}
 
 Layout make_layout(const lbm_params* p, bool solids, int64_t n_links)
 {
@@ -715,6 +745,10 @@ Layout make_layout(const lbm_params* p, bool solids, int64_t n_links)
     L.face_vel = off; off += align_up(es * (size_t)face_planes(p, face_off));
     L.wall_T = off; off += align_up(8 * LBM_MAX_GROUPS);
     L.accum = off; off += align_up(8 * 4 * LBM_MAX_GROUPS);
+    const size_t max_seg = max_segments(n_links);
+    L.seg_begin = off; off += align_up(8 * (max_seg + 1));
+    L.group_seg = off; off += align_up(4 * (LBM_MAX_GROUPS + 1));
+    L.seg_sum = off; off += align_up(8 * 4 * max_seg);
     L.diag = off; off += align_up(8 * LBM_DIAG_COUNT);
     L.unstable = off; off += ALIGN;
     L.total = off;
@@ -813,6 +847,10 @@ LinkArgs<R> link_args(lbm_ctx* c, int mode, char* fsrc, char* fdst, char* gsrc, 
     a.mode = mode;
     a.in_kernel = c->in_kernel ? 1 : 0;
     a.bb = make_bounce<R>(&c->p, c->in_kernel, c->face_vel);
+    a.seg_begin = c->seg_begin;
+    a.group_seg = c->group_seg;
+    a.seg_sum = c->seg_sum;
+    a.n_seg = c->n_seg;
     return a;
 }
 
@@ -884,7 +922,6 @@ lbm_status enqueue_step(lbm_ctx* c, hipStream_t stream, bool last)
         // link's bounced population was left
         const bool timed = c->profile && stream == c->stream;
         if (timed) LBM_HIP(c, timed_begin(c, stream, LBM_KERNEL_FORCE), "profile event");
-        LBM_HIP(c, launch_zero_f64(c->accum, 4 * LBM_MAX_GROUPS, stream), "zero accumulators");
         la.begin = 0;
         la.end = n_links;
         LBM_HIP(c, (launch_link_force<L, R>(la, stream)), "force kernel");
@@ -1080,6 +1117,9 @@ lbm_status lbm_create(const lbm_params* p, const uint8_t* solid_labels, void* de
         c->face_vel = base + L.face_vel;
         c->wall_T = (double*)(base + L.wall_T);
         c->accum = (double*)(base + L.accum);
+        c->seg_begin = (int64_t*)(base + L.seg_begin);
+        c->group_seg = (int32_t*)(base + L.group_seg);
+        c->seg_sum = (double*)(base + L.seg_sum);
         c->diag = (double*)(base + L.diag);
         c->unstable = (int32_t*)(base + L.unstable);
         c->colf = make_collision<float>(p);
@@ -1107,6 +1147,11 @@ lbm_status lbm_create(const lbm_params* p, const uint8_t* solid_labels, void* de
         std::vector<int32_t>& cell = all.cell;
         std::vector<int32_t>& cellw = all.cellw;
         std::vector<uint32_t>& meta = all.meta;
+        std::vector<int64_t> seg_begin;
+        std::vector<int32_t> group_seg;
+        build_segments(meta, &seg_begin, &group_seg);
+        c->n_seg = (int64_t)seg_begin.size() - 1;
+        if ((size_t)c->n_seg > max_segments(nl)) throw std::runtime_error("internal: too many force segments");
         std::vector<double> wallT(LBM_MAX_GROUPS, 0.0);
         for (int f = 0; f < 6; ++f) wallT[f] = p->face_T[f];
         for (int gidx = 6; gidx < LBM_MAX_GROUPS; ++gidx) wallT[gidx] = p->solid_T;
@@ -1122,6 +1167,10 @@ lbm_status lbm_create(const lbm_params* p, const uint8_t* solid_labels, void* de
             e = hipMemcpyAsync(c->mask, mask.data(), 4 * (size_t)G.ncell, hipMemcpyHostToDevice, c->stream);
         if (e == hipSuccess)
             e = hipMemcpyAsync(c->wall_T, wallT.data(), 8 * LBM_MAX_GROUPS, hipMemcpyHostToDevice, c->stream);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(c->seg_begin, seg_begin.data(), 8 * seg_begin.size(), hipMemcpyHostToDevice, c->stream);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(c->group_seg, group_seg.data(), 4 * group_seg.size(), hipMemcpyHostToDevice, c->stream);
         if (e == hipSuccess) e = launch_zero_f64(c->accum, 4 * LBM_MAX_GROUPS, c->stream);
         if (e == hipSuccess) e = launch_zero_f64((double*)c->unstable, 1, c->stream);  // flag sits in a 256-B slot
         // the host vectors die at return: wait for the copies

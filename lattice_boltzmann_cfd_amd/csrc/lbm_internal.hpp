@@ -139,7 +139,17 @@ struct LinkArgs {
     int32_t mode;
     int32_t in_kernel;     // bounce-back happened inside the step kernel
     Bounce<R> bb;          // face rules and the PRESSURE faces' velocities
+    // force pass: the links cut into segments of one group each, at most
+    // LINK_SEGMENT links long; segment k is links [seg_begin[k], seg_begin[k + 1])
+    // and group g owns segments [group_seg[g], group_seg[g + 1])
+    const int64_t* seg_begin;
+    const int32_t* group_seg;
+    double* seg_sum;  // per segment: Fx, Fy, Fz, Q
+    int64_t n_seg;
 };
+
+// Links per force-pass segment: one wavefront sums a segment, 16 links a lane.
+constexpr int64_t LINK_SEGMENT = 1024;
 
 template <typename R>
 struct FieldArgs {

@@ -773,72 +773,100 @@ __global__ void __launch_bounds__(BLOCK) k_link_direct(LinkArgs<R> a)
 // the bounced population f_p^+ of each link where the step left it: with
 // in-kernel bounce-back (opp p, x) in place (the even step's usual store or
 // the odd step's bounce-back store); with link passes the scatter
-// destination; with two buffers B(opp p, x).  Values a Dirichlet temperature link stores after
-// anti-bounce-back are converted back.  It sums the momentum exchange
-// 2 c_p f_p^+ and the heat w T_w - 2 g_p^+ per group: wavefront shuffles, then
-// fp64 LDS atomics per block, then one global atomic per block and touched
-// group; a grid-stride loop keeps the block count (and the global atomics)
-// small.
+// destination; with two buffers B(opp p, x).  Values a Dirichlet temperature
+// link stores after anti-bounce-back are converted back.  Per link: the
+// momentum exchange 2 c_p f_p^+ and the heat w T_w - 2 g_p^+ (link_sum).
+template <class L, typename R>
+__device__ __forceinline__ LinkSum link_force_term(const LinkArgs<R>& a, int64_t l)
+{
+    const uint32_t meta = a.meta[l];
+    const int p = (int)(meta & LINK_DIR_MASK);
+    const int32_t grp = (int32_t)((meta >> LINK_GROUP_SHIFT) & LINK_GROUP_MASK);
+    const bool g7 = (meta & LINK_TEMP) != 0;
+    int32_t plane, idx;
+    bool transformed;
+    if (a.in_kernel && a.mode != LINK_AB) {
+        // even step: the usual store; odd step: the bounce-back store
+        plane = opp(p);
+        idx = a.cell[l];
+        transformed = a.mode == LINK_AA_AFTER_ODD;
+    } else {
+        // link passes, or the two-buffer pull: the link's destination
+        const LinkSlots sl = link_slots(a.mode, p, a.cell[l], a.cellw[l]);
+        plane = sl.dst_plane;
+        idx = sl.dst_idx;
+        transformed = true;
+    }
+    if (!g7 && transformed && ((meta >> LINK_RULE_SHIFT) & 3u) == RULE_SLIP) {
+        // the reflected population landed at x + c_t
+        plane = refl_rt<L>((int)((meta >> LINK_AXIS_SHIFT) & 3u), p);
+        idx = a.cellw[l];
+    }
+    R v = ld(g7 ? a.g_dst : a.f_dst, posb(a.geo, g7, plane, idx));
+    if (transformed && g7 && (meta & LINK_DIRICHLET)) v = (R)(a.omega * a.wall_T[grp]) - v;    return link_sum<L>(a, meta, p, grp, v, transformed, l);
+}
+
+// The sums are taken in a fixed order, so the same populations give the same
+// forces bit for bit: one wavefront per segment (a run of at most
+// LINK_SEGMENT links of one group), each lane adding its links in index
+// order, then a butterfly over the lanes; k_force_groups then adds each
+// group's segments in order.  No atomics.
 template <class L, typename R>
 __global__ void __launch_bounds__(BLOCK) k_link_force(LinkArgs<R> a)
 {
-    __shared__ double acc[4 * LBM_GROUPS];
-    for (int i = threadIdx.x; i < 4 * LBM_GROUPS; i += BLOCK) acc[i] = 0.0;
-    __syncthreads();
-    for (int64_t base = a.begin + (int64_t)blockIdx.x * BLOCK; base < a.end; base += (int64_t)gridDim.x * BLOCK) {
-        const int64_t l = base + threadIdx.x;
-        LinkSum c{0.0, 0.0, 0.0, 0.0};
-        int32_t grp = -1;
-        if (l < a.end) {
-            const uint32_t meta = a.meta[l];
-            const int p = (int)(meta & LINK_DIR_MASK);
-            grp = (int32_t)((meta >> LINK_GROUP_SHIFT) & LINK_GROUP_MASK);
-            const bool g7 = (meta & LINK_TEMP) != 0;
-            int32_t plane, idx;
-            bool transformed;
-            if (a.in_kernel && a.mode != LINK_AB) {
-                // even step: the usual store; odd step: the bounce-back store
-                plane = opp(p);
-                idx = a.cell[l];
-                transformed = a.mode == LINK_AA_AFTER_ODD;
-            } else {
-                // link passes, or the two-buffer pull: the link's destination
-                const LinkSlots sl = link_slots(a.mode, p, a.cell[l], a.cellw[l]);
-                plane = sl.dst_plane;
-                idx = sl.dst_idx;
-                transformed = true;
-            }
-            if (!g7 && transformed && ((meta >> LINK_RULE_SHIFT) & 3u) == RULE_SLIP) {
-                // the reflected population landed at x + c_t
-                plane = refl_rt<L>((int)((meta >> LINK_AXIS_SHIFT) & 3u), p);
-                idx = a.cellw[l];
-            }
-            R v = ld(g7 ? a.g_dst : a.f_dst, posb(a.geo, g7, plane, idx));
-            if (transformed && g7 && (meta & LINK_DIRICHLET)) v = (R)(a.omega * a.wall_T[grp]) - v;
-            c = link_sum<L>(a, meta, p, grp, v, transformed, l);
-        }
-        const int32_t lead = __shfl(grp, 0, 64);
-        if (__all(grp == lead || grp < 0)) {
-            c.fx = wave_sum(c.fx);
-            c.fy = wave_sum(c.fy);
-            c.fz = wave_sum(c.fz);
-            c.q = wave_sum(c.q);
-            if ((threadIdx.x & 63) == 0 && lead >= 0) {
-                atomicAdd(&acc[4 * lead + 0], c.fx);
-                atomicAdd(&acc[4 * lead + 1], c.fy);
-                atomicAdd(&acc[4 * lead + 2], c.fz);
-                atomicAdd(&acc[4 * lead + 3], c.q);
-            }
-        } else if (grp >= 0) {
-            atomicAdd(&acc[4 * grp + 0], c.fx);
-            atomicAdd(&acc[4 * grp + 1], c.fy);
-            atomicAdd(&acc[4 * grp + 2], c.fz);
-            atomicAdd(&acc[4 * grp + 3], c.q);
-        }
+    const int64_t seg = (int64_t)blockIdx.x * (BLOCK / 64) + (threadIdx.x >> 6);
+    if (seg >= a.n_seg) return;  // whole wavefronts leave together
+    const int64_t end = a.seg_begin[seg + 1];
+    LinkSum c{0.0, 0.0, 0.0, 0.0};
+    for (int64_t l = a.seg_begin[seg] + (threadIdx.x & 63); l < end; l += 64) {
+        const LinkSum t = link_force_term<L>(a, l);
+        c.fx += t.fx;
+        c.fy += t.fy;
+        c.fz += t.fz;
+        c.q += t.q;
     }
+    c.fx = wave_sum(c.fx);
+    c.fy = wave_sum(c.fy);
+    c.fz = wave_sum(c.fz);
+    c.q = wave_sum(c.q);
+    if ((threadIdx.x & 63) == 0) {
+        double* out = a.seg_sum + 4 * seg;
+        out[0] = c.fx;
+        out[1] = c.fy;
+        out[2] = c.fz;
+        out[3] = c.q;
+    }
+}
+
+// Per group (one block each): the sum of its segments, thread t adding
+// segments t, t + BLOCK, ... in order, then a fixed halving tree over the
+// threads in local data share; written to the group's four accumulators (zero
+// for a group without links).
+__global__ void __launch_bounds__(BLOCK) k_force_groups(const int32_t* group_seg, const double* seg_sum, double* accum)
+{
+    __shared__ double part[4][BLOCK];
+    const int g = (int)blockIdx.x;
+    double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+    for (int32_t k = group_seg[g] + (int32_t)threadIdx.x; k < group_seg[g + 1]; k += BLOCK) {
+        const double* v = seg_sum + 4 * (int64_t)k;
+        s0 += v[0];
+        s1 += v[1];
+        s2 += v[2];
+        s3 += v[3];
+    }
+    part[0][threadIdx.x] = s0;
+    part[1][threadIdx.x] = s1;
+    part[2][threadIdx.x] = s2;
+    part[3][threadIdx.x] = s3;
     __syncthreads();
-    for (int i = threadIdx.x; i < 4 * LBM_GROUPS; i += BLOCK)
-        if (acc[i] != 0.0) atomicAdd(a.accum + i, acc[i]);
+    for (int h = BLOCK / 2; h > 0; h >>= 1) {
+        if ((int)threadIdx.x < h) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) part[c][threadIdx.x] += part[c][threadIdx.x + h];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x < 4) accum[4 * g + threadIdx.x] = part[threadIdx.x][0];
 }
 
 // ------------------------------------------------------ init / read
@@ -1106,9 +1134,15 @@ hipError_t launch_link_direct(const LinkArgs<R>& a, hipStream_t s)
 template <class L, typename R>
 hipError_t launch_link_force(const LinkArgs<R>& a, hipStream_t s)
 {
-    if (a.end <= a.begin) return hipSuccess;
-    const int64_t blocks = std::min<int64_t>((a.end - a.begin + BLOCK - 1) / BLOCK, 1024);
-    hipLaunchKernelGGL((k_link_force<L, R>), dim3((unsigned)blocks), dim3(BLOCK), 0, s, a);
+    if (a.n_seg > 0) {
+        const int64_t waves = BLOCK / 64;
+        hipLaunchKernelGGL((k_link_force<L, R>), dim3((unsigned)((a.n_seg + waves - 1) / waves)), dim3(BLOCK), 0, s,
+                           a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_force_groups, dim3(LBM_GROUPS), dim3(BLOCK), 0, s, a.group_seg, (const double*)a.seg_sum,
+                       a.accum);
     return hipGetLastError();
 }
 

@@ -150,9 +150,9 @@ def test_submissions_split_bitwise(streaming):
     for k in ("rho", "u", "T"):
         assert np.array_equal(whole[k], split[k], equal_nan=True)
         assert np.array_equal(whole[k], three[k], equal_nan=True)
-    # forces of the last step: same values, summed in a different order
+    # forces of the last step: the same values, summed in a fixed order
     fw, fs = whole["forces"][-1], split["forces"][-1]
-    assert np.allclose(fw, fs, rtol=1e-6, atol=1e-9)
+    assert np.array_equal(fw, fs) and np.array_equal(fw, three["forces"][-1])
     # drag series across submission boundaries against the oracle
     o = oracle_run(w, 100, want_diag=True)
     check_forces(split["forces"][0], o["diag"][36], 4, split["links19"] + split["links7"], "after 37")
@@ -161,14 +161,18 @@ def test_submissions_split_bitwise(streaming):
 
 @pytest.mark.parametrize("streaming", [binding.LBM_STREAM_AA, binding.LBM_STREAM_AB, binding.LBM_STREAM_AB_PUSH])
 def test_repeatable_bitwise(streaming):
-    """The same run twice gives the same fields bit for bit: no cell's result
-    depends on the order in which blocks run (a race would show here)."""
+    """The same run twice gives the same fields, forces and heat bit for bit:
+    no result depends on the order in which blocks run (a race would show
+    here)."""
     say(f"CASE repeatability streaming={streaming}")
     w = dirichlet_spheres_case()
     a = gpu_run(w, [7, 93], streaming=streaming)
     b = gpu_run(w, [7, 93], streaming=streaming)
     for k in ("rho", "u", "T"):
         assert np.array_equal(a[k], b[k], equal_nan=True), k
+    # the force and heat sums are taken in a fixed order: the same bits as well
+    for fa, fb in zip(a["forces"], b["forces"]):
+        assert np.array_equal(fa, fb)
 
 
 @pytest.mark.parametrize("dtype", [4, 8])
@@ -279,7 +283,7 @@ def test_graph_replays_match_eager_steps(streaming, links):
             assert graph.time == t
             for a, b, name in zip((r.cpu().numpy(), u.cpu().numpy(), T.cpu().numpy()), ref[t][:3], "ruT"):
                 assert np.array_equal(a, b, equal_nan=True), f"{name} differs at t={t}"
-            assert np.allclose(f, ref[t][3], rtol=1e-6, atol=1e-9)
+            assert np.array_equal(f, ref[t][3])
     finally:
         eager.close()
         graph.close()
