@@ -251,8 +251,10 @@ lbm_status lbm_read_macros(lbm_ctx* ctx, void* rho, void* u, void* T);
  * the momentum the fluid hands over through its links, c_p f_out - c_in f_in
  * per link (2 c_p f_p^+ for a wall), Q = heat into the fluid through its
  * Dirichlet links.  Groups beyond
- * LBM_MAX_GROUPS are zero-filled.  Synchronises the stream; returns
- * LBM_E_UNSTABLE if a read-back saw a non-finite fluid value. */
+ * LBM_MAX_GROUPS are zero-filled.  The sums are taken in a fixed order (no
+ * atomics), so the same state gives the same values bit for bit.
+ * Synchronises the stream; returns LBM_E_UNSTABLE if a read-back saw a
+ * non-finite fluid value. */
 lbm_status lbm_wall_force(lbm_ctx* ctx, double* out, int32_t n_groups);
 
 /* Indices of the values lbm_diagnostics() returns. */
