@@ -4,14 +4,21 @@
 
 A "step" is one pass of the whole fused step (the in-place AA kernel for
 D3Q19 (+D3Q7), bounce-back at walls and solids included; the wall-force pass
-on the last step of the submission) over the resident population buffer.  W untimed steps, then exactly
-K timed steps in one submission, bracketed by stream synchronisation; HIP
-events on the library's stream (torch's current stream) time the region.
+on the last step of the submission) over the resident population buffer.
+The solver is created first (host link lists, device buffer, the library's
+replay graph: the "pipeline creation", timed on its own and reported as
+setup_ms), then W untimed steps, then timed regions of exactly K steps in one
+submission each, bracketed by stream synchronisation; HIP events on the
+library's stream (torch's current stream) time each region.  The line's value
+is the mean over the regions (three by default, as the pages quote means of
+three runs), with every region and the minimum beside it.
 
 Prints one JSON line: MLUPS (cells * steps / s / 1e6, every cell counted),
 the roofline of the dominant kernel (algorithmic HBM bytes per launch / its
-average duration, against the 8 TB/s HBM peak) and the oracle's throughput on
-the host cores on a bounded sample of the same workload.
+average duration over the timed regions, against the 8 TB/s HBM peak; the
+kernel's own duration from per-kernel timing after the timed regions beside
+it) and the oracle's throughput on the host cores on a bounded sample of the
+same workload.
 """
 from __future__ import annotations
 
@@ -176,11 +183,12 @@ def main(argv=None):
                     help="oracle steps on one host thread for the same baseline, about 14 s per step at 256^3 "
                          "(0: skip)")
     ap.add_argument("--repeats", type=int, default=3,
-                    help="timed regions of K steps in all: the first gives the line's value; all of them, their "
-                         "mean and minimum are reported as repeat_MLUPS (the pages quote means of three runs)")
-    ap.add_argument("--profile-steps", type=int, default=0,
-                    help="after the timed region, this many more steps with per-kernel timing (lbm_profile); "
-                         "adds the mean milliseconds per launch of each kernel kind to the line")
+                    help="timed regions of K steps: the line's value is their mean; every region and the minimum "
+                         "are reported as repeat_MLUPS (the pages quote means of three runs)")
+    ap.add_argument("--profile-steps", type=int, default=32,
+                    help="after the timed regions, this many more steps with per-kernel timing (lbm_profile): the "
+                         "mean milliseconds per launch of each kernel kind, and the step kernel's own roofline "
+                         "fraction beside the timed one (0: skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run torch's device copy of 1 GiB 10 times (reference kernel for HBM counters)")
     args = ap.parse_args(argv)
@@ -208,34 +216,39 @@ def main(argv=None):
 
     w = inputs.make(args.workload)
     thermal = bool(w.params.get("thermal"))
+    # pipeline creation, timed apart from the steps: links on the host, the
+    # device buffer, the upload and the library's replay graph
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
     solver = binding.Solver(w.params, w.labels, dtype=args.dtype, streaming=args.streaming)
+    torch.cuda.synchronize()
+    t_create = time.perf_counter() - t0
+    t0 = time.perf_counter()
     solver.init(w.rho, w.u, w.T if thermal else None)
+    torch.cuda.synchronize()
+    t_init = time.perf_counter() - t0
     stream = torch.cuda.current_stream()
     solver.step(args.warmup)
     torch.cuda.synchronize()
 
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    solver.step(args.steps)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end)
-    # unstable runs raise here (LBM_E_UNSTABLE) rather than report a number
-    rho, _, _ = solver.macros()
-    solver.wall_force(0)
-    ms_per_step = ms / args.steps
-    mlups = w.cells * args.steps / (ms / 1e3) / 1e6
-    runs = [mlups]
-    for _ in range(args.repeats - 1):
-        # the same timed region again, after the read-back above
+    region_ms = []
+    for r in range(max(args.repeats, 1)):
         torch.cuda.synchronize()
         start.record(stream)
         solver.step(args.steps)
         end.record(stream)
         torch.cuda.synchronize()
-        runs.append(w.cells * args.steps / (start.elapsed_time(end) / 1e3) / 1e6)
+        region_ms.append(start.elapsed_time(end))
+        if r == 0:
+            # unstable runs raise here (LBM_E_UNSTABLE) rather than report a number
+            rho, _, _ = solver.macros()
+            solver.wall_force(0)
+    runs = [w.cells * args.steps / (ms / 1e3) / 1e6 for ms in region_ms]
+    ms = sum(region_ms) / len(region_ms)
+    ms_per_step = ms / args.steps
+    mlups = sum(runs) / len(runs)
 
     two_d = int(w.params.get("lattice", 0)) == 1
     bpc = bytes_per_cell(thermal, args.dtype, args.streaming, two_d)
@@ -243,14 +256,19 @@ def main(argv=None):
     has_links = (solver.num_links(flow) + solver.num_links(temp)) > 0
     launches = 2 if args.streaming == 2 else 1
     per_launch_bytes = bpc * w.cells / launches
-    # periodic boxes run exactly `launches` bulk kernels per step and nothing else
+    # the timed regions hold `launches` bulk kernels per step; the force pass
+    # of each submission's last step (and the link passes of a link-pass box)
+    # are counted in the step's time as well
     kernel_ms = ms_per_step / launches
     achieved = per_launch_bytes / (kernel_ms / 1e3) / 1e9
     traffic = load_traffic(args.workload, args.dtype, args.streaming)
     kernel = STREAMING[args.streaming][1]
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": kernel,
-                "bytes_per_cell": bpc, "launch_includes_links": has_links}
+                "bytes_per_cell": bpc, "bytes_per_launch": int(per_launch_bytes),
+                "timing": "HIP events around the timed regions on the library's stream, per launch of the step "
+                          "kernel (the gaps between launches included)",
+                "launch_includes_links": has_links}
 
     line = {
         "metric": METRIC, "value": round(mlups, 1), "unit": "MLUPS", "n_gpus": 1, "steps": args.steps,
@@ -261,16 +279,26 @@ def main(argv=None):
                    "streaming": STREAMING[args.streaming][2],
                    "hbm_TBps_algorithmic": round(hbm_gbps(mlups, bpc) / 1e3, 3)},
         "roofline": roofline,
+        "repeat_MLUPS": {"runs": [round(v, 1) for v in runs], "mean": round(mlups, 1), "min": round(min(runs), 1)},
+        "setup_ms": {"create": round(t_create * 1e3, 1), "init": round(t_init * 1e3, 1),
+                     "note": "solver creation (host link lists and checks, device buffer, upload, the replay graph "
+                             "captured and instantiated) and equilibrium initialisation, before any timed step"},
     }
-    if len(runs) > 1:
-        line["repeat_MLUPS"] = {"runs": [round(v, 1) for v in runs], "mean": round(sum(runs) / len(runs), 1),
-                                "min": round(min(runs), 1)}
     if args.profile_steps > 0:
-        # per-kernel breakdown, outside the timed region (each kernel launched on its own between events)
+        # per-kernel breakdown, outside the timed regions (each kernel launched on its own between events)
         solver.profile(True)
         solver.step(args.profile_steps)
-        line["kernel_ms"] = {k: round(ms / n, 5) for k, (ms, n) in solver.kernel_times().items()}
+        times = solver.kernel_times()
         solver.profile(False)
+        line["kernel_ms"] = {k: round(t / n, 5) for k, (t, n) in times.items()}
+        step_kinds = ("ab_collide", "ab_pull") if args.streaming == 2 else ("step_even", "step_odd")
+        t_step = sum(times[k][0] for k in step_kinds if k in times)
+        n_step = sum(times[k][1] for k in step_kinds if k in times)
+        if n_step:
+            k_ms = t_step / n_step
+            k_gbps = per_launch_bytes / (k_ms / 1e3) / 1e9
+            roofline["kernel_profile"] = {"ms_per_launch": round(k_ms, 5), "achieved": round(k_gbps, 1),
+                                          "frac": round(k_gbps / HBM_PEAK_GBPS, 4), "launches": n_step}
     if w.labels is not None:
         # solid cells are updated too (on NaN); the throughput over fluid cells only
         fluid = int((w.labels == 0).sum())

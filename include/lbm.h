@@ -207,6 +207,18 @@ size_t lbm_required_bytes(const lbm_params* p, const uint8_t* solid_labels);
 /* Validate the parameters, build the wall/solid link lists on the host
  * (every fluid cell x and direction p whose neighbour x + c_p is a wall face
  * or a solid cell), carve device_buf and upload the links.
+ * Defined by: "Multi-GPU thermal lattice Boltzmann simulations using OpenACC
+ * and MPI", Sec. 2 (the problem: a box of no-slip walls with half-way
+ * bounce-back, Dirichlet walls with anti-bounce-back and adiabatic walls,
+ * the relaxation matrices S and Q, the Boussinesq force) and "GPU lattice
+ * Boltzmann: streaming layout and performance", streaming-layout section
+ * (one population buffer in place or two buffers, per-link wall rules).
+ * The links are checked before upload: no two links may store into one
+ * slot and no solid cell's store may meet a fluid neighbour's bounce-back
+ * store (see lbm_check_links); a failure is LBM_E_INVALID.
+ * The step's replay graph (16 steps) is captured and instantiated here, once,
+ * so that later submissions carry no set-up work (the page's "pipeline
+ * creation", which it times apart from the steps).
  * device_buf: device memory of device_bytes bytes, BORROWED: the caller owns
  * it and keeps it alive until lbm_destroy(); the populations live in it, so
  * saving its bytes and lbm_time() checkpoints the state (lbm_resume).
@@ -223,13 +235,29 @@ lbm_status lbm_create(const lbm_params* p, const uint8_t* solid_labels, void* de
                       size_t device_bytes, void* hip_stream, lbm_ctx** out);
 
 /* Set the state to equilibrium of the given fields and the time to 0.
+ * Defined by: "GPU Optimization for High-Quality Kinetic Fluid Simulation",
+ * Sec. 3 (the initialisation step of its baseline GPU solver: populations,
+ * density and velocity set up on the device before the first step; Eq. 2,
+ * density and velocity as moments of f) and "Multi-GPU thermal lattice
+ * Boltzmann simulations using OpenACC and MPI", Sec. 2 (the equilibrium
+ * moments of both lattices).  The pages do not say which populations start
+ * a run; the reading here is f = f_eq(rho, u), g = N^-1 n_eq(T, u).  The
+ * latched forces and heat and the sticky unstable flag are cleared (a fresh
+ * run).
  * rho: nx*ny*nz values, u: three planes (ux, uy, uz) of nx*ny*nz values,
  * T: nx*ny*nz values or NULL (thermal runs then start at T = 0); all device
  * pointers in the context's dtype, read by kernels enqueued on the stream.
  * Values on solid cells are ignored.  Asynchronous. */
 lbm_status lbm_init_fields(lbm_ctx* ctx, const void* rho, const void* u, const void* T);
 
-/* Enqueue n fused time steps (a "submission"): per step one in-place kernel
+/* Enqueue n fused time steps (a "submission").  Defined by: "GPU lattice
+ * Boltzmann: streaming layout and performance", streaming-layout section (the
+ * AA pattern: even steps read (q, x) and write (opposite(q), x), odd steps
+ * read (opposite(q), x - c_q) and write (q, x + c_q); submissions of many
+ * steps; forces taken in the last step of a submission) and "Multi-GPU
+ * thermal lattice Boltzmann simulations using OpenACC and MPI", Sec. 2
+ * (the MRT collision of both lattices with the force term, half-way
+ * bounce-back and anti-bounce-back).  Per step one in-place kernel
  * (collision + streaming of D3Q19 and, if thermal, D3Q7, with the half-way
  * bounce-back of wall and solid links inside it; with links =
  * LBM_LINKS_PASSES, link gather and scatter kernels after it instead).  The
@@ -239,7 +267,11 @@ lbm_status lbm_init_fields(lbm_ctx* ctx, const void* rho, const void* u, const v
 lbm_status lbm_step(lbm_ctx* ctx, int64_t n);
 
 /* Macroscopic fields at the current time: rho, u = (sum c f + F/2)/rho as
- * three planes, T (may be NULL; ignored unless thermal).  Device pointers in
+ * three planes, T (may be NULL; ignored unless thermal).  Defined by:
+ * "Multi-GPU thermal lattice Boltzmann simulations using OpenACC and MPI",
+ * Sec. 2 (rho = sum f, u = (sum e f + F/2)/rho, T = sum g); the populations
+ * are found where the AA pattern left them after an odd or an even step
+ * count ("GPU lattice Boltzmann: streaming layout and performance").  Device pointers in
  * the context's dtype, written by a kernel on the stream.  Solid cells get
  * NaN.  If a fluid cell's rho or T is not finite, a sticky LBM_E_UNSTABLE is
  * recorded and returned by the next lbm_wall_force() or lbm_diagnostics().
@@ -247,7 +279,12 @@ lbm_status lbm_step(lbm_ctx* ctx, int64_t n);
 lbm_status lbm_read_macros(lbm_ctx* ctx, void* rho, void* u, void* T);
 
 /* Copy the latched per-group sums of the last step of the last submission to
- * out (host, 4*n_groups doubles): (Fx, Fy, Fz) = force on the face or solid,
+ * out (host, 4*n_groups doubles).  Defined by: "GPU lattice Boltzmann:
+ * streaming layout and performance", streaming-layout section (momentum
+ * exchange per wall link, taken at the step whose forces are read back) and
+ * "Multi-GPU thermal lattice Boltzmann simulations using OpenACC and MPI",
+ * Sec. 2 (the anti-bounce-back of a Dirichlet temperature link, through
+ * which heat enters the fluid).  (Fx, Fy, Fz) = force on the face or solid,
  * the momentum the fluid hands over through its links, c_p f_out - c_in f_in
  * per link (2 c_p f_p^+ for a wall), Q = heat into the fluid through its
  * Dirichlet links.  Groups beyond
@@ -334,6 +371,17 @@ int64_t lbm_time(const lbm_ctx* ctx);
  * the saved context would have.  No device work.  Errors: LBM_E_INVALID for a
  * NULL context or t < 0. */
 lbm_status lbm_resume(lbm_ctx* ctx, int64_t t);
+
+/* Host only (no device work): build the links lbm_create() would build for
+ * these parameters and labels and check them, as lbm_create() does: no two
+ * links store into one slot (the returning populations of the bounce-back
+ * inside the step kernel, and with links = LBM_LINKS_PASSES the stores of
+ * the link passes after an even and after an odd step), and every solid cell
+ * leaves the slot a fluid neighbour bounces into to that neighbour (its mask
+ * bit).  The in-place step ("GPU lattice Boltzmann: streaming layout and
+ * performance": each cell writes exactly the slots it read) relies on both.
+ * Returns LBM_OK, or LBM_E_INVALID with the reason in lbm_last_error(NULL). */
+lbm_status lbm_check_links(const lbm_params* p, const uint8_t* solid_labels);
 
 /* Number of links of the flow lattice's list (lattice = 19 for D3Q19 or 9
  * for D2Q9) or of the temperature lattice's (7 for D3Q7, 5 for D2Q5); -1

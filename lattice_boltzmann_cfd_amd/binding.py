@@ -36,7 +36,7 @@ KERNEL_NAMES = ("step_even", "step_odd", "ab_collide", "ab_pull", "link_gather",
 ABI_FUNCTIONS = (
     "lbm_required_bytes", "lbm_create", "lbm_init_fields", "lbm_step", "lbm_read_macros",
     "lbm_wall_force", "lbm_diagnostics", "lbm_time", "lbm_resume", "lbm_num_links", "lbm_count_links", "lbm_last_error",
-    "lbm_destroy", "lbm_profile", "lbm_profile_read",
+    "lbm_destroy", "lbm_profile", "lbm_profile_read", "lbm_check_links",
 )
 
 
@@ -101,6 +101,8 @@ def library():
         lib.lbm_num_links.restype = ctypes.c_int64
         lib.lbm_count_links.argtypes = [P, ctypes.POINTER(ctypes.c_uint8), ctypes.c_int32]
         lib.lbm_count_links.restype = ctypes.c_int64
+        lib.lbm_check_links.argtypes = [P, ctypes.POINTER(ctypes.c_uint8)]
+        lib.lbm_check_links.restype = ctypes.c_int
         lib.lbm_last_error.argtypes = [vp]
         lib.lbm_last_error.restype = ctypes.c_char_p
         lib.lbm_destroy.argtypes = [vp]
@@ -241,6 +243,16 @@ def lbm_count_links(params: dict, labels, lattice: int) -> int:
     return int(library().lbm_count_links(ctypes.byref(p), lp, int(lattice)))
 
 
+def lbm_check_links(params: dict, labels=None, dtype=4, streaming=LBM_STREAM_AUTO):
+    """Raise LbmError if the links lbm_create would build store twice into
+    one slot (host only)."""
+    p = to_params(params, dtype, streaming)
+    lp, _keep = _labels_ptr(labels, params)
+    st = library().lbm_check_links(ctypes.byref(p), lp)
+    if st != LBM_OK:
+        raise LbmError(st, lbm_last_error(None))
+
+
 def lbm_last_error(ctx) -> str:
     s = library().lbm_last_error(ctypes.c_void_p(ctx) if ctx else None)
     return s.decode() if s else ""
@@ -303,21 +315,32 @@ class Solver:
 
     def init(self, rho, u, T=None):
         n = self.cells
-        rho_d, u_d, T_d = self._dev(rho, (n,)), self._dev(u, (3, n)), self._dev(T, (n,))
+        # the inputs may come from work on the caller's stream: the solver's
+        # stream waits for it, then converts, copies and reads them itself
+        self.stream.wait_stream(self.torch.cuda.current_stream(self.device))
         with self.torch.cuda.stream(self.stream):
+            rho_d, u_d, T_d = self._dev(rho, (n,)), self._dev(u, (3, n)), self._dev(T, (n,))
             lbm_init_fields(self.ctx, rho_d.data_ptr(), u_d.data_ptr(), T_d.data_ptr() if T_d is not None else 0)
-        self._keep = (rho_d, u_d, T_d)  # read by a kernel on the stream
+        self._keep = (rho, u, T, rho_d, u_d, T_d)  # read by a copy or a kernel on the stream
 
     def step(self, n: int):
         lbm_step(self.ctx, n)
 
     def macros(self):
+        """(rho, u[3, n], T or None) as device tensors, written on the
+        solver's stream; the caller's current stream waits for them."""
         t = self.torch
         n = self.cells
-        rho = t.empty(n, dtype=self.tdtype, device=self.device)
-        u = t.empty((3, n), dtype=self.tdtype, device=self.device)
-        T = t.empty(n, dtype=self.tdtype, device=self.device) if self.params.get("thermal") else None
-        lbm_read_macros(self.ctx, rho.data_ptr(), u.data_ptr(), T.data_ptr() if T is not None else 0)
+        caller = t.cuda.current_stream(self.device)
+        with t.cuda.stream(self.stream):
+            rho = t.empty(n, dtype=self.tdtype, device=self.device)
+            u = t.empty((3, n), dtype=self.tdtype, device=self.device)
+            T = t.empty(n, dtype=self.tdtype, device=self.device) if self.params.get("thermal") else None
+            lbm_read_macros(self.ctx, rho.data_ptr(), u.data_ptr(), T.data_ptr() if T is not None else 0)
+        caller.wait_stream(self.stream)
+        for x in (rho, u, T):
+            if x is not None and caller != self.stream:
+                x.record_stream(caller)
         return rho, u, T
 
     def wall_force(self, n_groups: int = MAX_GROUPS) -> np.ndarray:

@@ -27,6 +27,7 @@ struct lbm_ctx {
     bool push = false;  // ... stepped in one pass (collide and push)
     bool two_d = false;  // D2Q9 + D2Q5 on one z layer
     hipStream_t stream = nullptr;
+    int device = 0;  // current device at lbm_create
     Geometry geo{};
     char* f = nullptr;
     char* g = nullptr;
@@ -686,6 +687,133 @@ std::vector<uint32_t> build_mask(const lbm_params* p, const uint8_t* labels)
     return mask;
 }
 
+// Run-time check that no two links store into one slot, and that no solid
+// cell's odd-step store meets a fluid neighbour's bounce-back store (the
+// in-place scheme needs every slot written by exactly one cell per step).
+// The stores the link lists stand for:
+//  * bounce-back inside the step kernel (odd step, and the one-pass
+//    two-buffer step): a link (x, p) stores the returning population at
+//    (opp p, x), a SLIP link at (p reflected, x + c_t), a temperature link at
+//    (opp k, x);
+//  * link passes after an even step: (p, x + c_p) (the link's cellw);
+//    after an odd step: (opp p, x).
+// A solid cell s stores direction q at (q, s + c_q) unless its mask marks q
+// as claimed; a solid link (x, p) with s = x + c_p stores at (opp p, x), so
+// s must mark opp p.  The links are bucketed by plane and each plane's cells
+// marked in one reusable bitmap of nx*ny*nz bits: O(links) time.  Returns an
+// empty string when the links are consistent.
+std::string check_link_destinations(const lbm_params* p, const LinkList& L, const std::vector<uint32_t>* mask,
+                                    bool passes)
+{
+    const bool two_d = p->lattice == LBM_LATTICE_2D;
+    const int Qf = two_d ? Q9 : Q19, Qt = two_d ? Q5 : Q7;
+    int cf[Q19][3], ct[Q7][3];
+    lattice_dirs(p, false, cf);
+    lattice_dirs(p, true, ct);
+    // c[d] of direction d (0 = rest) of either lattice, and its opposite / reflections
+    auto comp = [&](bool temp, int d, int a) { return d == 0 ? 0 : (temp ? ct[d - 1][a] : cf[d - 1][a]); };
+    auto find = [&](bool temp, int x, int y, int z) {
+        const int nq = temp ? Qt : Qf;
+        for (int r = 0; r < nq; ++r)
+            if (comp(temp, r, 0) == x && comp(temp, r, 1) == y && comp(temp, r, 2) == z) return r;
+        return -1;
+    };
+    // tables: opposite directions of both lattices, reflections across each axis
+    int opp_t[2][Q19], refl_t[3][Q19];
+    for (int t = 0; t < 2; ++t)
+        for (int d = 0; d < (t ? Qt : Qf); ++d)
+            opp_t[t][d] = find(t != 0, -comp(t != 0, d, 0), -comp(t != 0, d, 1), -comp(t != 0, d, 2));
+    for (int a = 0; a < 3; ++a)
+        for (int d = 0; d < Qf; ++d) {
+            int c[3] = {comp(false, d, 0), comp(false, d, 1), comp(false, d, 2)};
+            c[a] = -c[a];
+            refl_t[a][d] = find(false, c[0], c[1], c[2]);
+        }
+    auto opposite = [&](bool temp, int d) { return opp_t[temp ? 1 : 0][d]; };
+    auto reflected = [&](int d, int a) { return refl_t[a][d]; };
+    const int64_t n = (int64_t)p->nx * p->ny * p->nz;
+    const int64_t nl = (int64_t)L.meta.size();
+    const int planes = Qf + Qt;
+    std::vector<int64_t> start(planes + 1);
+    std::vector<int32_t> cells(nl);
+    std::vector<uint64_t> bits((size_t)((n + 63) / 64), 0u);
+    auto check_set = [&](auto slot_of, const char* what) -> std::string {
+        // counting sort of the links' destination cells by plane
+        std::fill(start.begin(), start.end(), 0);
+        for (int64_t l = 0; l < nl; ++l) {
+            int32_t cell;
+            ++start[slot_of(l, &cell) + 1];
+        }
+        for (int q = 0; q < planes; ++q) start[q + 1] += start[q];
+        std::vector<int64_t> pos(start.begin(), start.end() - 1);
+        for (int64_t l = 0; l < nl; ++l) {
+            int32_t cell;
+            const int q = slot_of(l, &cell);
+            cells[pos[q]++] = cell;
+        }
+        for (int q = 0; q < planes; ++q) {
+            std::string err;
+            for (int64_t i = start[q]; i < start[q + 1] && err.empty(); ++i) {
+                const int32_t c = cells[i];
+                uint64_t& w = bits[(size_t)c >> 6];
+                const uint64_t b = uint64_t(1) << (c & 63);
+                if (w & b) err = std::string("two links store into one slot (") + what + ", plane " +
+                                 std::to_string(q) + ", cell " + std::to_string(c) + ")";
+                w |= b;
+            }
+            for (int64_t i = start[q]; i < start[q + 1]; ++i) bits[(size_t)cells[i] >> 6] = 0u;
+            if (!err.empty()) return err;
+        }
+        return "";
+    };
+    auto unpack = [&](int64_t l, bool* temp, int* d, uint32_t* rule, int* axis) {
+        const uint32_t m = L.meta[l];
+        *temp = (m & LINK_TEMP) != 0;
+        *d = (int)(m & LINK_DIR_MASK);
+        *rule = (m >> LINK_RULE_SHIFT) & 3u;
+        *axis = (int)((m >> LINK_AXIS_SHIFT) & 3u);
+    };
+    // bounce-back stores (in the step kernel) and link-pass stores after an odd step
+    std::string err = check_set(
+        [&](int64_t l, int32_t* cell) {
+            bool temp;
+            int d, axis;
+            uint32_t rule;
+            unpack(l, &temp, &d, &rule, &axis);
+            if (!temp && rule == RULE_SLIP) {
+                *cell = L.cellw[l];
+                return reflected(d, axis);
+            }
+            *cell = L.cell[l];
+            return (temp ? Qf : 0) + opposite(temp, d);
+        },
+        "returning populations");
+    if (err.empty() && passes)
+        err = check_set(
+            [&](int64_t l, int32_t* cell) {
+                bool temp;
+                int d, axis;
+                uint32_t rule;
+                unpack(l, &temp, &d, &rule, &axis);
+                *cell = L.cellw[l];
+                return (temp ? Qf : 0) + d;
+            },
+            "link passes after an even step");
+    if (!err.empty() || !mask || passes) return err;
+    for (int64_t l = 0; l < nl; ++l) {
+        const uint32_t m = L.meta[l];
+        const int grp = (int)((m >> LINK_GROUP_SHIFT) & LINK_GROUP_MASK);
+        if (grp < 6 || (m & LINK_TEMP)) continue;
+        const int d = (int)(m & LINK_DIR_MASK);
+        const uint32_t ms = (*mask)[(size_t)L.cellw[l]];
+        const int o = opposite(false, d);
+        if (!(ms & MASK_SOLID) || !((ms >> o) & 1u))
+            return "solid cell " + std::to_string(L.cellw[l]) + " does not leave direction " + std::to_string(o) +
+                   " to the fluid cell " + std::to_string(L.cell[l]) + " that bounces into that slot";
+    }
+    return "";
+}
+
 struct Layout {
     size_t f, g, f2, g2, mask, lcell, lcellw, lmeta, scratch, face_vel, wall_T, accum, seg_begin, group_seg, seg_sum,
         diag, unstable, total;
@@ -820,21 +948,31 @@ hipError_t add_up_timed(lbm_ctx* c)
 // captures run on a private stream and are never timed).
 #define LBM_TIMED(ctx, stream, kind, call, what)                                       \
     do {                                                                               \
-        const bool timed_ = (ctx)->profile && (stream) == (ctx)->stream;               \
+        const bool timed_ = timing && (ctx)->profile && (stream) == (ctx)->stream;     \
         if (timed_) LBM_HIP(ctx, timed_begin(ctx, stream, kind), "profile event");     \
         LBM_HIP(ctx, call, what);                                                      \
         if (timed_) LBM_HIP(ctx, timed_end(ctx, stream), "profile event");             \
     } while (0)
 
+// Where a step's kernels keep their per-call scratch: the gathered link
+// values (link passes) and the force pass's per-segment sums (the context's
+// own buffer).
+struct StepScratch {
+    char* links;
+    double* seg_sum;
+};
+
+StepScratch own_scratch(const lbm_ctx* c) { return StepScratch{c->scratch, c->seg_sum}; }
+
 template <typename R>
-LinkArgs<R> link_args(lbm_ctx* c, int mode, char* fsrc, char* fdst, char* gsrc, char* gdst)
+LinkArgs<R> link_args(lbm_ctx* c, int mode, char* fsrc, char* fdst, char* gsrc, char* gdst, const StepScratch& sc)
 {
     LinkArgs<R> a{};
     a.geo = c->geo;
     a.cell = c->lcell;
     a.cellw = c->lcellw;
     a.meta = c->lmeta;
-    a.scratch = (R*)c->scratch;
+    a.scratch = (R*)sc.links;
     a.wall_T = c->wall_T;
     a.accum = c->accum;
     a.f_src = (R*)fsrc;
@@ -849,7 +987,7 @@ LinkArgs<R> link_args(lbm_ctx* c, int mode, char* fsrc, char* fdst, char* gsrc, 
     a.bb = make_bounce<R>(&c->p, c->in_kernel, c->face_vel);
     a.seg_begin = c->seg_begin;
     a.group_seg = c->group_seg;
-    a.seg_sum = c->seg_sum;
+    a.seg_sum = sc.seg_sum;
     a.n_seg = c->n_seg;
     return a;
 }
@@ -862,9 +1000,10 @@ template <>
 const Collision<double>& collision<double>(const lbm_ctx* c) { return c->cold; }
 
 // Enqueue one time step (parity from c->t) on `stream` and advance c->t;
-// `last` adds the force/heat pass of a submission's last step.
+// `last` adds the force/heat pass of a submission's last step.  `sc` names
+// the step's scratch; `timing` = false never times the launches.
 template <class L, typename R>
-lbm_status enqueue_step(lbm_ctx* c, hipStream_t stream, bool last)
+lbm_status enqueue_step(lbm_ctx* c, hipStream_t stream, bool last, const StepScratch& sc, bool timing = true)
 {
     const int64_t n_links = c->n_f + c->n_g;
     const bool passes = !c->in_kernel && n_links > 0;
@@ -882,7 +1021,7 @@ lbm_status enqueue_step(lbm_ctx* c, hipStream_t stream, bool last)
         s.parity = parity;
         LBM_TIMED(c, stream, parity ? LBM_KERNEL_STEP_ODD : LBM_KERNEL_STEP_EVEN,
                   (launch_aa_step<L, R>(s, c->thermal, c->lds[parity], stream)), "AA step kernel");
-        la = link_args<R>(c, parity == 0 ? LINK_AA_AFTER_EVEN : LINK_AA_AFTER_ODD, c->f, c->f, c->g, c->g);
+        la = link_args<R>(c, parity == 0 ? LINK_AA_AFTER_EVEN : LINK_AA_AFTER_ODD, c->f, c->f, c->g, c->g, sc);
         if (passes) {
             // link passes: gather every source, then scatter
             la.begin = 0;
@@ -909,7 +1048,7 @@ lbm_status enqueue_step(lbm_ctx* c, hipStream_t stream, bool last)
             LBM_TIMED(c, stream, LBM_KERNEL_AB_PULL, (launch_ab_pull<L, R>(s, c->thermal, c->lds[1], stream)),
                       "A-B pull kernel");
         }
-        la = link_args<R>(c, LINK_AB, fa, fb, ga, gb);
+        la = link_args<R>(c, LINK_AB, fa, fb, ga, gb, sc);
         if (passes) {
             // sources in one buffer, destinations in the other: one pass
             la.begin = 0;
@@ -920,7 +1059,7 @@ lbm_status enqueue_step(lbm_ctx* c, hipStream_t stream, bool last)
     if (last) {
         // forces and heat of the submission's last step, read where each
         // link's bounced population was left
-        const bool timed = c->profile && stream == c->stream;
+        const bool timed = timing && c->profile && stream == c->stream;
         if (timed) LBM_HIP(c, timed_begin(c, stream, LBM_KERNEL_FORCE), "profile event");
         la.begin = 0;
         la.end = n_links;
@@ -932,7 +1071,7 @@ lbm_status enqueue_step(lbm_ctx* c, hipStream_t stream, bool last)
 }
 
 // Capture 8 even/odd step pairs (kernel arguments and all) as one graph,
-// once per context.  Replays of 16 steps measured 0.4-1.7 % faster than of 2
+// once per context, at lbm_create.  Replays of 16 steps measured 0.4-1.7 % faster than of 2
 // steps on boxes of 4 M to 67 M cells (no slower on any), the gaps between
 // graph launches being a larger share of a short step.  Any failure leaves
 // the context on per-step launches.
@@ -953,16 +1092,24 @@ void capture_pair(lbm_ctx* c)
     bool ok = hipStreamBeginCapture(c->capture_stream, hipStreamCaptureModeThreadLocal) == hipSuccess;
     if (ok) {
         bool launched = true;
-        for (int i = 0; i < steps && launched; ++i) launched = enqueue_step<L, R>(c, c->capture_stream, false) == LBM_OK;
+        for (int i = 0; i < steps && launched; ++i)
+            launched = enqueue_step<L, R>(c, c->capture_stream, false, own_scratch(c)) == LBM_OK;
         ok = hipStreamEndCapture(c->capture_stream, &graph) == hipSuccess && launched && graph;
     }
     c->t = t_saved;
     c->err = err_saved;
     hipGraphExec_t exec = nullptr;
     if (ok && hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) == hipSuccess) {
-        c->pair = exec;
-        c->pair_steps = steps;
-        c->pair_failed = false;
+        // move the graph's work to the device now, or its first launch
+        // (inside the caller's first long submission) would carry that cost
+        if (hipGraphUpload(exec, c->capture_stream) == hipSuccess &&
+            hipStreamSynchronize(c->capture_stream) == hipSuccess) {
+            c->pair = exec;
+            c->pair_steps = steps;
+            c->pair_failed = false;
+        } else {
+            (void)hipGraphExecDestroy(exec);
+        }
     }
     if (graph) (void)hipGraphDestroy(graph);
     (void)hipGetLastError();  // a failed capture leaves no sticky error for the caller
@@ -970,7 +1117,7 @@ void capture_pair(lbm_ctx* c)
 
 // n steps: an odd first step alone, then replays of the step-pair graph,
 // then the remaining steps (the very last with the force pass) launched
-// directly.  Short submissions launch every step directly.
+// directly.  Submissions of at most 17 steps launch every step directly.
 template <class L, typename R>
 lbm_status step_impl(lbm_ctx* c, int64_t n)
 {
@@ -978,15 +1125,14 @@ lbm_status step_impl(lbm_ctx* c, int64_t n)
     if (c->profile) {
         // every kernel launched and timed on its own
         for (; left > 0; --left) {
-            if (lbm_status st = enqueue_step<L, R>(c, c->stream, left == 1)) return st;
+            if (lbm_status st = enqueue_step<L, R>(c, c->stream, left == 1, own_scratch(c))) return st;
             if (c->timed.size() >= 1024) LBM_HIP(c, add_up_timed(c), "profile timing");
         }
         return LBM_OK;
     }
-    if (left >= 6) capture_pair<L, R>(c);
     if (c->pair && left > c->pair_steps + 1) {
         if (c->t & 1) {
-            if (lbm_status st = enqueue_step<L, R>(c, c->stream, false)) return st;
+            if (lbm_status st = enqueue_step<L, R>(c, c->stream, false, own_scratch(c))) return st;
             --left;
         }
         while (left > c->pair_steps) {
@@ -996,7 +1142,7 @@ lbm_status step_impl(lbm_ctx* c, int64_t n)
         }
     }
     while (left > 0) {
-        if (lbm_status st = enqueue_step<L, R>(c, c->stream, left == 1)) return st;
+        if (lbm_status st = enqueue_step<L, R>(c, c->stream, left == 1, own_scratch(c))) return st;
         --left;
     }
     return LBM_OK;
@@ -1069,6 +1215,7 @@ lbm_status lbm_create(const lbm_params* p, const uint8_t* solid_labels, void* de
         c->push = p->streaming == LBM_STREAM_AB_PUSH;
         c->two_d = p->lattice == LBM_LATTICE_2D;
         c->stream = (hipStream_t)hip_stream;
+        if (hipGetDevice(&c->device) != hipSuccess) c->device = 0;
         const bool solids = any_solid(p, solid_labels);
         const uint8_t* lab = solids ? solid_labels : nullptr;
         LinkList lf, lg;
@@ -1155,14 +1302,22 @@ lbm_status lbm_create(const lbm_params* p, const uint8_t* solid_labels, void* de
         std::vector<double> wallT(LBM_MAX_GROUPS, 0.0);
         for (int f = 0; f < 6; ++f) wallT[f] = p->face_T[f];
         for (int gidx = 6; gidx < LBM_MAX_GROUPS; ++gidx) wallT[gidx] = p->solid_T;
+        std::vector<uint32_t> mask;
+        if (solids) mask = build_mask(p, solid_labels);
+        {
+            const std::string bad = check_link_destinations(p, all, solids ? &mask : nullptr, !c->in_kernel);
+            if (!bad.empty()) {
+                g_create_error = "internal: " + bad;
+                delete c;
+                return LBM_E_INVALID;
+            }
+        }
         hipError_t e = hipSuccess;
         if (nl > 0) {
             if (e == hipSuccess) e = hipMemcpyAsync(c->lcell, cell.data(), 4 * nl, hipMemcpyHostToDevice, c->stream);
             if (e == hipSuccess) e = hipMemcpyAsync(c->lcellw, cellw.data(), 4 * nl, hipMemcpyHostToDevice, c->stream);
             if (e == hipSuccess) e = hipMemcpyAsync(c->lmeta, meta.data(), 4 * nl, hipMemcpyHostToDevice, c->stream);
         }
-        std::vector<uint32_t> mask;
-        if (solids) mask = build_mask(p, solid_labels);
         if (e == hipSuccess && solids)
             e = hipMemcpyAsync(c->mask, mask.data(), 4 * (size_t)G.ncell, hipMemcpyHostToDevice, c->stream);
         if (e == hipSuccess)
@@ -1180,6 +1335,11 @@ lbm_status lbm_create(const lbm_params* p, const uint8_t* solid_labels, void* de
             delete c;
             return LBM_E_DEVICE;
         }
+        // the replay graph of 16 steps, built once here (the pipeline creation
+        // of "GPU lattice Boltzmann: streaming layout and performance", kept
+        // out of the submissions that follow)
+        if (c->two_d) c->es == 4 ? capture_pair<Lat2D, float>(c) : capture_pair<Lat2D, double>(c);
+        else c->es == 4 ? capture_pair<Lat3D, float>(c) : capture_pair<Lat3D, double>(c);
         *out = c;
         return LBM_OK;
     } catch (const std::bad_alloc&) {
@@ -1218,6 +1378,9 @@ lbm_status lbm_init_fields(lbm_ctx* c, const void* rho, const void* u, const voi
                      : launch_init<Lat3D, double>(a, c->thermal, c->stream);
     }
     if (e != hipSuccess) return device_error(c, e, "init kernel");
+    // a fresh state: no forces of an earlier run, no unstable flag
+    LBM_HIP(c, launch_zero_f64(c->accum, 4 * LBM_MAX_GROUPS, c->stream), "clear accumulators");
+    LBM_HIP(c, launch_zero_f64((double*)c->unstable, 1, c->stream), "clear flag");
     c->initialised = true;
     return LBM_OK;
 }
@@ -1350,6 +1513,40 @@ int64_t lbm_count_links(const lbm_params* p, const uint8_t* solid_labels, int32_
     } catch (...) {
         return -1;
     }
+}
+
+lbm_status lbm_check_links(const lbm_params* p, const uint8_t* solid_labels)
+{
+    g_create_error.clear();
+    try {
+        std::string why = validate(p);
+        if (why.empty() && solid_on_slip_layer(p, solid_labels)) why = "a solid cell lies in the first cell layer of a SLIP face";
+        if (!why.empty()) {
+            g_create_error = why;
+            return LBM_E_INVALID;
+        }
+        const bool solids = any_solid(p, solid_labels);
+        const uint8_t* lab = solids ? solid_labels : nullptr;
+        LinkList lf, lg, all;
+        build_links(p, lab, false, &lf);
+        if (p->thermal) build_links(p, lab, true, &lg);
+        order_links(lf, lg, &all);
+        std::vector<uint32_t> mask;
+        if (solids) mask = build_mask(p, solid_labels);
+        const bool walls = nonperiodic(p, 0) || nonperiodic(p, 2) || nonperiodic(p, 4);
+        const bool in_kernel = p->links == LBM_LINKS_IN_KERNEL && (walls || solids);
+        const std::string bad = check_link_destinations(p, all, solids ? &mask : nullptr, !in_kernel);
+        if (!bad.empty()) {
+            g_create_error = "internal: " + bad;
+            return LBM_E_INVALID;
+        }
+        return LBM_OK;
+    } catch (const std::bad_alloc&) {
+        g_create_error = "host allocation failed";
+    } catch (const std::exception& ex) {
+        g_create_error = ex.what();
+    }
+    return LBM_E_INVALID;
 }
 
 int64_t lbm_num_links(const lbm_ctx* c, int32_t lattice)
