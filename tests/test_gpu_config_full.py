@@ -13,10 +13,15 @@ risk: tau = 0.5205 in the 256^3 cavity, 0.5129 in the 512^3 cell).
   * 512^3 random-sphere convection cell, 1000 steps: the same.
 Each run is repeated in fp64 (the build the oracle pins at 1e-11) and the
 largest fp32 - fp64 field differences at the end are printed: they are the
-drift of fp32 rounding over the run, recorded, with loose bounds that only
-catch a broken build.  The fp32 mass bounds allow the rounding of the
-collision's per-cell sums to drift the total; a population lost or doubled
-at one cell each step would change it by about steps / cells."""
+drift of fp32 rounding over the run.  Measured on MI355X (fp32 mass change
+over the run; largest fp32 - fp64 field difference at the end):
+  sol128    1000 steps   1.3e-10   6.2e-8 (rho), 1.1e-8 (u)
+  sphere128 2000 steps   2.9e-10   6.0e-8 (rho), 7.1e-10 (u); drag 1.3e-7 rel.
+  cavity256 5000 steps   1.6e-11   6.2e-8 (rho), 8.8e-9 (u), 9.0e-8 (T)
+  rb512     1000 steps   1.1e-8    6.0e-8 (rho), 5.3e-11 (u), 1.5e-7 (T)
+The bounds are about a hundred times these; a population lost or doubled at
+one cell each step would change the mass by about steps / cells (6e-3 at
+128^3 after 1000 steps, 7e-6 at 512^3)."""
 import numpy as np
 import pytest
 
@@ -76,10 +81,10 @@ def test_sol128_1000_steps():
     say(f"  fp32 mass change {dm:.3e}, momentum change per cell {mom:.3e}, umax {aa['d1'][6]:.4f}; "
         f"fp32-fp64 drift {drift(aa, d64, fl)}; fp64 mass change {mass_change(d64):.3e}")
     assert np.isfinite(aa["u"]).all()
-    assert dm <= 1e-5
+    assert dm <= 1e-8
     assert mass_change(d64) <= 1e-13
-    assert mom <= 1e-6
-    assert max(drift(aa, d64, fl).values()) <= 1e-3
+    assert mom <= 1e-9
+    assert max(drift(aa, d64, fl).values()) <= 1e-5
 
 
 def test_sphere128_2000_steps_drag_every_100():
@@ -97,8 +102,9 @@ def test_sphere128_2000_steps_drag_every_100():
     assert (drag32 > 0).all()
     assert drag32[-1] > drag32[9] > drag32[0]
     assert (drag32 < total).all()
-    assert np.abs(drag32 - drag64).max() <= 1e-3 * drag64.max()
-    assert mass_change(r32) <= 1e-5
+    assert np.abs(drag32 - drag64).max() <= 1e-5 * drag64.max()
+    assert max(drift(r32, r64, fl).values()) <= 1e-5
+    assert mass_change(r32) <= 1e-8
 
 
 def thermal_case(name, w, steps, mass_tol):
@@ -115,12 +121,12 @@ def thermal_case(name, w, steps, mass_tol):
     assert hot > 0 > cold
     assert mass_change(r32) <= mass_tol
     assert mass_change(r64) <= 1e-12
-    assert max(drift(r32, r64, fl).values()) <= 1e-2
+    assert max(drift(r32, r64, fl).values()) <= 1e-5
 
 
 def test_cavity256_5000_steps():
-    thermal_case("cavity256", inputs.make("cavity256"), 5000, 1e-4)
+    thermal_case("cavity256", inputs.make("cavity256"), 5000, 1e-9)
 
 
 def test_rb512_1000_steps():
-    thermal_case("rb512", inputs.make("rb512"), 1000, 1e-4)
+    thermal_case("rb512", inputs.make("rb512"), 1000, 1e-6)

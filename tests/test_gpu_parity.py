@@ -201,6 +201,51 @@ def test_unstable_flag():
     assert e.value.status == binding.LBM_E_UNSTABLE
 
 
+def test_reinit_after_unstable_run_clears_flag_and_forces():
+    """lbm_init_fields starts a fresh run: the sticky unstable flag and the
+    latched forces of the blown-up run are cleared, so forces and diagnostics
+    read back normally, and the new run matches a context that never blew up."""
+    say("CASE re-init after unstable")
+    n = 16
+    rng = np.random.default_rng(0)
+    lab = inputs.sphere_labels(n, n, n, 3.0)
+    p = inputs.base_params(n, n, n, inputs.bgk_rates(0.5001))
+    s = binding.Solver(p, lab)
+    try:
+        s.init(np.ones(n ** 3), 0.4 * rng.uniform(-1, 1, (3, n ** 3)))
+        s.step(400)
+        s.macros()
+        with pytest.raises(binding.LbmError) as e:
+            s.diagnostics()
+        assert e.value.status == binding.LBM_E_UNSTABLE
+        rho, u, _ = inputs.rest(n, n, n)
+        s.init(rho, u)
+        assert np.array_equal(s.wall_force(), np.zeros((binding.MAX_GROUPS, 4)))
+        p2 = dict(p, accel=[1e-5, 0.0, 0.0])
+        s.close()
+        s = binding.Solver(p2, lab)
+        s.init(np.ones(n ** 3), 0.4 * rng.uniform(-1, 1, (3, n ** 3)))
+        s.step(400)
+        s.macros()
+        with pytest.raises(binding.LbmError):
+            s.wall_force()
+        s.init(rho, u)
+        s.step(5)
+        rho_a, u_a, _ = s.macros()
+        forces = s.wall_force()
+        diag = s.diagnostics()
+        assert np.isfinite(forces).all() and forces[6, 0] > 0
+        assert diag[binding.LBM_DIAG_FLUID_CELLS] == (lab == 0).sum()
+        assert abs(diag[binding.LBM_DIAG_MASS] - (lab == 0).sum()) <= 1e-3
+        fresh = gpu_run(inputs.Workload("rest", p2, rho, u, None, lab, 5), [5])
+        fl = lab == 0
+        assert np.array_equal(rho_a.cpu().double().numpy()[fl], fresh["rho"][fl])
+        assert np.array_equal(u_a.cpu().double().numpy()[:, fl], fresh["u"][:, fl])
+        assert np.array_equal(forces, fresh["forces"][-1])
+    finally:
+        s.close()
+
+
 def test_invalid_step_count():
     say("CASE invalid step")
     w = inputs.tg32(shape=(8, 8, 8))
