@@ -266,6 +266,27 @@ lbm_status lbm_init_fields(lbm_ctx* ctx, const void* rho, const void* u, const v
  * n = 0 is a no-op; n < 0 is LBM_E_INVALID.  Asynchronous. */
 lbm_status lbm_step(lbm_ctx* ctx, int64_t n);
 
+/* Bytes of the library's static per-GPU scratch used by lbm_step_noalloc. */
+enum { LBM_NOALLOC_SCRATCH_BYTES = 16 << 20 };
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): lbm_step()
+ * without allocation.  The same n steps with the same results bit for bit,
+ * each kernel launched directly on the context's stream (no replay graph, no
+ * per-kernel timing), and the step's per-call scratch -- the gathered link
+ * values of LBM_LINKS_PASSES and the force pass's per-segment sums -- in a
+ * static device array of LBM_NOALLOC_SCRATCH_BYTES bytes that the library
+ * holds on each GPU until the process ends, instead of the context's buffer.
+ * Calls no hipMalloc, hipFree or other allocating routine.  Every call on one
+ * GPU shares that GPU's array and leaves its contents behind (each step
+ * writes every scratch value it reads before reading it, so nothing needs
+ * clearing); calls that overlap in time on one GPU (other streams, other
+ * threads) race on it.  Errors: LBM_E_INVALID (NULL context, n < 0, no
+ * lbm_init_fields, or a context whose scratch exceeds the array: links *
+ * dtype for LBM_LINKS_PASSES plus 32 bytes per 1024 links of a group),
+ * LBM_E_DEVICE.  Asynchronous. */
+lbm_status lbm_step_noalloc(lbm_ctx* ctx, int64_t n);
+
 /* Macroscopic fields at the current time: rho, u = (sum c f + F/2)/rho as
  * three planes, T (may be NULL; ignored unless thermal).  Defined by:
  * "Multi-GPU thermal lattice Boltzmann simulations using OpenACC and MPI",

@@ -36,8 +36,9 @@ KERNEL_NAMES = ("step_even", "step_odd", "ab_collide", "ab_pull", "link_gather",
 ABI_FUNCTIONS = (
     "lbm_required_bytes", "lbm_create", "lbm_init_fields", "lbm_step", "lbm_read_macros",
     "lbm_wall_force", "lbm_diagnostics", "lbm_time", "lbm_resume", "lbm_num_links", "lbm_count_links", "lbm_last_error",
-    "lbm_destroy", "lbm_profile", "lbm_profile_read", "lbm_check_links",
+    "lbm_destroy", "lbm_profile", "lbm_profile_read", "lbm_check_links", "lbm_step_noalloc",
 )
+LBM_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class LbmParams(ctypes.Structure):
@@ -103,6 +104,8 @@ def library():
         lib.lbm_count_links.restype = ctypes.c_int64
         lib.lbm_check_links.argtypes = [P, ctypes.POINTER(ctypes.c_uint8)]
         lib.lbm_check_links.restype = ctypes.c_int
+        lib.lbm_step_noalloc.argtypes = [vp, ctypes.c_int64]
+        lib.lbm_step_noalloc.restype = ctypes.c_int
         lib.lbm_last_error.argtypes = [vp]
         lib.lbm_last_error.restype = ctypes.c_char_p
         lib.lbm_destroy.argtypes = [vp]
@@ -203,6 +206,10 @@ def lbm_init_fields(ctx, rho: int, u: int, T: int | None = None):
 
 def lbm_step(ctx, n: int):
     _check(ctx, library().lbm_step(ctypes.c_void_p(ctx), int(n)))
+
+
+def lbm_step_noalloc(ctx, n: int):
+    _check(ctx, library().lbm_step_noalloc(ctypes.c_void_p(ctx), int(n)))
 
 
 def lbm_read_macros(ctx, rho: int | None, u: int | None, T: int | None = None):
@@ -325,6 +332,11 @@ class Solver:
 
     def step(self, n: int):
         lbm_step(self.ctx, n)
+
+    def step_noalloc(self, n: int):
+        """The same steps through lbm_step_noalloc (no allocation, no replay
+        graph; scratch in the library's static per-GPU array)."""
+        lbm_step_noalloc(self.ctx, n)
 
     def macros(self):
         """(rho, u[3, n], T or None) as device tensors, written on the

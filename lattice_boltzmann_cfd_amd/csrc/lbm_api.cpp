@@ -8,6 +8,7 @@
 #include <cstring>
 #include <exception>
 #include <iterator>
+#include <mutex>
 #include <new>
 #include <stdexcept>
 #include <string>
@@ -955,8 +956,9 @@ hipError_t add_up_timed(lbm_ctx* c)
     } while (0)
 
 // Where a step's kernels keep their per-call scratch: the gathered link
-// values (link passes) and the force pass's per-segment sums (the context's
-// own buffer).
+// values (link passes) and the force pass's per-segment sums.  Normally the
+// context's own buffer; lbm_step_noalloc points them into the library's
+// static device array.
 struct StepScratch {
     char* links;
     double* seg_sum;
@@ -1148,6 +1150,16 @@ lbm_status step_impl(lbm_ctx* c, int64_t n)
     return LBM_OK;
 }
 
+// n steps, each launched directly on the caller's stream with the step's
+// scratch in `sc`; never timed, no graph.
+template <class L, typename R>
+lbm_status step_direct(lbm_ctx* c, int64_t n, const StepScratch& sc)
+{
+    for (int64_t left = n; left > 0; --left)
+        if (lbm_status st = enqueue_step<L, R>(c, c->stream, left == 1, sc, false)) return st;
+    return LBM_OK;
+}
+
 template <typename R>
 FieldArgs<R> field_args(lbm_ctx* c)
 {
@@ -1163,6 +1175,40 @@ FieldArgs<R> field_args(lbm_ctx* c)
     a.bb = make_bounce<R>(&c->p, c->in_kernel, c->face_vel);
     a.col = collision<R>(c);
     return a;
+}
+
+// Scratch of lbm_step_noalloc: one static array per GPU, held until the
+// process ends.  Host code never uses the name `scratch` as an address (on
+// the host it names a stand-in): the device address comes from
+// hipGetSymbolAddress, once per device with that device current, and is kept
+// in noalloc_ptr.
+static __device__ __align__(256) char scratch[LBM_NOALLOC_SCRATCH_BYTES];
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex noalloc_mutex;
+void* noalloc_ptr[NOALLOC_MAX_DEVICES] = {};
+
+// Device address of `scratch` on `dev` (looked up on the first call for that device).
+hipError_t noalloc_scratch(int dev, void** out)
+{
+    *out = nullptr;
+    if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(noalloc_mutex);
+    if (!noalloc_ptr[dev]) {
+        int cur = -1;
+        hipError_t e = hipGetDevice(&cur);
+        if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+        void* ptr = nullptr;
+        if (e == hipSuccess) e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur >= 0 && cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        noalloc_ptr[dev] = ptr;
+    }
+    *out = noalloc_ptr[dev];
+    return hipSuccess;
 }
 
 }  // namespace
@@ -1399,6 +1445,33 @@ lbm_status lbm_step(lbm_ctx* c, int64_t n)
     if (n == 0) return LBM_OK;
     if (c->two_d) return c->es == 4 ? step_impl<Lat2D, float>(c, n) : step_impl<Lat2D, double>(c, n);
     return c->es == 4 ? step_impl<Lat3D, float>(c, n) : step_impl<Lat3D, double>(c, n);
+}
+
+lbm_status lbm_step_noalloc(lbm_ctx* c, int64_t n)
+{
+    if (!c) return LBM_E_INVALID;
+    if (n < 0) {
+        c->err = "n must be >= 0";
+        return LBM_E_INVALID;
+    }
+    if (!c->initialised) {
+        c->err = "lbm_init_fields has not been called";
+        return LBM_E_INVALID;
+    }
+    // the step's scratch: gathered link values, then the force pass's segment sums
+    const size_t links = (c->in_kernel || c->n_f + c->n_g == 0) ? 0 : align_up((size_t)c->es * (c->n_f + c->n_g));
+    const size_t need = links + 8 * 4 * (size_t)c->n_seg;
+    if (need > LBM_NOALLOC_SCRATCH_BYTES) {
+        c->err = "lbm_step_noalloc: this context needs " + std::to_string(need) + " bytes of scratch, more than the " +
+                 std::to_string((size_t)LBM_NOALLOC_SCRATCH_BYTES) + " the library holds per GPU (use lbm_step)";
+        return LBM_E_INVALID;
+    }
+    if (n == 0) return LBM_OK;
+    void* base = nullptr;
+    LBM_HIP(c, noalloc_scratch(c->device, &base), "static scratch address");
+    const StepScratch sc{(char*)base, (double*)((char*)base + links)};
+    if (c->two_d) return c->es == 4 ? step_direct<Lat2D, float>(c, n, sc) : step_direct<Lat2D, double>(c, n, sc);
+    return c->es == 4 ? step_direct<Lat3D, float>(c, n, sc) : step_direct<Lat3D, double>(c, n, sc);
 }
 
 lbm_status lbm_read_macros(lbm_ctx* c, void* rho, void* u, void* T)
