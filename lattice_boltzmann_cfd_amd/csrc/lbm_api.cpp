@@ -1102,8 +1102,7 @@ void capture_pair(lbm_ctx* c)
     c->err = err_saved;
     hipGraphExec_t exec = nullptr;
     if (ok && hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) == hipSuccess) {
-        // move the graph's work to the device now, or its first launch
-        // (inside the caller's first long submission) would carry that cost
+        // move the graph's work to the device now, not at its first launch
         if (hipGraphUpload(exec, c->capture_stream) == hipSuccess &&
             hipStreamSynchronize(c->capture_stream) == hipSuccess) {
             c->pair = exec;
