@@ -131,6 +131,19 @@ bool finite(double v) { return std::isfinite(v); }
 // slower in either precision, so the value is not arbitrary).
 int64_t plane_stride(int64_t n) { return (n + 63) / 64 * 64 + 1024; }
 
+// Words of the mask array before its bitmap (the cell count rounded up to a
+// wavefront, so the bitmap starts on a 256-byte boundary).
+int64_t mask_words(int64_t n) { return (n + 63) / 64 * 64; }
+
+// One bit per cell, set where the cell's mask word is not 0.
+std::vector<uint32_t> near_bits(const std::vector<uint32_t>& mask)
+{
+    std::vector<uint32_t> bits((mask.size() + 31) / 32, 0u);
+    for (size_t i = 0; i < mask.size(); ++i)
+        if (mask[i]) bits[i >> 5] |= 1u << (i & 31);
+    return bits;
+}
+
 // Automatic tiling (lbm_params.tile_log2 = 0): tiles hold 32 KiB of each
 // plane (2^13 fp32 or 2^12 fp64 cells), 64 KiB (2^14 cells) for an
 // isothermal fp32 D3Q19 box, and a thermal fp32 box keeps its temperature
@@ -396,6 +409,7 @@ Bounce<R> make_bounce(const lbm_params* p, bool in_kernel, void* face_vel)
         b.face_area[f] = face_area(p, f);
     }
     face_planes(p, b.face_off);
+    b.near_off = (int32_t)mask_words((int64_t)p->nx * p->ny * p->nz);
     b.face_vel = (R*)face_vel;
     b.solid_gw = (R)(omega * p->solid_T);
     b.solid_dirichlet = p->solid_thermal == LBM_DIRICHLET ? 1 : 0;
@@ -865,7 +879,7 @@ Layout make_layout(const lbm_params* p, bool solids, int64_t n_links)
         L.g = L.f + (size_t)g_in_f * es;
         L.g2 = L.f2 + (size_t)g_in_f * es;
     }
-    L.mask = off; off += solids ? align_up(4 * (size_t)n) : 0;
+    L.mask = off; off += solids ? align_up(4 * (size_t)(mask_words(n) + (n + 31) / 32)) : 0;
     L.lcell = off; off += align_up(4 * (size_t)n_links);
     L.lcellw = off; off += align_up(4 * (size_t)n_links);
     L.lmeta = off; off += align_up(4 * (size_t)n_links);
@@ -1363,8 +1377,13 @@ lbm_status lbm_create(const lbm_params* p, const uint8_t* solid_labels, void* de
             if (e == hipSuccess) e = hipMemcpyAsync(c->lcellw, cellw.data(), 4 * nl, hipMemcpyHostToDevice, c->stream);
             if (e == hipSuccess) e = hipMemcpyAsync(c->lmeta, meta.data(), 4 * nl, hipMemcpyHostToDevice, c->stream);
         }
+        std::vector<uint32_t> bits;
+        if (solids) bits = near_bits(mask);
         if (e == hipSuccess && solids)
             e = hipMemcpyAsync(c->mask, mask.data(), 4 * (size_t)G.ncell, hipMemcpyHostToDevice, c->stream);
+        if (e == hipSuccess && solids)
+            e = hipMemcpyAsync(c->mask + mask_words(G.ncell), bits.data(), 4 * bits.size(), hipMemcpyHostToDevice,
+                               c->stream);
         if (e == hipSuccess)
             e = hipMemcpyAsync(c->wall_T, wallT.data(), 8 * LBM_MAX_GROUPS, hipMemcpyHostToDevice, c->stream);
         if (e == hipSuccess)

@@ -70,6 +70,10 @@ enum LinkRule : uint32_t { RULE_WALL = 0, RULE_SLIP = 1, RULE_VELOCITY = 2, RULE
 // which re-reads and re-stores the slot the solid cell's odd step would store
 // direction q to.  Temperature direction k (D3Q7: 1..6, D2Q5: 1..4) is the
 // flow lattice's axis direction k, so those bits serve both lattices.
+// The mask words are followed (Bounce::near_off words after the first) by a
+// bitmap of one bit per cell, set where the cell's mask word is not 0: the
+// step kernels read that bit first (a wavefront's 64 bits are 8 bytes) and
+// the 4-byte word only where it is set.
 constexpr uint32_t MASK_SOLID = 1u << 31;
 
 // Which slots a link pass reads and writes.
@@ -94,7 +98,7 @@ struct Bounce {
     int32_t solid_dirichlet;  // solids have a Dirichlet temperature
     int32_t in_kernel;        // walls and solids are handled inside the step kernel
     int32_t slip, vel, pres;  // bit f: face f is a SLIP / VELOCITY / PRESSURE face
-    int32_t pad0;
+    int32_t near_off;         // boxes with solids: words from the mask to its bitmap of cells with mask != 0
     R face_rho[6];            // wall density (VELOCITY, PRESSURE faces)
     R face_u[6][3];           // wall velocity (VELOCITY faces)
     // PRESSURE faces: the velocity of every cell of the face in its last

@@ -168,7 +168,8 @@ __device__ __forceinline__ Blocked blocked_dirs(const Bounce<R>& bb, const uint3
     b.wall = ((fw & 1u) ? dirs_through<L>(0) : 0u) | ((fw & 2u) ? dirs_through<L>(1) : 0u) |
              ((fw & 4u) ? dirs_through<L>(2) : 0u) | ((fw & 8u) ? dirs_through<L>(3) : 0u) |
              ((fw & 16u) ? dirs_through<L>(4) : 0u) | ((fw & 32u) ? dirs_through<L>(5) : 0u);
-    const uint32_t m = mask ? mask[cell] : 0u;
+    uint32_t m = 0u;
+    if (mask && ((mask[bb.near_off + (cell >> 5)] >> (cell & 31)) & 1u)) m = mask[cell];
     b.is_solid = (m & MASK_SOLID) != 0;
     b.solid = b.is_solid ? 0u : m;
     b.claim = b.is_solid ? (m & ~MASK_SOLID) : 0u;
