@@ -151,7 +151,9 @@ enum { LBM_LATTICE_3D = 0, LBM_LATTICE_2D = 1 };
  * population over the whole box (the
  * structure of arrays of "Multi-GPU thermal lattice Boltzmann simulations
  * using OpenACC and MPI", Sec. 3).  Whatever is asked, a buffer that would
- * reach 4 GiB tiled is stored one plane per population. */
+ * hold 2^32 elements or more tiled is stored one plane per population; the
+ * automatic choice tiles a buffer of 4 GiB or more only where that measured
+ * faster on MI355X (D3Q19 + D3Q7 in fp32, D2Q9 + D2Q5 in fp64). */
 
 /* Occupancy of the step kernels (no effect on results, only on speed).
  * occupancy[0] governs the even steps (in place or AB_PUSH) and the collide

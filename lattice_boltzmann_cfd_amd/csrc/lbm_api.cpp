@@ -163,17 +163,33 @@ int64_t tile_plane_bytes(const lbm_params* p)
     return iso3d_fp32 ? 2 * TILE_PLANE_BYTES : TILE_PLANE_BYTES;
 }
 
+// Automatic layout of a population buffer of 4 GiB or more: tiles (lane
+// offsets of 32-bit elements, scaled to bytes in 64-bit arithmetic) for the
+// kernel instances that ran faster that way on MI355X, one plane per
+// population for the others.  Same-box A/B of the step: the 512^3 box with
+// random spheres (D3Q19 + D3Q7, fp32) -3.5 % tiled (even step -9.8 %), the
+// 8193^2 heated cell (D2Q9 + D2Q5, fp64) -4.4 %; the 512^3 periodic box
+// (D3Q19) +1.2 % tiled in fp32 and +5.4 % in fp64, the 512^3 random-sphere box
+// in fp64 +3.2 %.
+bool tiles_for_large_buffers(const lbm_params* p)
+{
+    const bool two_d = p->lattice == LBM_LATTICE_2D;
+    return p->thermal && ((!two_d && p->dtype == 4) || (two_d && p->dtype == 8));
+}
+
 // Tile geometry of the population buffers (see Geometry).  Tiles are used
 // when asked for (tile_log2 in 6..20) or, automatically, when the box holds
-// at least four of them, and only while every population buffer stays below
-// 4 GiB, so that a lane's offset from its plane's base fits in 32 bits;
-// otherwise one plane per population over the whole box (each plane < 4 GiB,
-// checked by validate()).  Splitting larger buffers into groups of planes
-// that each stay below 4 GiB measured slower on MI355X (512^3 thermal 1 %,
-// the 8193^2 fp64 2D cell 5 %) than one plane per population.  Writes the
-// element counts of the flow and temperature buffers and, when the
-// temperature planes share the flow planes' tiles, the element offset of the
-// temperature buffer inside the flow buffer (else -1).
+// at least four of them and the buffer stays below 4 GiB (or, larger, for the
+// instances tiles_for_large_buffers() names); always only while every
+// population buffer holds fewer than 2^32 elements, so that a lane's element
+// offset from its plane's base fits in 32 bits.  Otherwise one plane per
+// population over the whole box (each plane < 4 GiB, checked by validate()).
+// Splitting larger buffers into groups of planes that each stay below 4 GiB
+// measured slower on MI355X (512^3 thermal 1 %, the 8193^2 fp64 2D cell 5 %)
+// than one plane per population.  Writes the element counts of the flow and
+// temperature buffers and, when the temperature planes share the flow
+// planes' tiles, the element offset of the temperature buffer inside the flow
+// buffer (else -1).
 void tile_geometry(const lbm_params* p, Geometry* G, int64_t* elems_f, int64_t* elems_g, int64_t* g_in_f)
 {
     const int64_t n = (int64_t)p->nx * p->ny * p->nz;
@@ -192,7 +208,9 @@ void tile_geometry(const lbm_params* p, Geometry* G, int64_t* elems_f, int64_t* 
         const int64_t limit = (int64_t(1) << 32) - (int64_t(1) << 20);
         const bool shared = p->thermal && (automatic ? p->dtype == 4 : true);
         const int64_t QF = shared ? Q + QT : Q;
-        if (QF * A < (int64_t(1) << 24) && tiles * QF * A * p->dtype < limit) {
+        const bool small = tiles * QF * A * p->dtype < limit;
+        const bool allowed = small || !automatic || tiles_for_large_buffers(p);
+        if (QF * A < (int64_t(1) << 24) && tiles * QF * A < limit && allowed) {
             G->tile_lg = lg;
             G->tile_mask = (uint32_t)(A - 1);
             G->qstride = A;

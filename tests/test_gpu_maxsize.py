@@ -1,15 +1,21 @@
 """GPU parity at the largest boxes the library accepts.
 
-A population plane (one plane per population) or a whole tiled buffer must
-stay below 2^32 - 2^20 bytes, because lanes address it with 32-bit offsets.
-These boxes sit just under that limit, where an offset overflow would show:
+A population plane (one plane per population) must stay below 2^32 - 2^20
+bytes, and a tiled buffer below 2^32 - 2^20 elements (lanes address a buffer
+with 32-bit element offsets, scaled to bytes in 64-bit arithmetic); the
+automatic layout tiles a buffer of 4 GiB or more only for the thermal fp32 3D
+and fp64 2D kernels.  These boxes sit just under those limits, where an
+offset overflow would show:
   * fp32 D3Q19, one plane per population: 1.07e9 cells (81 GB), walls on z;
   * fp64 D3Q19, one plane per population: 5.37e8 cells (81 GB), periodic;
-  * fp32 D3Q19 in tiles of 2^14 cells: the largest tiled buffer, walls on z;
+  * fp32 D3Q19 in tiles of 2^14 cells: the largest automatically tiled
+    isothermal buffer (just under 4 GiB), walls on z;
   * fp32 D3Q19 + D3Q7 in shared tiles of 2^13 cells: the largest tiled
-    thermal buffer, a heated cavity.
-One layer more is rejected (one plane per population) or stored untiled
-(tiles), checked on the host.  The initial state is an analytic field
+    thermal buffer (just under 2^32 elements, 17 GB), a heated cavity;
+  * fp64 D2Q9 + D2Q5 in tiles of 2^12 cells: the largest tiled 2D buffer
+    (the D2Q9 planes just under 2^32 elements, 34 GB), a heated strip.
+One layer (row) more is rejected (one plane per population) or stored
+untiled (tiles), checked on the host.  The initial state is an analytic field
 generated on the device; after 9 steps, windows at the box's first cells,
 its middle and its last cells are compared element by element with the
 oracle stepping the same windows (cells farther than 9 from a cut window edge
@@ -43,8 +49,13 @@ def case(name):
         shape, dtype, thermal = (383, 383, 385), 4, False
         kinds = [PER, PER, PER, PER, WALL, WALL]
     elif name == "tiles_thermal_f32":
-        shape, dtype, thermal = (345, 344, 347), 4, True
+        shape, dtype, thermal = (548, 548, 549), 4, True
         kinds = [WALL] * 6
+    elif name == "tiles_2d_f64":
+        p = inputs.base_params_2d(21840, 21845, inputs.mrt_rates_2d(0.6), thermal=True, face_kind=[WALL, WALL, PER, PER],
+                                  face_thermal=[1, 1, 0, 0], face_T=[0.5, -0.5, 0.0, 0.0],
+                                  s5=inputs.thermal_rates_2d(0.02), accel=(1e-5, 2e-6), gbeta=(0.0, 1e-4))
+        return p, 8
     else:
         raise KeyError(name)
     kw = dict(face_kind=kinds, accel=(1e-5, 2e-6, 0.0))
@@ -56,11 +67,16 @@ def case(name):
 
 
 def state_np(shape, idx, thermal):
-    """The initial state at cell indices idx (fp64)."""
+    """The initial state at cell indices idx (fp64); on one z layer u_z = 0
+    and T varies in x and y."""
     nx, ny, nz = shape
     x, y, z = idx % nx, (idx // nx) % ny, idx // (nx * ny)
     sx, sy, sz = (np.sin(2 * math.pi * x / nx), np.sin(2 * math.pi * y / ny), np.sin(2 * math.pi * z / nz))
     rho = 1.0 + 0.01 * sx * sy
+    if nz == 1:
+        u = np.stack([0.03 * sy, 0.03 * sx, 0.0 * sx])
+        T = 0.4 * sx * sy if thermal else None
+        return rho, u, T
     u = np.stack([0.03 * sy, 0.03 * sz, 0.03 * sx])
     T = 0.4 * sx * sz if thermal else None
     return rho, u, T
@@ -82,10 +98,14 @@ def state_device(torch, shape, dtype, thermal, chunk=1 << 26):
         sz = torch.sin(2 * math.pi * z.double() / nz)
         rho[s:s + idx.numel()] = (1.0 + 0.01 * sx * sy).to(td)
         u[0, s:s + idx.numel()] = (0.03 * sy).to(td)
-        u[1, s:s + idx.numel()] = (0.03 * sz).to(td)
-        u[2, s:s + idx.numel()] = (0.03 * sx).to(td)
+        if nz == 1:
+            u[1, s:s + idx.numel()] = (0.03 * sx).to(td)
+            u[2, s:s + idx.numel()] = 0.0
+        else:
+            u[1, s:s + idx.numel()] = (0.03 * sz).to(td)
+            u[2, s:s + idx.numel()] = (0.03 * sx).to(td)
         if thermal:
-            T[s:s + idx.numel()] = (0.4 * sx * sz).to(td)
+            T[s:s + idx.numel()] = (0.4 * sx * (sy if nz == 1 else sz)).to(td)
         del idx, x, y, z, sx, sy, sz
     return rho, u, T
 
@@ -94,7 +114,7 @@ def required(p, dtype, **extra):
     return binding.lbm_required_bytes(dict(p, **extra), None, dtype=dtype)
 
 
-@pytest.mark.parametrize("name", ["planes_f32", "planes_f64", "tiles_f32", "tiles_thermal_f32"])
+@pytest.mark.parametrize("name", ["planes_f32", "planes_f64", "tiles_f32", "tiles_thermal_f32", "tiles_2d_f64"])
 def test_largest_box_windows(name):
     import torch
 
@@ -102,21 +122,26 @@ def test_largest_box_windows(name):
     shape = (p["nx"], p["ny"], p["nz"])
     n = shape[0] * shape[1] * shape[2]
     thermal = bool(p["thermal"])
+    two_d = int(p.get("lattice", 0)) == 1
     say(f"CASE largest box {name} {shape} = {n:,} cells, dtype={dtype}")
-    bigger = dict(p, nz=p["nz"] + 1)
+    bigger = dict(p, ny=p["ny"] + 1) if two_d else dict(p, nz=p["nz"] + 1)
+    nb = n + (shape[0] if two_d else shape[0] * shape[1])
     if name.startswith("planes"):
         # one plane per population: the plane is just under the limit, one layer more is rejected
         assert ((n + 63) // 64 * 64 + 1024) * dtype < LIMIT
         assert required(p, dtype) == required(p, dtype, tile_log2=31)
         assert required(bigger, dtype) == 0
     else:
-        # tiled: the whole tiled buffer just under the limit; one layer more is stored untiled
+        # tiled: the largest tiled flow buffer just under its limit (4 GiB for the isothermal
+        # kernel, 2^32 elements for the others); one layer more is stored untiled
         tiled, untiled = required(p, dtype), required(p, dtype, tile_log2=31)
         assert tiled != untiled
-        planes = 26 if thermal else 19
-        lg = 13 if thermal else 14
-        tiles = -(-n // (1 << lg))
-        assert tiles * planes * (1 << lg) * dtype < LIMIT
+        planes, lg = {"tiles_f32": (19, 14), "tiles_thermal_f32": (26, 13), "tiles_2d_f64": (9, 12)}[name]
+        unit = dtype if name == "tiles_f32" else 1  # bytes or elements
+        assert -(-n // (1 << lg)) * planes * (1 << lg) * unit < LIMIT
+        assert -(-nb // (1 << lg)) * planes * (1 << lg) * unit >= LIMIT
+        if unit == 1:
+            assert -(-n // (1 << lg)) * planes * (1 << lg) * dtype > 2 ** 32  # past what 32-bit byte offsets reach
         assert required(bigger, dtype) == required(bigger, dtype, tile_log2=31)
 
     s = binding.Solver(p, None, dtype=dtype)
@@ -127,9 +152,10 @@ def test_largest_box_windows(name):
         rho, u, T = s.macros()
         torch.cuda.synchronize()
         del rho0, u0, T0
-        windows = [((0, 0, 0), (WIN,) * 3),
-                   ((shape[0] // 2, shape[1] // 2, shape[2] // 2), (WIN,) * 3),
-                   ((shape[0] - WIN, shape[1] - WIN, shape[2] - WIN), (WIN,) * 3)]
+        wz = 1 if two_d else WIN
+        windows = [((0, 0, 0), (WIN, WIN, wz)),
+                   ((shape[0] // 2, shape[1] // 2, shape[2] // 2), (WIN, WIN, wz)),
+                   ((shape[0] - WIN, shape[1] - WIN, shape[2] - wz), (WIN, WIN, wz))]
         worst = 0.0
         for lo, wn in windows:
             idx = window_indices(shape, lo, wn)
