@@ -354,3 +354,26 @@ def test_label_arrays_checked_by_the_binding(lib, bad):
         binding.lbm_count_links(w.params, lab, 19)
     # the same labels in range and of the right size are accepted, whatever their integer type
     assert binding.lbm_required_bytes(w.params, w.labels.astype(np.int32)) == binding.lbm_required_bytes(w.params, w.labels)
+
+
+@pytest.mark.parametrize("shape,thermal,lattice,dtype,tiled", [
+    ((512, 512, 512), True, 0, 4, True),    # D3Q19 + D3Q7 fp32, 14 GB: tiled
+    ((512, 512, 512), False, 0, 4, False),  # D3Q19 fp32, 10 GB: one plane per population
+    ((512, 512, 512), True, 0, 8, False),   # D3Q19 + D3Q7 fp64, 28 GB: one plane per population
+    ((8193, 8193, 1), True, 1, 8, True),    # D2Q9 + D2Q5 fp64, 7.5 GB: tiled
+    ((256, 256, 256), False, 0, 8, True),   # below 4 GiB: tiled whatever the kernel
+    ((1021, 1030, 1020), False, 0, 4, False),  # 2^32 elements or more: one plane per population
+])
+def test_automatic_layout_of_large_buffers(lib, shape, thermal, lattice, dtype, tiled):
+    """Buffers of 4 GiB or more are tiled only for the kernels measured faster
+    that way (thermal fp32 3D, thermal fp64 2D) and only below 2^32 elements;
+    the rest keep one plane per population (the layout tile_log2 = 31 asks for)."""
+    nx, ny, nz = shape
+    if lattice:
+        p = inputs.base_params_2d(nx, ny, inputs.mrt_rates_2d(0.6), thermal=thermal, s5=[0, 1, 1, 1, 1])
+    else:
+        p = inputs.base_params(nx, ny, nz, inputs.mrt_rates(0.6), thermal=thermal, s7=[0, 1, 1, 1, 1, 1, 1])
+    auto = binding.lbm_required_bytes(p, dtype=dtype)
+    planes = binding.lbm_required_bytes(dict(p, tile_log2=31), dtype=dtype)
+    assert auto > 0 and planes > 0
+    assert (auto != planes) == tiled
