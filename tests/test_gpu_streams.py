@@ -1,0 +1,50 @@
+"""The binding on a stream of its own (binding.Solver(stream=...)).
+
+The library runs every kernel on the stream its context was created with.
+The binding converts and copies the caller's fields on that stream, after it
+has waited for the caller's current stream, and allocates the read-back
+tensors there, making the caller's current stream wait for them.  Inputs
+produced on the caller's stream just before init, and read-backs used on the
+caller's stream right after, must then give exactly the fields of a solver on
+the caller's own stream."""
+import numpy as np
+import pytest
+
+from harness import say
+from lattice_boltzmann_cfd_amd import binding, inputs
+from test_gpu_parity import dirichlet_spheres_case
+
+pytestmark = pytest.mark.gpu
+
+
+def run(w, own_stream):
+    import torch
+
+    side = torch.cuda.Stream() if own_stream else None
+    s = binding.Solver(w.params, w.labels, stream=side)
+    try:
+        # inputs made on the caller's current stream, handed over at once
+        rho = torch.from_numpy(w.rho).cuda() * 1.0
+        u = torch.from_numpy(w.u).cuda() * 1.0
+        T = torch.from_numpy(w.T).cuda() * 1.0
+        s.init(rho, u, T)
+        del rho, u, T
+        s.step(23)
+        r, v, t = s.macros()
+        # used on the caller's stream without a synchronisation of the solver's
+        out = [(r * 1.0).cpu().numpy(), (v * 1.0).cpu().numpy(), (t * 1.0).cpu().numpy()]
+        forces = s.wall_force()
+        return out, forces
+    finally:
+        s.close()
+
+
+def test_solver_on_its_own_stream_equals_current_stream():
+    say("CASE solver on a stream of its own")
+    w = dirichlet_spheres_case()
+    ref, fref = run(w, False)
+    got, fgot = run(w, True)
+    fl = w.labels == 0
+    for a, b in zip(ref, got):
+        assert np.array_equal(a[..., fl], b[..., fl])
+    assert np.array_equal(fref, fgot)
