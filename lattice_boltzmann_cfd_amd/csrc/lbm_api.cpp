@@ -1105,10 +1105,10 @@ lbm_status enqueue_step(lbm_ctx* c, hipStream_t stream, bool last, const StepScr
 }
 
 // Capture 8 even/odd step pairs (kernel arguments and all) as one graph,
-// once per context, at lbm_create.  Replays of 16 steps measured 0.4-1.7 % faster than of 2
-// steps on boxes of 4 M to 67 M cells (no slower on any), the gaps between
-// graph launches being a larger share of a short step.  Any failure leaves
-// the context on per-step launches.
+// once per context, at lbm_create.  Replays of 16 steps measured 0.4-1.7 %
+// faster than of 2 steps on boxes of 4 M to 67 M cells (no slower on any),
+// the gaps between graph launches being a larger share of a short step.  Any
+// failure leaves the context on per-step launches.
 template <class L, typename R>
 void capture_pair(lbm_ctx* c)
 {
@@ -1629,7 +1629,8 @@ lbm_status lbm_check_links(const lbm_params* p, const uint8_t* solid_labels)
     g_create_error.clear();
     try {
         std::string why = validate(p);
-        if (why.empty() && solid_on_slip_layer(p, solid_labels)) why = "a solid cell lies in the first cell layer of a SLIP face";
+        if (why.empty() && solid_on_slip_layer(p, solid_labels))
+            why = "a solid cell lies in the first cell layer of a SLIP face";
         if (!why.empty()) {
             g_create_error = why;
             return LBM_E_INVALID;

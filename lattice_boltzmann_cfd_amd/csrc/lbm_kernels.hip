@@ -809,7 +809,8 @@ __device__ __forceinline__ LinkSum link_force_term(const LinkArgs<R>& a, int64_t
         idx = a.cellw[l];
     }
     R v = ld(g7 ? a.g_dst : a.f_dst, posb(a.geo, g7, plane, idx));
-    if (transformed && g7 && (meta & LINK_DIRICHLET)) v = (R)(a.omega * a.wall_T[grp]) - v;    return link_sum<L>(a, meta, p, grp, v, transformed, l);
+    if (transformed && g7 && (meta & LINK_DIRICHLET)) v = (R)(a.omega * a.wall_T[grp]) - v;
+    return link_sum<L>(a, meta, p, grp, v, transformed, l);
 }
 
 // The sums are taken in a fixed order, so the same populations give the same

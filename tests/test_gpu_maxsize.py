@@ -52,8 +52,8 @@ def case(name):
         shape, dtype, thermal = (548, 548, 549), 4, True
         kinds = [WALL] * 6
     elif name == "tiles_2d_f64":
-        p = inputs.base_params_2d(21840, 21845, inputs.mrt_rates_2d(0.6), thermal=True, face_kind=[WALL, WALL, PER, PER],
-                                  face_thermal=[1, 1, 0, 0], face_T=[0.5, -0.5, 0.0, 0.0],
+        p = inputs.base_params_2d(21840, 21845, inputs.mrt_rates_2d(0.6), thermal=True,
+                                  face_kind=[WALL, WALL, PER, PER], face_thermal=[1, 1, 0, 0], face_T=[0.5, -0.5, 0.0, 0.0],
                                   s5=inputs.thermal_rates_2d(0.02), accel=(1e-5, 2e-6), gbeta=(0.0, 1e-4))
         return p, 8
     else:
