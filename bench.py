@@ -61,6 +61,8 @@ WORKLOAD_INFO = {
               "rho=1 (the 128^3 recipe at 512^3)",
     "sphere128": "D3Q19 MRT, 128^3 periodic, centred solid sphere R=16, bounce-back links, gx=1e-6",
     "cavity256": "thermal D3Q19+D3Q7 MRT, 256^3 cavity, x- hot/x+ cold, adiabatic others, Ra=1e7, Pr=0.71",
+    "cavity385": "thermal D3Q19+D3Q7 MRT, 385^3 cavity (the thermal-LBM page's 3D grid; it runs fp64), x- hot/x+ "
+                 "cold, adiabatic others, Ra=1e7, Pr=0.71",
     "rb512": "thermal D3Q19+D3Q7 MRT, 512^3, periodic x/y, z- hot/z+ cold, random spheres R 4..12 (10%), "
              "Ra=1e8, Pr=0.71",
     "tg32": "D3Q19 MRT, 32^3 periodic Taylor-Green, tau=0.6",

@@ -362,6 +362,17 @@ def cavity256(shape=(256, 256, 256), Ra=1e7, Pr=0.71, H=256) -> Workload:
     return Workload("cavity256", p, rho, u, T, None, 5000, dict(scales=sc, Ra=Ra, Pr=Pr, H=H))
 
 
+def cavity385(shape=(385, 385, 385), Ra=1e7, Pr=0.71, H=None) -> Workload:
+    """The thermal-LBM page's 3D strong-scaling grid (Sec. 2: 385^3, odd so
+    that the half-way walls put a cell on the centre plane; 6000 steps, run
+    in double precision there) with the heated-cavity recipe of cavity256 (the
+    page's Rayleigh number for it is not printed); H defaults to the box
+    width."""
+    H = shape[0] if H is None else H
+    w = cavity256(shape, Ra=Ra, Pr=Pr, H=H)
+    return Workload("cavity385", w.params, w.rho, w.u, w.T, None, 6000, w.info)
+
+
 def rb512(shape=(512, 512, 512), Ra=1e8, Pr=0.71, H=512, seed=5, rmin=4, rmax=12) -> Workload:
     """Reduced boxes keep the recipe; the largest radius is clamped to
     (nz - 1)//2 - 1 so that a sphere fits between the plates."""
@@ -430,7 +441,7 @@ def tg2d(shape=(256, 256), u0=0.05, seed=1, tau=0.6) -> Workload:
 
 
 WORKLOADS = dict(tg32=tg32, sol128=sol128, sol256=sol256, sol512=sol512, sphere128=sphere128, cavity256=cavity256,
-                 rb512=rb512,
+                 cavity385=cavity385, rb512=rb512,
                  channel256=channel256, cavity2d=cavity2d, tg2d=tg2d)
 
 

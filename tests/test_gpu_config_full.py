@@ -10,7 +10,9 @@ risk: tau = 0.5205 in the 256^3 cavity, 0.5129 in the 512^3 cell).
     is still accelerating);
   * 256^3 heated cavity, 5000 steps: finite, closed-box mass kept, heat
     enters through the hot wall and leaves through the cold one;
-  * 512^3 random-sphere convection cell, 1000 steps: the same.
+  * 512^3 random-sphere convection cell, 1000 steps: the same;
+  * 385^3 heated cavity (the thermal page's 3D grid and length), 6000 steps:
+    the same.
 Each run is repeated in fp64 (the build the oracle pins at 1e-11) and the
 largest fp32 - fp64 field differences at the end are printed: they are the
 drift of fp32 rounding over the run.  Measured on MI355X (fp32 mass change
@@ -19,6 +21,7 @@ over the run; largest fp32 - fp64 field difference at the end):
   sphere128 2000 steps   2.9e-10   6.0e-8 (rho), 7.1e-10 (u); drag 1.3e-7 rel.
   cavity256 5000 steps   1.6e-11   6.2e-8 (rho), 8.8e-9 (u), 9.0e-8 (T)
   rb512     1000 steps   1.1e-8    6.0e-8 (rho), 5.3e-11 (u), 1.5e-7 (T)
+  cavity385 6000 steps   6.2e-12   6.2e-8 (rho), 8.0e-9 (u), 1.0e-7 (T)
 The bounds are about a hundred times these; a population lost or doubled at
 one cell each step would change the mass by about steps / cells (6e-3 at
 128^3 after 1000 steps, 7e-6 at 512^3)."""
@@ -112,7 +115,7 @@ def thermal_case(name, w, steps, mass_tol):
     r32 = run(w, [steps], 4)
     r64 = run(w, [steps], 8)
     fl = fluid_mask(w)
-    axis = 0 if name == "cavity256" else 2
+    axis = 0 if name in ("cavity256", "cavity385") else 2
     hot, cold = r32["heat"][2 * axis], r32["heat"][2 * axis + 1]
     say(f"  fp32: mass change {mass_change(r32):.3e}, umax {r32['d1'][binding.LBM_DIAG_UMAX]:.4f}, "
         f"Q hot {hot:.4e}, Q cold {cold:.4e}; fp64 mass change {mass_change(r64):.3e}, "
@@ -130,3 +133,10 @@ def test_cavity256_5000_steps():
 
 def test_rb512_1000_steps():
     thermal_case("rb512", inputs.make("rb512"), 1000, 1e-6)
+
+
+def test_cavity385_6000_steps():
+    """The thermal page's 3D grid and length (385^3, 6000 steps, run in double
+    precision there), with the heated-cavity recipe; fp32 against fp64 as
+    above."""
+    thermal_case("cavity385", inputs.make("cavity385"), 6000, 1e-9)
