@@ -145,15 +145,16 @@ enum { LBM_LATTICE_3D = 0, LBM_LATTICE_2D = 1 };
  * Kinetic Fluid Simulation", Sec. 4.1); thermal boxes may keep the
  * temperature planes in the same tiles.  tile_log2 = 0 picks the layout
  * measured fastest on MI355X: tiles of 32 KiB per plane (2^13 fp32 or 2^12
- * fp64 cells; 64 KiB, 2^14 cells, for isothermal fp32 D3Q19) when the box
- * holds at least four tiles, shared tiles for thermal fp32.  6..20 asks for
+ * fp64 cells; 64 KiB for isothermal fp32 D3Q19, 2^14 cells, and thermal fp64
+ * D3Q19 + D3Q7, 2^13 cells) when the box holds at least four tiles, shared
+ * tiles for thermal boxes except fp64 D2Q9 + D2Q5.  6..20 asks for
  * tiles of 2^k cells (shared for thermal boxes).  31 asks for one plane per
  * population over the whole box (the
  * structure of arrays of "Multi-GPU thermal lattice Boltzmann simulations
  * using OpenACC and MPI", Sec. 3).  Whatever is asked, a buffer that would
  * hold 2^32 elements or more tiled is stored one plane per population; the
  * automatic choice tiles a buffer of 4 GiB or more only where that measured
- * faster on MI355X (D3Q19 + D3Q7 in fp32, D2Q9 + D2Q5 in fp64). */
+ * faster on MI355X (D3Q19 + D3Q7 in either precision, D2Q9 + D2Q5 in fp64). */
 
 /* Occupancy of the step kernels (no effect on results, only on speed).
  * occupancy[0] governs the even steps (in place or AB_PUSH) and the collide

@@ -145,22 +145,29 @@ std::vector<uint32_t> near_bits(const std::vector<uint32_t>& mask)
 }
 
 // Automatic tiling (lbm_params.tile_log2 = 0): tiles hold 32 KiB of each
-// plane (2^13 fp32 or 2^12 fp64 cells), 64 KiB (2^14 cells) for an
-// isothermal fp32 D3Q19 box, and a thermal fp32 box keeps its temperature
-// planes in the same tiles as its flow planes.  Measured on MI355X in
-// same-box A/B runs of this library against one plane per population:
-// 256^3 fp32 step -6.1 %, 256^3 thermal fp32 -5.1 % (-1.2 % more with
-// shared tiles), the 8193^2 2D cell in fp32 -9.3 % (-2.0 % more), 256^3 fp64
-// -2.8 % with 2^12 instead of 2^13 cells; shared tiles cost 0.7 % in fp64.
-// With the occupancy bounds, 2^14 instead of 2^13 cells: 256^3 isothermal
-// fp32 -1.4 % (a sphere in that box and the open channel: within 0.4 %);
-// every other instance as fast or faster at 32 KiB per plane.
+// plane (2^13 fp32 or 2^12 fp64 cells), 64 KiB (2^14 fp32 or 2^13 fp64
+// cells) for an isothermal fp32 D3Q19 box and a thermal fp64 D3Q19 + D3Q7
+// box; a thermal box keeps its temperature planes in the same tiles as its
+// flow planes, except the fp64 2D one.  Measured on MI355X in same-box A/B
+// runs of this library against one plane per population: 256^3 fp32 step
+// -6.1 %, 256^3 thermal fp32 -5.1 % (-1.2 % more with shared tiles), the
+// 8193^2 2D cell in fp32 -9.3 % (-2.0 % more), 256^3 fp64 -2.8 % with 2^12
+// instead of 2^13 cells; shared tiles cost 0.7 % on the fp64 2D cell.  With
+// the occupancy bounds, 2^14 instead of 2^13 cells: 256^3 isothermal fp32
+// -1.4 % (a sphere in that box and the open channel: within 0.4 %).  The
+// thermal fp64 3D kernel in shared tiles of 2^13 cells against its earlier
+// layout (separate tiles of 2^12 cells below 4 GiB, one plane per population
+// above): 256^3 -0.4 %, 385^3 -8.0 %, 450^3 -8.2 %, 512^3 +1.1 % (with random
+// spheres +4.4 %); 2^12 and 2^14 cells were 2.2 % and 1.6 % slower at 385^3.
+// Every other instance as fast or faster at 32 KiB per plane.
 constexpr int64_t TILE_PLANE_BYTES = 32768;
 
 int64_t tile_plane_bytes(const lbm_params* p)
 {
-    const bool iso3d_fp32 = p->lattice == LBM_LATTICE_3D && !p->thermal && p->dtype == 4;
-    return iso3d_fp32 ? 2 * TILE_PLANE_BYTES : TILE_PLANE_BYTES;
+    const bool three_d = p->lattice == LBM_LATTICE_3D;
+    const bool iso3d_fp32 = three_d && !p->thermal && p->dtype == 4;
+    const bool thermal3d_fp64 = three_d && p->thermal && p->dtype == 8;
+    return iso3d_fp32 || thermal3d_fp64 ? 2 * TILE_PLANE_BYTES : TILE_PLANE_BYTES;
 }
 
 // Automatic layout of a population buffer of 4 GiB or more: tiles (lane
@@ -168,13 +175,16 @@ int64_t tile_plane_bytes(const lbm_params* p)
 // kernel instances that ran faster that way on MI355X, one plane per
 // population for the others.  Same-box A/B of the step: the 512^3 box with
 // random spheres (D3Q19 + D3Q7, fp32) -3.5 % tiled (even step -9.8 %), the
-// 8193^2 heated cell (D2Q9 + D2Q5, fp64) -4.4 %; the 512^3 periodic box
-// (D3Q19) +1.2 % tiled in fp32 and +5.4 % in fp64, the 512^3 random-sphere box
-// in fp64 +3.2 %.
+// 8193^2 heated cell (D2Q9 + D2Q5, fp64) -4.4 %, heated cavities in fp64
+// (D3Q19 + D3Q7) -8 % at 385^3 and 450^3 (+1.1 % at 512^3, +4.4 % for the
+// 512^3 random-sphere box: boxes of a power of two suit the planes' shift);
+// the periodic box (D3Q19) +1.2 % tiled in fp32 at 512^3 (+4.6 % at 400^3,
+// +0.8 % at 450^3, +2.1 % at 480^3) and +5.4 % in fp64 at 512^3 (+2.1 % at
+// 448^3, but -6.5 % at 385^3).
 bool tiles_for_large_buffers(const lbm_params* p)
 {
     const bool two_d = p->lattice == LBM_LATTICE_2D;
-    return p->thermal && ((!two_d && p->dtype == 4) || (two_d && p->dtype == 8));
+    return p->thermal && (!two_d || p->dtype == 8);
 }
 
 // Tile geometry of the population buffers (see Geometry).  Tiles are used
@@ -206,7 +216,7 @@ void tile_geometry(const lbm_params* p, Geometry* G, int64_t* elems_f, int64_t* 
         const int64_t A = int64_t(1) << lg;
         const int64_t tiles = (n + A - 1) >> lg;
         const int64_t limit = (int64_t(1) << 32) - (int64_t(1) << 20);
-        const bool shared = p->thermal && (automatic ? p->dtype == 4 : true);
+        const bool shared = p->thermal && (automatic ? p->dtype == 4 || !two_d : true);
         const int64_t QF = shared ? Q + QT : Q;
         const bool small = tiles * QF * A * p->dtype < limit;
         const bool allowed = small || !automatic || tiles_for_large_buffers(p);

@@ -359,14 +359,15 @@ def test_label_arrays_checked_by_the_binding(lib, bad):
 @pytest.mark.parametrize("shape,thermal,lattice,dtype,tiled", [
     ((512, 512, 512), True, 0, 4, True),    # D3Q19 + D3Q7 fp32, 14 GB: tiled
     ((512, 512, 512), False, 0, 4, False),  # D3Q19 fp32, 10 GB: one plane per population
-    ((512, 512, 512), True, 0, 8, False),   # D3Q19 + D3Q7 fp64, 28 GB: one plane per population
+    ((512, 512, 512), True, 0, 8, True),    # D3Q19 + D3Q7 fp64, 28 GB: tiled
+    ((550, 550, 550), True, 0, 8, False),   # the same, 2^32 elements or more: one plane per population
     ((8193, 8193, 1), True, 1, 8, True),    # D2Q9 + D2Q5 fp64, 7.5 GB: tiled
     ((256, 256, 256), False, 0, 8, True),   # below 4 GiB: tiled whatever the kernel
     ((1021, 1030, 1020), False, 0, 4, False),  # 2^32 elements or more: one plane per population
 ])
 def test_automatic_layout_of_large_buffers(lib, shape, thermal, lattice, dtype, tiled):
     """Buffers of 4 GiB or more are tiled only for the kernels measured faster
-    that way (thermal fp32 3D, thermal fp64 2D) and only below 2^32 elements;
+    that way (thermal 3D, thermal fp64 2D) and only below 2^32 elements;
     the rest keep one plane per population (the layout tile_log2 = 31 asks for)."""
     nx, ny, nz = shape
     if lattice:

@@ -11,6 +11,8 @@ of:
     periodic box, the momentum budget d(sum j)/dt = sum F - wall force, AA
     equal to two-buffer bit for bit.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -171,9 +173,13 @@ def test_channel256_windows():
 
 
 def test_fp64_full_size_windows(sol256, cavity256, rb512):
-    """The fp64 build at the full sizes (256^3 tiled, 512^3 one plane per
-    population), against the oracle's windows with the fp64 bar 1e-11."""
-    for name, w, steps in (("sol256", sol256, 7), ("cavity256", cavity256, 6), ("rb512", rb512, 7)):
+    """The fp64 build at the full sizes, in the automatic layouts (tiles; the
+    thermal planes in the flow planes' tiles) and the 512^3 box also in one
+    plane per population, against the oracle's windows with the fp64 bar
+    1e-11."""
+    rb512_planes = dataclasses.replace(rb512, params=dict(rb512.params, tile_log2=31))
+    for name, w, steps in (("sol256", sol256, 7), ("cavity256", cavity256, 6), ("rb512", rb512, 7),
+                           ("rb512 planes", rb512_planes, 7)):
         say(f"CASE {name} full size fp64, {steps} steps, windows")
         g = gpu_run(w, [steps], dtype=8, want_forces=False)
         wins = random_windows(w.shape, 3, 2 * steps + 12, seed=64 + steps) + [((0, 0, 0), (26, 26, 26))]

@@ -3,8 +3,8 @@
 A population plane (one plane per population) must stay below 2^32 - 2^20
 bytes, and a tiled buffer below 2^32 - 2^20 elements (lanes address a buffer
 with 32-bit element offsets, scaled to bytes in 64-bit arithmetic); the
-automatic layout tiles a buffer of 4 GiB or more only for the thermal fp32 3D
-and fp64 2D kernels.  These boxes sit just under those limits, where an
+automatic layout tiles a buffer of 4 GiB or more only for the thermal 3D
+and the thermal fp64 2D kernels.  These boxes sit just under those limits, where an
 offset overflow would show:
   * fp32 D3Q19, one plane per population: 1.07e9 cells (81 GB), walls on z;
   * fp64 D3Q19, one plane per population: 5.37e8 cells (81 GB), periodic;
@@ -12,6 +12,7 @@ offset overflow would show:
     isothermal buffer (just under 4 GiB), walls on z;
   * fp32 D3Q19 + D3Q7 in shared tiles of 2^13 cells: the largest tiled
     thermal buffer (just under 2^32 elements, 17 GB), a heated cavity;
+  * the same in fp64 (34 GB);
   * fp64 D2Q9 + D2Q5 in tiles of 2^12 cells: the largest tiled 2D buffer
     (the D2Q9 planes just under 2^32 elements, 34 GB), a heated strip.
 One layer (row) more is rejected (one plane per population) or stored
@@ -48,8 +49,8 @@ def case(name):
     elif name == "tiles_f32":
         shape, dtype, thermal = (383, 383, 385), 4, False
         kinds = [PER, PER, PER, PER, WALL, WALL]
-    elif name == "tiles_thermal_f32":
-        shape, dtype, thermal = (548, 548, 549), 4, True
+    elif name in ("tiles_thermal_f32", "tiles_thermal_f64"):
+        shape, dtype, thermal = (548, 548, 549), 4 if name.endswith("f32") else 8, True
         kinds = [WALL] * 6
     elif name == "tiles_2d_f64":
         p = inputs.base_params_2d(21840, 21845, inputs.mrt_rates_2d(0.6), thermal=True,
@@ -114,7 +115,8 @@ def required(p, dtype, **extra):
     return binding.lbm_required_bytes(dict(p, **extra), None, dtype=dtype)
 
 
-@pytest.mark.parametrize("name", ["planes_f32", "planes_f64", "tiles_f32", "tiles_thermal_f32", "tiles_2d_f64"])
+@pytest.mark.parametrize("name", ["planes_f32", "planes_f64", "tiles_f32", "tiles_thermal_f32", "tiles_thermal_f64",
+                                  "tiles_2d_f64"])
 def test_largest_box_windows(name):
     import torch
 
@@ -136,7 +138,8 @@ def test_largest_box_windows(name):
         # kernel, 2^32 elements for the others); one layer more is stored untiled
         tiled, untiled = required(p, dtype), required(p, dtype, tile_log2=31)
         assert tiled != untiled
-        planes, lg = {"tiles_f32": (19, 14), "tiles_thermal_f32": (26, 13), "tiles_2d_f64": (9, 12)}[name]
+        planes, lg = {"tiles_f32": (19, 14), "tiles_thermal_f32": (26, 13), "tiles_thermal_f64": (26, 13),
+                      "tiles_2d_f64": (9, 12)}[name]
         unit = dtype if name == "tiles_f32" else 1  # bytes or elements
         assert -(-n // (1 << lg)) * planes * (1 << lg) * unit < LIMIT
         assert -(-nb // (1 << lg)) * planes * (1 << lg) * unit >= LIMIT
