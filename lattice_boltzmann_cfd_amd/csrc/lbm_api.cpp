@@ -152,7 +152,7 @@ std::vector<uint32_t> near_bits(const std::vector<uint32_t>& mask)
 // runs of this library against one plane per population: 256^3 fp32 step
 // -6.1 %, 256^3 thermal fp32 -5.1 % (-1.2 % more with shared tiles), the
 // 8193^2 2D cell in fp32 -9.3 % (-2.0 % more), 256^3 fp64 -2.8 % with 2^12
-// instead of 2^13 cells; shared tiles cost 0.7 % on the fp64 2D cell.  With
+// instead of 2^13 cells; shared tiles cost the fp64 2D cell 6.1 %.  With
 // the occupancy bounds, 2^14 instead of 2^13 cells: 256^3 isothermal fp32
 // -1.4 % (a sphere in that box and the open channel: within 0.4 %).  The
 // thermal fp64 3D kernel in shared tiles of 2^13 cells against its earlier
