@@ -146,6 +146,28 @@ def test_cavity256_mass_closed_box(cavity256):
     assert heat[0] > 0 and heat[1] < 0  # the hot wall heats and the cold wall cools the T=0 fluid
 
 
+@pytest.mark.parametrize("dtype", [4, 8])
+def test_cavity385_windows_from_a_random_state(dtype):
+    """The thermal page's 385^3 grid (rows, planes and tiles out of step: 385
+    is odd, and the tiles of 2^13 cells cut rows anywhere) from a seeded random
+    state, so that every population slot holds a distinct value and a slot
+    read from the wrong tile or plane shows; 7 steps, windows at corners,
+    edges, faces and inside against the oracle."""
+    w = inputs.make("cavity385")
+    rng = np.random.default_rng(385)
+    n = w.cells
+    w = dataclasses.replace(w, rho=1.0 + rng.uniform(-1e-3, 1e-3, n), u=rng.uniform(-0.02, 0.02, (3, n)),
+                            T=rng.uniform(-0.5, 0.5, n))
+    steps = 7
+    say(f"CASE cavity385 full size thermal dtype={dtype}, random state, {steps} steps, windows")
+    g = gpu_run(w, [steps], dtype=dtype, want_forces=False)
+    N, m = 385, 24
+    windows = [((0, 0, 0), (m, m, m)), ((N - m, N - m, N - m), (m, m, m)), ((N - m, 0, 191), (m, m, m)),
+               ((0, 180, N - m), (m, m, m)), ((181, N - m, 0), (m, m, m))]
+    windows += random_windows(w.shape, 3, m, seed=385 + dtype)
+    compare_windows(w, g, steps, windows, dtype=dtype)
+
+
 @pytest.fixture(scope="module")
 def rb512():
     return inputs.make("rb512")
