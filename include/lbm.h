@@ -222,9 +222,12 @@ size_t lbm_required_bytes(const lbm_params* p, const uint8_t* solid_labels);
  * The step's replay graph (16 steps) is captured and instantiated here, once,
  * so that later submissions carry no set-up work (the page's "pipeline
  * creation", which it times apart from the steps).
- * device_buf: device memory of device_bytes bytes, BORROWED: the caller owns
- * it and keeps it alive until lbm_destroy(); the populations live in it, so
- * saving its bytes and lbm_time() checkpoints the state (lbm_resume).
+ * device_buf: device memory of device_bytes bytes, 256-byte aligned,
+ * BORROWED: the caller owns it and keeps it alive until lbm_destroy(); the
+ * populations live in it, so saving its bytes and lbm_time() checkpoints the
+ * state (lbm_resume).  Every population slot, padding included, is set to
+ * NaN here; lbm_init_fields then writes the slots the cells own, so a read of
+ * any other slot would show as NaN in the fields.
  * hip_stream: a hipStream_t (NULL = the null stream), BORROWED.
  * Host arrays are copied before the call returns.  On failure nothing is kept
  * and *out is NULL.  Errors: LBM_E_INVALID (bad sizes, a rate outside [0, 2),

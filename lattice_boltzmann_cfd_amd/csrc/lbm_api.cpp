@@ -1399,7 +1399,15 @@ lbm_status lbm_create(const lbm_params* p, const uint8_t* solid_labels, void* de
                 return LBM_E_INVALID;
             }
         }
-        hipError_t e = hipSuccess;
+        // No byte of the buffer is left as the caller handed it over: every
+        // population slot, padding and tile tails included, and the gathered
+        // link values start as NaN (lbm_init_fields writes the slots the
+        // cells own, so a read of a slot no cell owns shows in the fields);
+        // the rest starts at zero, then takes the uploads.
+        hipError_t e = launch_fill_words(base + L.f, L.mask - L.f, 0xffffffffu, c->stream);
+        if (e == hipSuccess) e = launch_fill_words(base + L.mask, L.scratch - L.mask, 0u, c->stream);
+        if (e == hipSuccess) e = launch_fill_words(base + L.scratch, L.face_vel - L.scratch, 0xffffffffu, c->stream);
+        if (e == hipSuccess) e = launch_fill_words(base + L.face_vel, L.total - L.face_vel, 0u, c->stream);
         if (nl > 0) {
             if (e == hipSuccess) e = hipMemcpyAsync(c->lcell, cell.data(), 4 * nl, hipMemcpyHostToDevice, c->stream);
             if (e == hipSuccess) e = hipMemcpyAsync(c->lcellw, cellw.data(), 4 * nl, hipMemcpyHostToDevice, c->stream);

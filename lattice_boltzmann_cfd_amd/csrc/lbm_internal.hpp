@@ -206,5 +206,8 @@ template <class L, typename R> hipError_t launch_read(const FieldArgs<R>& a, boo
 template <class L, typename R>
 hipError_t launch_diag(const FieldArgs<R>& a, bool thermal, double* out, hipStream_t s);
 hipError_t launch_zero_f64(double* p, int64_t n, hipStream_t s);
+// Every 32-bit word of [p, p + bytes) set to `word` (0xffffffff: a NaN in
+// fp32 and fp64); p and bytes multiples of 16.
+hipError_t launch_fill_words(void* p, size_t bytes, uint32_t word, hipStream_t s);
 
 }  // namespace lbm

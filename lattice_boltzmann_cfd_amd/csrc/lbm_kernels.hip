@@ -1058,6 +1058,14 @@ __global__ void __launch_bounds__(BLOCK) k_zero_f64(double* p, int64_t n)
     if (i < n) p[i] = 0.0;
 }
 
+// Every 32-bit word of [p, p + 16 n16 bytes) set to `word`.  Grid-stride
+// over 16-byte words.
+__global__ void __launch_bounds__(BLOCK) k_fill_words(uint4* p, int64_t n16, uint32_t word)
+{
+    const uint4 v = make_uint4(word, word, word, word);
+    for (int64_t i = (int64_t)blockIdx.x * BLOCK + threadIdx.x; i < n16; i += (int64_t)gridDim.x * BLOCK) p[i] = v;
+}
+
 inline dim3 grid_for(int64_t n) { return dim3((unsigned)((n + BLOCK - 1) / BLOCK)); }
 
 }  // namespace
@@ -1182,6 +1190,16 @@ hipError_t launch_zero_f64(double* p, int64_t n, hipStream_t s)
 {
     if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_zero_f64, grid_for(n), dim3(BLOCK), 0, s, p, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_words(void* p, size_t bytes, uint32_t word, hipStream_t s)
+{
+    if (((uintptr_t)p | bytes) & 15u) return hipErrorInvalidValue;
+    const int64_t n16 = (int64_t)(bytes / 16);
+    if (n16 == 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((n16 + BLOCK - 1) / BLOCK, 65536);
+    hipLaunchKernelGGL(k_fill_words, dim3((unsigned)blocks), dim3(BLOCK), 0, s, (uint4*)p, n16, word);
     return hipGetLastError();
 }
 
