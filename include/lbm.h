@@ -426,7 +426,9 @@ int64_t lbm_count_links(const lbm_params* p, const uint8_t* solid_labels, int32_
  * is NULL).  Valid until the next call on the same context. */
 const char* lbm_last_error(const lbm_ctx* ctx);
 
-/* Release the context (host memory only; device_buf stays the caller's). */
+/* Wait for the work queued on the context's stream, then release the
+ * context (its host memory and its replay graph; device_buf stays the
+ * caller's, who may free it once this returns).  NULL is ignored. */
 void lbm_destroy(lbm_ctx* ctx);
 
 #ifdef __cplusplus

@@ -308,7 +308,10 @@ class Solver:
         if nbytes == 0:
             raise LbmError(LBM_E_INVALID, "parameters rejected by lbm_required_bytes")
         self.nbytes = nbytes
-        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        # allocated on the solver's stream, where every use of it is queued, so
+        # that torch reuses the memory only after that work
+        with torch.cuda.stream(self.stream):
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         self.ctx = lbm_create(params, labels, self.buf.data_ptr(), nbytes, self.stream.cuda_stream, dtype, streaming)
         self._keep = None
 

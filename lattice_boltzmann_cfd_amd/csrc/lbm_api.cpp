@@ -1726,6 +1726,12 @@ lbm_status lbm_profile_read(lbm_ctx* c, double* ms, int64_t* launches, int32_t n
 
 const char* lbm_last_error(const lbm_ctx* c) { return c ? c->err.c_str() : g_create_error.c_str(); }
 
-void lbm_destroy(lbm_ctx* c) { delete c; }
+void lbm_destroy(lbm_ctx* c)
+{
+    if (!c) return;
+    // the queued steps may still read the caller's buffer and the graph
+    (void)hipStreamSynchronize(c->stream);
+    delete c;
+}
 
 }  // extern "C"

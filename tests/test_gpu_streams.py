@@ -48,3 +48,20 @@ def test_solver_on_its_own_stream_equals_current_stream():
     for a, b in zip(ref, got):
         assert np.array_equal(a[..., fl], b[..., fl])
     assert np.array_equal(fref, fgot)
+
+
+def test_destroy_waits_for_queued_steps():
+    """lbm_destroy returns only after the steps queued on the context's stream
+    have run (the caller may free the buffer at once): 400 steps of a 128^3
+    box on a stream of its own, then close() with nothing else waited for,
+    and the stream is idle when it returns."""
+    import torch
+
+    w = inputs.make("sol128")
+    side = torch.cuda.Stream()
+    s = binding.Solver(w.params, w.labels, stream=side)
+    s.init(w.rho, w.u)
+    side.synchronize()
+    s.step(400)  # about 20 ms of queued work
+    s.close()
+    assert side.query()
