@@ -77,6 +77,13 @@ def library():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built: run `python -m lattice_boltzmann_cfd_amd.build` "
                                "(there is no CPU fallback)")
+        # torch ships its own HIP runtime under the system runtime's soname.
+        # Loaded first, it is the copy this library binds to, and the process
+        # holds one runtime.  Loaded after this library, it would bring a
+        # second runtime beside the system one, and this library's would then
+        # find no device.
+        import torch  # noqa: F401
+
         lib = ctypes.CDLL(LIB_PATH)
         P = ctypes.POINTER(LbmParams)
         vp = ctypes.c_void_p
