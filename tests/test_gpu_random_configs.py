@@ -8,15 +8,19 @@ thermal rule and temperature of every bounded face, solid balls of up to
 three labels (Dirichlet or adiabatic), random relaxation rates, body force and
 buoyancy, a random initial state, the precision, the streaming mode, link
 passes or bounce-back in the kernel, the tile size and the occupancy bounds,
-two submissions of random lengths, and lbm_step or lbm_step_noalloc.  A ball the library would reject (one
+two submissions of random lengths, lbm_step or lbm_step_noalloc, per-kernel
+timing on or off, and a checkpoint after the first submission resumed in a
+second solver (equal to the uninterrupted run bit for bit).  A ball the library would reject (one
 on a free-slip face's layer) drops the balls; every drawn case is checked to
 be valid on the host.  The fields after both submissions and the forces and heat of the
 last step must meet the parity bar of test_gpu_parity (1e-4 fp32, 1e-11 fp64
-on fields; forces relative 1e-4 / 1e-10 plus the fp32 summation floor)."""
+on fields; forces relative 1e-4 / 1e-10 plus the fp32 summation floor), and
+the volume diagnostics must equal their definition over the read-back fields
+(fp64 rounding of the sums)."""
 import numpy as np
 import pytest
 
-from harness import oracle_run, say
+from harness import fluid_mask, oracle_run, say, volume_sums
 from lattice_boltzmann_cfd_amd import binding, inputs
 from test_gpu_parity import check_fields, check_forces
 
@@ -114,42 +118,80 @@ def draw(seed):
         u[2] = 0.0
     T = rng.uniform(-0.2, 0.2, n) if thermal else None
     steps = [int(v) for v in rng.integers(1, 26, size=2)]
-    noalloc = bool(rng.random() < 0.2)
+    extra = dict(noalloc=bool(rng.random() < 0.2), resume=bool(rng.random() < 0.3),
+                 profile=bool(rng.random() < 0.2))
     w = inputs.Workload(f"random{seed}", p, rho, u, T, labels, sum(steps))
-    return w, dtype, streaming, steps, noalloc
+    return w, dtype, streaming, steps, extra
 
 
-def gpu_steps(w, steps, dtype, streaming, noalloc):
-    """The submissions through lbm_step, or lbm_step_noalloc; the fields at
-    the end and the forces latched by the last submission."""
+def fields(torch, s):
+    rho, u, T = s.macros()
+    torch.cuda.synchronize()
+    return dict(rho=rho.cpu().double().numpy(), u=u.cpu().double().numpy(),
+                T=T.cpu().double().numpy() if T is not None else None)
+
+
+def gpu_steps(w, steps, dtype, streaming, extra):
+    """The two submissions through lbm_step, or lbm_step_noalloc, with
+    per-kernel timing on for the second if drawn; the fields at the end, the
+    forces latched by the last submission and the volume diagnostics.  If
+    drawn, the state after the first submission is saved, resumed in a second
+    solver and stepped through the second submission again: fields and forces
+    must equal the uninterrupted run's bit for bit."""
     import torch
 
+    thermal = bool(w.params["thermal"])
     s = binding.Solver(w.params, w.labels, dtype=dtype, streaming=streaming)
+    step = s.step_noalloc if extra["noalloc"] else s.step
+    saved = None
     try:
-        s.init(w.rho, w.u, w.T if w.params["thermal"] else None)
-        for n in steps:
-            (s.step_noalloc if noalloc else s.step)(n)
+        s.init(w.rho, w.u, w.T if thermal else None)
+        step(steps[0])
+        if extra["resume"]:
+            saved = s.checkpoint()
+        if extra["profile"]:
+            s.profile(True)
+        step(steps[1])
         forces = s.wall_force()
-        rho, u, T = s.macros()
-        torch.cuda.synchronize()
+        out = fields(torch, s)
+        out.update(forces=forces, time=s.time, diag=s.diagnostics())
+        if extra["profile"]:
+            launches = sum(n for _, n in s.kernel_times().values())
+            # lbm_step_noalloc times nothing; lbm_step times every launch while profiling
+            assert launches == 0 if extra["noalloc"] else launches >= steps[1]
+            s.profile(False)
         flow, temp = (9, 5) if int(w.params.get("lattice", 0)) == 1 else (19, 7)
-        return dict(rho=rho.cpu().double().numpy(), u=u.cpu().double().numpy(),
-                    T=T.cpu().double().numpy() if T is not None else None, forces=forces, time=s.time,
-                    links=s.num_links(flow) + s.num_links(temp))
+        out["links"] = s.num_links(flow) + s.num_links(temp)
     finally:
         s.close()
+    if saved is not None:
+        r = binding.Solver(w.params, w.labels, dtype=dtype, streaming=streaming)
+        try:
+            r.resume(*saved)
+            (r.step_noalloc if extra["noalloc"] else r.step)(steps[1])
+            again = fields(torch, r)
+            assert np.array_equal(r.wall_force(), out["forces"])
+        finally:
+            r.close()
+        for k in ("rho", "u", "T"):
+            if out[k] is not None:
+                assert np.array_equal(again[k], out[k], equal_nan=True), f"resumed run differs in {k}"
+    return out
 
 
 @pytest.mark.parametrize("seed", range(N_CASES))
 def test_random_configuration(seed):
-    w, dtype, streaming, steps, noalloc = draw(seed)
+    w, dtype, streaming, steps, extra = draw(seed)
     p = w.params
     say(f"CASE random seed={seed} {'2D' if p.get('lattice') else '3D'} {w.shape} thermal={p['thermal']} "
         f"dtype={dtype} streaming={streaming} links={p['links']} tile={p['tile_log2']} occ={p['occupancy']} "
         f"faces={p['face_kind']} solids={0 if w.labels is None else int((w.labels != 0).sum())} steps={steps} "
-        f"noalloc={noalloc}")
-    g = gpu_steps(w, steps, dtype, streaming, noalloc)
+        f"{' '.join(k for k, v in extra.items() if v)}")
+    g = gpu_steps(w, steps, dtype, streaming, extra)
     o = oracle_run(w, sum(steps), want_diag=True)
     check_fields(g, o, w, dtype, f"random{seed}")
     check_forces(g["forces"], o["diag"][-1], dtype, g["links"], f"random{seed}")
     assert g["time"] == sum(steps)
+    own, mag = volume_sums(g["rho"], g["u"], g["T"], fluid_mask(w))
+    assert g["diag"][binding.LBM_DIAG_FLUID_CELLS] == fluid_mask(w).sum()
+    assert (np.abs(g["diag"] - own) <= 1e-12 * mag + 1e-300).all()
