@@ -179,8 +179,9 @@ def main(argv=None):
     ap.add_argument("--dtype", type=int, default=4, choices=(4, 8))
     ap.add_argument("--streaming", type=int, default=1, choices=(1, 2, 3),
                     help="1 in place (AA), 2 two buffers in two passes, 3 two buffers in one pass")
-    ap.add_argument("--cpu-steps", type=int, default=16,
-                    help="oracle steps for the CPU baseline, about 15 s on 16 host threads at 256^3 (0: skip)")
+    ap.add_argument("--cpu-steps", type=int, default=-1,
+                    help="oracle steps for the CPU baseline (0: skip; default: 16 at 256^3, about 15 s on 16 host "
+                         "threads, and as many fewer as the box has more cells, at least 1)")
     ap.add_argument("--cpu-steps-one-thread", type=int, default=1,
                     help="oracle steps on one host thread for the same baseline, about 14 s per step at 256^3 "
                          "(0: skip)")
@@ -315,8 +316,9 @@ def main(argv=None):
     del rho, solver
     torch.cuda.empty_cache()
     roofline["practical"] = practical
-    if args.cpu_steps > 0:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_steps, args.cpu_steps_one_thread)
+    cpu_steps = args.cpu_steps if args.cpu_steps >= 0 else max(1, round(16 * 256 ** 3 / w.cells))
+    if cpu_steps > 0:
+        line["cpu_baseline"] = cpu_baseline(w, cpu_steps, args.cpu_steps_one_thread)
     print(json.dumps(line), flush=True)
     return 0
 
