@@ -181,7 +181,7 @@ def main(argv=None):
                     help="1 in place (AA), 2 two buffers in two passes, 3 two buffers in one pass")
     ap.add_argument("--cpu-steps", type=int, default=-1,
                     help="oracle steps for the CPU baseline (0: skip; default: 16 at 256^3, about 15 s on 16 host "
-                         "threads, and as many fewer as the box has more cells, at least 1)")
+                         "threads, as many fewer as the box has more cells, an eighth of that in 2D, at least 1)")
     ap.add_argument("--cpu-steps-one-thread", type=int, default=1,
                     help="oracle steps on one host thread for the same baseline, about 14 s per step at 256^3 "
                          "(0: skip)")
@@ -316,7 +316,10 @@ def main(argv=None):
     del rho, solver
     torch.cuda.empty_cache()
     roofline["practical"] = practical
-    cpu_steps = args.cpu_steps if args.cpu_steps >= 0 else max(1, round(16 * 256 ** 3 / w.cells))
+    # about 2.7e8 cell updates in 3D (16 steps at 256^3); the oracle's streaming runs on one thread on a
+    # 2D box (one z plane), so an eighth of that there
+    budget = 16 * 256 ** 3 // (8 if int(w.params.get("lattice", 0)) == 1 else 1)
+    cpu_steps = args.cpu_steps if args.cpu_steps >= 0 else max(1, round(budget / w.cells))
     if cpu_steps > 0:
         line["cpu_baseline"] = cpu_baseline(w, cpu_steps, args.cpu_steps_one_thread)
     print(json.dumps(line), flush=True)
