@@ -139,6 +139,7 @@ def test_null_context_calls_are_invalid(lib):
     assert lib.lbm_num_links(None, 19) == -1
     assert lib.lbm_profile(None, 1) == binding.LBM_E_INVALID
     assert lib.lbm_profile_read(None, None, None, 0) == binding.LBM_E_INVALID
+    lib.lbm_destroy(None)  # ignored
 
 
 def test_solid_on_a_slip_layer_rejected(lib):
