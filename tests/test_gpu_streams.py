@@ -65,3 +65,35 @@ def test_destroy_waits_for_queued_steps():
     s.step(400)  # about 20 ms of queued work
     s.close()
     assert side.query()
+
+
+def test_two_contexts_on_two_streams_interleaved():
+    """Two contexts share nothing: a sphere box and a thermal cavity, each on
+    a stream of its own, their submissions interleaved with no wait between
+    them, give the fields and forces of each run alone, bit for bit."""
+    import torch
+
+    from harness import gpu_run
+
+    w1 = inputs.make("sphere128", shape=(36, 30, 28), R=6.0, gx=1e-5)
+    w2 = inputs.make("cavity256", shape=(34, 30, 26))
+    alone = [gpu_run(w, [37, 63]) for w in (w1, w2)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    solvers = [binding.Solver(w.params, w.labels, stream=st) for w, st in zip((w1, w2), streams)]
+    try:
+        for s, w in zip(solvers, (w1, w2)):
+            s.init(w.rho, w.u, w.T if w.params["thermal"] else None)
+        for n in (37, 63):
+            for s in solvers:
+                s.step(n)
+        for s, w, ref in zip(solvers, (w1, w2), alone):
+            rho, u, T = s.macros()
+            torch.cuda.synchronize()
+            assert np.array_equal(rho.cpu().double().numpy(), ref["rho"], equal_nan=True)
+            assert np.array_equal(u.cpu().double().numpy(), ref["u"], equal_nan=True)
+            if T is not None:
+                assert np.array_equal(T.cpu().double().numpy(), ref["T"], equal_nan=True)
+            assert np.array_equal(s.wall_force(), ref["forces"][-1])
+    finally:
+        for s in solvers:
+            s.close()
