@@ -287,10 +287,14 @@ enum { LBM_NOALLOC_SCRATCH_BYTES = 16 << 20 };
  * GPU shares that GPU's array and leaves its contents behind (each step
  * writes every scratch value it reads before reading it, so nothing needs
  * clearing); calls that overlap in time on one GPU (other streams, other
- * threads) race on it.  Errors: LBM_E_INVALID (NULL context, n < 0, no
- * lbm_init_fields, or a context whose scratch exceeds the array: links *
- * dtype for LBM_LINKS_PASSES plus 32 bytes per 1024 links of a group),
- * LBM_E_DEVICE.  Asynchronous. */
+ * threads) race on it.  The array's device address is looked up by
+ * lbm_create, so a call does no set-up work.  Under graph capture the graph
+ * holds the launches of one call, with that call's step parities, while the
+ * context's time (host state) advances once, at the call: capture an even
+ * number of steps and set the time after replays with lbm_resume.  Errors:
+ * LBM_E_INVALID (NULL context, n < 0, no lbm_init_fields, or a context whose
+ * scratch exceeds the array: links * dtype for LBM_LINKS_PASSES plus 32
+ * bytes per 1024 links of a group), LBM_E_DEVICE.  Asynchronous. */
 lbm_status lbm_step_noalloc(lbm_ctx* ctx, int64_t n);
 
 /* Macroscopic fields at the current time: rho, u = (sum c f + F/2)/rho as

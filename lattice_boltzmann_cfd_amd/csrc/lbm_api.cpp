@@ -1435,6 +1435,18 @@ lbm_status lbm_create(const lbm_params* p, const uint8_t* solid_labels, void* de
             delete c;
             return LBM_E_DEVICE;
         }
+        // the device address of lbm_step_noalloc's static scratch, looked up
+        // here (once per device) so that no lbm_step_noalloc call does set-up
+        // work, which a caller capturing it into a graph could not allow
+        {
+            void* noalloc_base = nullptr;
+            e = noalloc_scratch(c->device, &noalloc_base);
+            if (e != hipSuccess) {
+                g_create_error = std::string("static scratch address: ") + hipGetErrorString(e);
+                delete c;
+                return LBM_E_DEVICE;
+            }
+        }
         // the replay graph of 16 steps, built once here (the pipeline creation
         // of "GPU lattice Boltzmann: streaming layout and performance", kept
         // out of the submissions that follow)
