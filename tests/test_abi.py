@@ -379,3 +379,14 @@ def test_automatic_layout_of_large_buffers(lib, shape, thermal, lattice, dtype, 
     planes = binding.lbm_required_bytes(dict(p, tile_log2=31), dtype=dtype)
     assert auto > 0 and planes > 0
     assert (auto != planes) == tiled
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """Without the built library every call raises; nothing falls back to a
+    CPU path."""
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "LIB_PATH", os.path.join(ROOT, "no_such_dir", "liblbm_hip.so"))
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        binding.lbm_required_bytes(periodic())
+    with pytest.raises(RuntimeError, match="not built"):
+        binding.lbm_check_links(periodic())
